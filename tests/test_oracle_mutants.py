@@ -1,0 +1,98 @@
+"""Mutation check of the oracle's pins (no GPU).
+
+Each case plants one plausible slip in a copy of oracle.c (the committed
+oracle is untouched), builds it into a temporary library, and runs the pins
+of tests/test_oracle_pins.py against it: at least one pin must fail.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+ROUTE = [lambda: pins.test_route_matches_brute_force(16, 4, 2, 4, 256),
+         lambda: pins.test_route_matches_brute_force(256, 8, 4, 8, 128),
+         pins.test_route_textbook_special_case, pins.test_route_group_score_is_top2_sum,
+         pins.test_route_excluded_groups_never_selected, pins.test_route_ties_go_to_lower_index,
+         pins.test_route_weights_use_unbiased_scores]
+QUANT = [pins.test_quant_round_half_even_by_hand, pins.test_quant_closed_forms]
+DOTS = [pins.test_code_layout_by_hand] + \
+       [lambda b=b: pins.test_block_dots_brute_force(b) for b in (2, 4, 8)] + \
+       [lambda b=b: pins.test_matvec_equals_dequantised_matmul(b) for b in (2, 4, 8)]
+LAYER = [pins.test_single_expert_layer_is_dense_swiglu, pins.test_layer_linear_in_rsf_and_shared_alone,
+         pins.test_layer_equals_sum_of_experts]
+MISC = [pins.test_rmsnorm_closed_forms, pins.test_permute_is_stable_sort]
+ALL = ROUTE + QUANT + DOTS + LAYER + MISC
+
+MUTANTS = {
+    "group score = max only": ("gscore[g] = (m >= 2) ? b1 + b2 : b1;", "gscore[g] = b1;"),
+    "group ties to higher index": ("gscore[g] > gscore[best]", "gscore[g] >= gscore[best]"),
+    "expert ties to higher index": ("!taken[e] && (best < 0 || c[e] > c[best])",
+                                    "!taken[e] && (best < 0 || c[e] >= c[best])"),
+    "weights from biased score": ("(float)(s[idx[(size_t)t * k + i]] / sum",
+                                  "(float)(c[idx[(size_t)t * k + i]] / sum"),
+    "rsf dropped": ("/ sum * sh->rsf)", "/ sum)"),
+    "sigmoid sign": ("s[e] = 1.0 / (1.0 + exp(-z));", "s[e] = 1.0 / (1.0 + exp(z));"),
+    "gate weight transposed": ("gate_w[(size_t)e * H + j]", "gate_w[(size_t)j * E + e]"),
+    "round half away": ("rintf(xb[j] / db)", "roundf(xb[j] / db)"),
+    "reciprocal multiply": ("rintf(xb[j] / db)", "rintf(xb[j] * (1.0f / db))"),
+    "scale over 128": ("amax / 127.0f", "amax / 128.0f"),
+    "nibble order": ("(j & 1) ? (row[j >> 1] >> 4) : (row[j >> 1] & 15)",
+                     "(j & 1) ? (row[j >> 1] & 15) : (row[j >> 1] >> 4)"),
+    "int4 offset not two's complement": ("return nib >= 8 ? nib - 16 : nib;", "return nib - 8;"),
+    "int2 field order": ("int f = (row[j >> 2] >> (2 * (j & 3))) & 3;",
+                         "int f = (row[j >> 2] >> (6 - 2 * (j & 3))) & 3;"),
+    "wrong activation block scale": ("acc += (double)d[(size_t)t * nb + b] * (double)blk;",
+                                     "acc += (double)d[(size_t)t * nb] * (double)blk;"),
+    "silu -> sigmoid": ("double silu = gz / (1.0 + exp(-gz));", "double silu = 1.0 / (1.0 + exp(-gz));"),
+    "gate and up swapped": ("h[i] = (float)(silu * (double)u[i]);",
+                            "h[i] = (float)((double)u[i] / (1.0 + exp(-(double)u[i])) * gz);"),
+    "shared scaled by rsf": ("if (y_shared) acc += (double)y_shared[(size_t)t * H + r];",
+                             "if (y_shared) acc += sh->rsf * (double)y_shared[(size_t)t * H + r];"),
+    "rmsnorm eps outside sqrt": ("sqrt(ss / H + eps)", "(sqrt(ss / H) + eps)"),
+    "permute not stable": ("int row = fill[idx[a]]++;",
+                           "int row = off[idx[a]] + off[idx[a] + 1] - 1 - fill[idx[a]]++;"),
+}
+
+
+@pytest.fixture
+def mutant_lib(tmp_path):
+    saved = (oracle.LIB, oracle._lib)
+
+    def make(old, new):
+        src = open(SRC).read()
+        assert src.count(old) == 1, "mutation anchor not unique: %r" % old
+        d = tmp_path / "m"
+        d.mkdir(exist_ok=True)
+        (d / "oracle.c").write_text(src.replace(old, new))
+        (d / "oracle.h").write_text(open(SRC[:-1] + "h").read())
+        so = str(d / "liboracle_mut.so")
+        subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+                        "-ffp-contract=off", str(d / "oracle.c"), "-o", so, "-lm"], check=True)
+        oracle.LIB, oracle._lib = so, None
+        oracle.lib()
+
+    yield make
+    oracle.LIB, oracle._lib = saved
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, mutant_lib):
+    mutant_lib(*MUTANTS[name])
+    caught = []
+    for pin in ALL:
+        try:
+            pin()
+        except (AssertionError, ValueError, RuntimeError, IndexError):
+            caught.append(getattr(pin, "__name__", "pin"))
+    assert caught, "no pin caught the mutant %r" % name
+
+
+def test_unmutated_copy_passes(mutant_lib):
+    mutant_lib("static size_t row_bytes", "static size_t row_bytes")
+    for pin in ALL:
+        pin()
