@@ -1,0 +1,186 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) quantised mixture-of-experts layer.
+ *
+ * What the layer computes (GeekNews #31297 "Show HN: running GLM 5.2 on a
+ * slow computer", section "implemented features"; wpnews.pro "Colibri --
+ * GLM-5.2 (744B MoE) on 25GB RAM in one pure C file", model spec table):
+ *  - a DeepSeek-V3-style sigmoid router (noaux_tc: correction bias for
+ *    selection, group-limited top-k, weights normalised and multiplied by
+ *    routed_scaling_factor);
+ *  - Q8_0-style int8 activations in blocks of 32 with one fp32 scale each;
+ *  - routed and shared SwiGLU experts over int8 / packed int4 / packed int2
+ *    weight codes with per-row fp32 scales, as integer dot products;
+ *  - batch-union execution for multi-token batches (each selected expert
+ *    read once per batch, applied to every token routed to it);
+ *  - a weighted combine: 8 active + 1 shared expert per token.
+ *
+ * Conventions (all functions)
+ *  - Every pointer argument that names a tensor is a DEVICE pointer; the
+ *    moe_shape_t / moe_weights_t structs themselves live in host memory.
+ *  - The caller owns every buffer.  The library never allocates or frees,
+ *    never synchronises, and keeps no global state; calls are thread-safe
+ *    as long as concurrent calls use distinct workspaces and outputs.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *    returns at once.  Inputs are never written.  Outputs are overwritten,
+ *    except with MOE_ACCUMULATE, which adds into y.  y must not alias x.
+ *  - Argument checks run before any launch: a call that returns an error
+ *    has launched nothing.  T = 0 is a successful no-op.  A fault inside a
+ *    kernel is asynchronous and surfaces on the caller's next synchronise.
+ *  - Tensors are row-major and densely packed.
+ *
+ * Weight layout.  For an expert, gate and up are [I][H] (rows = I, in = H),
+ * down is [H][I]; each row holds in*wbits/8 bytes of codes; scales are one
+ * fp32 per row.  Codes are two's complement: wbits = 8 one int8 per byte;
+ * wbits = 4 two per byte, element 2m in the low nibble of byte m; wbits = 2
+ * four per byte, element 4m+i in bits 2i..2i+1.  A routed stack holds
+ * n_experts experts back to back: expert e's gate codes start at
+ * gate + e*I*(H*wbits/8) and its gate scales at gate_s + e*I.  Every row
+ * must start 16-byte aligned, which holds when the base pointers are
+ * 16-byte aligned (H*wbits/8 and I*wbits/8 are multiples of 16).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- types */
+typedef struct {
+    int32_t hidden;       /* H: multiple of 32; rows of H*wbits/8 bytes a multiple of 16 */
+    int32_t inter;        /* I: expert intermediate size, same rules as H */
+    int32_t n_experts;    /* E routed experts, 1..512 */
+    int32_t n_group;      /* G groups of E/G consecutive experts, 1..64 */
+    int32_t topk_group;   /* groups kept per token, 1..G */
+    int32_t top_k;        /* experts per token, 1..min(32, topk_group*E/G) */
+    int32_t n_shared;     /* 0 or 1 shared expert (weight 1, not scaled) */
+    int32_t wbits;        /* 2, 4 or 8 */
+    float   routed_scaling_factor;
+} moe_shape_t;
+
+typedef struct {
+    const uint8_t *gate, *up, *down;        /* packed codes (device) */
+    const float   *gate_s, *up_s, *down_s;  /* per-row fp32 scales (device) */
+} moe_weights_t;
+
+/* ---------------------------------------------------------------- errors */
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,        /* null pointer, negative size, inconsistent shape */
+    MOE_EUNSUPPORTED = 2,  /* valid but outside what the kernels implement */
+    MOE_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes */
+    MOE_EHIP = 4           /* a launch failed (hipGetLastError) */
+};
+const char *moe_strerror(int code);
+
+/* ---------------------------------------------------------------- flags */
+#define MOE_PATH_AUTO     0u  /* GEMV for small T, grouped GEMM otherwise */
+#define MOE_PATH_GEMV     1u  /* batch-union GEMV (T <= 8) */
+#define MOE_PATH_GROUPED  2u  /* token-permuted expert-grouped int8 MFMA GEMM */
+#define MOE_ACCUMULATE    4u  /* y += layer(x) instead of y = layer(x) */
+/* Stage selection, for timing one kernel of the path in isolation: when any
+ * MOE_STAGE bit is set, only the selected launches of the path run, in
+ * order.  Stage n is the n-th kernel launch of the chosen path (see
+ * moe_layer_stage_count).  Stages exchange their intermediate results
+ * through the workspace, so a caller running them one at a time must run
+ * all of them, in order, with the same arguments and workspace. */
+#define MOE_STAGE(n)      (1u << (8 + (n)))
+#define MOE_STAGE_MASK    0xFF00u
+
+/* ---------------------------------------------------------------- router */
+/* moe_route -- noaux_tc routing of T tokens (GeekNews #31297, implemented
+ * features: DeepSeek-V3-style sigmoid router with noaux_tc and
+ * routed_scaling_factor).
+ *   x       [T][H] fp32      token hidden states (unquantised)
+ *   gate_w  [E][H] fp32      router weights
+ *   bias    [E]    fp32      correction bias, used for selection only
+ *   topk_idx [T][k] int32    out: selected experts, ordered by biased score
+ *                            descending, ties to the lower index
+ *   topk_w   [T][k] fp32     out: sigmoid scores of the selected experts
+ *                            normalised to sum 1, times routed_scaling_factor
+ * Arithmetic: logits, sigmoid and all comparisons in fp64; group score =
+ * sum of the two largest biased scores of the group; the topk_group best
+ * groups are kept, the others excluded.
+ * ws: device scratch of at least moe_route_workspace_bytes(shape, T) bytes. */
+int moe_route(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w,
+              const float *bias, int32_t *topk_idx, float *topk_w,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_route_workspace_bytes(const moe_shape_t *shape, int32_t T);
+
+/* ---------------------------------------------------------------- activations */
+/* moe_quant_act -- Q8_0-style activation quantisation (GeekNews #31297,
+ * implemented features: integer-dot kernels on Q8_0-style int8
+ * activations).  Per row and per block of 32 consecutive elements:
+ * d = max|x| / 127 (fp32 IEEE division), q = round-half-even(x / d)
+ * (fp32 IEEE division), clamped to [-127, 127]; d = 0 gives q = 0.
+ *   x [T][D] fp32, D a multiple of 32  ->  q [T][D] int8, d [T][D/32] fp32 */
+int moe_quant_act(const float *x, int32_t T, int32_t D, int8_t *q, float *d, hipStream_t stream);
+
+/* moe_block_dots -- the integer block sums the expert kernels build on
+ * (exported for bit-exact testing):
+ *   out[t][r][b] = sum_{j<32} code[r][32b+j] * q[t][32b+j]   (int32)
+ *   codes [rows][D*wbits/8] packed as in the weight layout above (16-byte
+ *   aligned rows), q [T][D] int8, out [T][rows][D/32] int32. */
+int moe_block_dots(int32_t wbits, const uint8_t *codes, int32_t rows, int32_t D,
+                   const int8_t *q, int32_t T, int32_t *out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- experts */
+/* moe_expert_ffn -- one SwiGLU expert on quantised activations, unweighted:
+ *   g = W_gate x, u = W_up x, h = silu(g) * u, (qh, dh) = quant(h),
+ *   y = W_down h,  each product an integer block dot scaled by the
+ *   activation block scale and the weight row scale.
+ *   w       weights stack; `expert` selects expert `expert` of it
+ *   q, d    [T][H] int8 and [T][H/32] fp32 (as from moe_quant_act)
+ *   y       [T][H] fp32 out
+ * ws: at least moe_workspace_bytes(shape, T, MOE_PATH_GEMV) bytes. */
+int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t expert,
+                   const int8_t *q, const float *d, int32_t T, float *y,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- layer */
+/* moe_layer_forward -- the whole MoE layer for T tokens:
+ *   y[t] = sum_{i<k} topk_w[t][i] * FFN_{topk_idx[t][i]}(q(x[t])) + FFN_shared(q(x[t]))
+ *   x        [T][H] fp32
+ *   routed   stack of E experts; shared: one expert (NULL iff n_shared = 0)
+ *   y        [T][H] fp32 out (or accumulated into with MOE_ACCUMULATE)
+ *   idx_out, w_out  [T][k] (nullable): the routing, as moe_route returns it
+ *   flags    MOE_PATH_*, MOE_ACCUMULATE, MOE_STAGE(n)
+ * ws: at least moe_workspace_bytes(shape, T, flags) bytes, 256-byte aligned. */
+int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w,
+                      const float *bias, const moe_weights_t *routed, const moe_weights_t *shared,
+                      float *y, int32_t *idx_out, float *w_out, uint32_t flags,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags);
+/* number of kernel launches moe_layer_forward makes for these arguments
+ * (the n of MOE_STAGE(n) runs from 0 to this minus 1); < 0 on bad arguments */
+int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags);
+
+/* ---------------------------------------------------------------- stack */
+/* moe_rmsnorm -- out = x / sqrt(mean(x^2) + eps) * g per row, the sum of
+ * squares and the scaling in fp64 (the norm before each MoE layer of the
+ * decode stack x_{l+1} = x_l + MoE_l(RMSNorm(x_l))).
+ *   x [T][H], g [H], out [T][H] fp32; out may alias x. */
+int moe_rmsnorm(const float *x, const float *g, double eps, int32_t T, int32_t H, float *out,
+                hipStream_t stream);
+
+/* ---------------------------------------------------------------- permute */
+/* moe_permute -- the token permutation of the grouped path (batch-union
+ * MoE, GeekNews #31297 implemented features), exported for testing.
+ * Assignment a = t*k + i routes token t to expert idx[a].
+ *   off  [E+1]  out: off[e] .. off[e+1]-1 are expert e's rows
+ *   perm [T*k]  out: perm[row] = a, ascending a within each expert
+ *   inv  [T*k]  out: inv[a] = row
+ * ws: at least moe_permute_workspace_bytes(T, k, E) bytes, 256-byte aligned.
+ * idx entries must lie in [0, E). */
+int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *perm,
+                int32_t *off, int32_t *inv, void *ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

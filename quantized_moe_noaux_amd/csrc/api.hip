@@ -1,0 +1,253 @@
+// extern "C" entry points of libmoe: argument checks, workspace layout and
+// the launch sequences.  Declarations and contracts: include/moe.h.
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool al(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_shape(const moe_shape_t *s)
+{
+    if (!s) return MOE_EINVAL;
+    if (s->hidden <= 0 || s->inter <= 0 || s->hidden % 32 || s->inter % 32) return MOE_EINVAL;
+    if (s->n_experts <= 0 || s->n_group <= 0 || s->n_experts % s->n_group) return MOE_EINVAL;
+    if (s->topk_group < 1 || s->topk_group > s->n_group) return MOE_EINVAL;
+    if (s->top_k < 1 || s->top_k > s->topk_group * (s->n_experts / s->n_group)) return MOE_EINVAL;
+    if (s->n_shared < 0) return MOE_EINVAL;
+    if (!(s->routed_scaling_factor == s->routed_scaling_factor)) return MOE_EINVAL;  // NaN
+    if (s->wbits != 2 && s->wbits != 4 && s->wbits != 8) return MOE_EUNSUPPORTED;
+    if (s->n_shared > 1) return MOE_EUNSUPPORTED;
+    if (s->n_experts > kMaxExperts || s->n_group > kMaxGroups || s->top_k > kMaxTopK) return MOE_EUNSUPPORTED;
+    RouteCfg rc;
+    if (!route_cfg(*s, rc)) return MOE_EUNSUPPORTED;
+    ChunkCfg cc;
+    if (!chunk_cfg(s->hidden, s->wbits, cc) || !chunk_cfg(s->inter, s->wbits, cc)) return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_weights(const moe_weights_t *w)
+{
+    if (!w || !w->gate || !w->up || !w->down || !w->gate_s || !w->up_s || !w->down_s) return MOE_EINVAL;
+    if (!al(w->gate, 16) || !al(w->up, 16) || !al(w->down, 16)) return MOE_EINVAL;
+    if (!al(w->gate_s, 4) || !al(w->up_s, 4) || !al(w->down_s, 4)) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+inline int hip_rc(int e) { return e ? MOE_EHIP : MOE_OK; }
+
+size_t route_ws(const moe_shape_t &s, int T) { return align256(sizeof(double) * (size_t)T * s.n_experts); }
+
+// The stage list of the GEMV path for T tokens: the router / quantiser
+// launch(es), then (gate/up, down) for every chunk of <= kGemvMaxT tokens.
+int gemv_stage_count(int T) { return (T <= kGemvMaxT ? 1 : 2) + 2 * ((T + kGemvMaxT - 1) / kGemvMaxT); }
+
+bool gemv_lds_fits(const moe_shape_t &s, int T)
+{
+    const int Tc = T < kGemvMaxT ? T : kGemvMaxT;
+    const PlanDims pd = plan_dims(Tc, s.top_k, s.n_shared, false);
+    const size_t lds = sizeof(int) * (size_t)((pd.words + 3) & ~3) + (size_t)pd.P * s.inter +
+                       2 * sizeof(float) * (size_t)pd.P * (s.inter / 32);
+    return lds <= (size_t)kGemvMaxLdsAct;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *moe_strerror(int code)
+{
+    switch (code) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or parameter";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failed";
+    default: return "unknown error";
+    }
+}
+
+size_t moe_route_workspace_bytes(const moe_shape_t *shape, int32_t T)
+{
+    if (check_shape(shape) || T < 0) return 0;
+    return route_ws(*shape, T);
+}
+
+int moe_route(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w, const float *bias,
+              int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (T < 0) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !gate_w || !bias || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
+    if (!al(x, 16) || !al(gate_w, 16) || !al(ws, 256)) return MOE_EINVAL;
+    if (ws_bytes < route_ws(*shape, T)) return MOE_EWORKSPACE;
+    RouteCfg rcfg;
+    route_cfg(*shape, rcfg);
+    double *logits = static_cast<double *>(ws);
+    int e = (T <= kGemvMaxT)
+                ? launch_router_logits(x, T, shape->hidden, gate_w, shape->n_experts, logits, nullptr, nullptr, stream)
+                : launch_router_logits_tiled(x, T, shape->hidden, gate_w, shape->n_experts, logits, stream);
+    if (e) return MOE_EHIP;
+    return hip_rc(launch_topk(rcfg, logits, bias, T, topk_idx, topk_w, stream));
+}
+
+int moe_quant_act(const float *x, int32_t T, int32_t D, int8_t *q, float *d, hipStream_t stream)
+{
+    if (T < 0 || D <= 0 || D % 32) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !q || !d || !al(x, 16) || !al(q, 4) || !al(d, 4)) return MOE_EINVAL;
+    return hip_rc(launch_quant(x, T, D, q, d, stream));
+}
+
+int moe_block_dots(int32_t wbits, const uint8_t *codes, int32_t rows, int32_t D, const int8_t *q, int32_t T,
+                   int32_t *out, hipStream_t stream)
+{
+    if (wbits != 2 && wbits != 4 && wbits != 8) return MOE_EUNSUPPORTED;
+    if (rows < 0 || T < 0 || D <= 0 || D % 32) return MOE_EINVAL;
+    if ((D * wbits / 8) % 16) return MOE_EUNSUPPORTED;
+    if (T == 0 || rows == 0) return MOE_OK;
+    if (!codes || !q || !out || !al(codes, 16) || !al(q, 16)) return MOE_EINVAL;
+    return hip_rc(launch_block_dots(wbits, codes, rows, D, q, T, out, stream));
+}
+
+size_t moe_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags)
+{
+    (void)flags;
+    if (check_shape(shape) || T < 0) return 0;
+    return gemv_ws(*shape, T, false).total;
+}
+
+int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags)
+{
+    if (check_shape(shape) || T < 0) return -MOE_EINVAL;
+    if (T == 0) return 0;
+    if ((flags & 3u) == MOE_PATH_GROUPED) return -MOE_EUNSUPPORTED;
+    return gemv_stage_count(T);
+}
+
+int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t expert, const int8_t *q,
+                   const float *d, int32_t T, float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_weights(w))) return rc;
+    if (T < 0 || expert < 0 || expert >= shape->n_experts) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!q || !d || !y || !ws || !al(q, 16) || !al(d, 4) || !al(y, 4) || !al(ws, 256)) return MOE_EINVAL;
+    const GemvWs L = gemv_ws(*shape, T, true);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    char *base = static_cast<char *>(ws);
+    const int H = shape->hidden, nb = H / 32;
+    for (int c0 = 0; c0 < T; c0 += kGemvMaxT) {
+        GemvArgs a{};
+        a.T = (T - c0 < kGemvMaxT) ? T - c0 : kGemvMaxT;
+        a.H = H; a.I = shape->inter; a.E = shape->n_experts; a.wbits = shape->wbits; a.n_shared = 0;
+        route_cfg(*shape, a.rc);
+        a.logits = nullptr; a.bias = nullptr; a.single = expert;
+        a.routed = *w; a.shared = *w;
+        a.xq = q + (size_t)c0 * H; a.xd = d + (size_t)c0 * nb;
+        a.plan = reinterpret_cast<int *>(base + L.plan);
+        a.qh = reinterpret_cast<int8_t *>(base + L.qh);
+        a.dh = reinterpret_cast<float *>(base + L.dh);
+        a.y = y + (size_t)c0 * H;
+        a.accumulate = 0;
+        if (launch_gate_up(a, stream) || launch_down(a, stream)) return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
+int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w, const float *bias,
+                      const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
+                      float *w_out, uint32_t flags, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_weights(routed))) return rc;
+    if (shape->n_shared && (rc = check_weights(shared))) return rc;
+    if (!shape->n_shared && shared) return MOE_EINVAL;
+    if (T < 0) return MOE_EINVAL;
+    if (flags & ~(3u | MOE_ACCUMULATE | MOE_STAGE_MASK)) return MOE_EINVAL;
+    const uint32_t path = flags & 3u;
+    if (path == 3u) return MOE_EINVAL;
+    if (path == MOE_PATH_GROUPED) return MOE_EUNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !gate_w || !bias || !y || !ws) return MOE_EINVAL;
+    if ((idx_out == nullptr) != (w_out == nullptr)) return MOE_EINVAL;
+    if (!al(x, 16) || !al(gate_w, 16) || !al(y, 4) || !al(ws, 256)) return MOE_EINVAL;
+    if (x == y) return MOE_EINVAL;
+    if (!gemv_lds_fits(*shape, T)) return MOE_EUNSUPPORTED;
+    const GemvWs L = gemv_ws(*shape, T, false);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    const int nstages = gemv_stage_count(T);
+    const uint32_t sel = (flags & MOE_STAGE_MASK) >> 8;
+    if (sel && nstages > 8) return MOE_EINVAL;
+    auto run = [&](int s) { return sel == 0 || ((sel >> s) & 1u); };
+
+    char *base = static_cast<char *>(ws);
+    double *logits = reinterpret_cast<double *>(base + L.logits);
+    int8_t *xq = reinterpret_cast<int8_t *>(base + L.xq);
+    float *xd = reinterpret_cast<float *>(base + L.xd);
+    const int H = shape->hidden, nb = H / 32, E = shape->n_experts, k = shape->top_k;
+    int stage = 0;
+    if (T <= kGemvMaxT) {
+        if (run(stage) && launch_router_logits(x, T, H, gate_w, E, logits, xq, xd, stream)) return MOE_EHIP;
+        stage++;
+    } else {
+        if (run(stage) && launch_router_logits_tiled(x, T, H, gate_w, E, logits, stream)) return MOE_EHIP;
+        stage++;
+        if (run(stage) && launch_quant(x, T, H, xq, xd, stream)) return MOE_EHIP;
+        stage++;
+    }
+    for (int c0 = 0; c0 < T; c0 += kGemvMaxT) {
+        GemvArgs a{};
+        a.T = (T - c0 < kGemvMaxT) ? T - c0 : kGemvMaxT;
+        a.H = H; a.I = shape->inter; a.E = E; a.wbits = shape->wbits; a.n_shared = shape->n_shared;
+        route_cfg(*shape, a.rc);
+        a.logits = logits + (size_t)c0 * E; a.bias = bias; a.single = -1;
+        a.routed = *routed;
+        if (shared) a.shared = *shared;
+        a.xq = xq + (size_t)c0 * H; a.xd = xd + (size_t)c0 * nb;
+        a.plan = reinterpret_cast<int *>(base + L.plan);
+        a.qh = reinterpret_cast<int8_t *>(base + L.qh);
+        a.dh = reinterpret_cast<float *>(base + L.dh);
+        a.y = y + (size_t)c0 * H;
+        a.idx_out = idx_out ? idx_out + (size_t)c0 * k : nullptr;
+        a.w_out = w_out ? w_out + (size_t)c0 * k : nullptr;
+        a.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+        if (run(stage) && launch_gate_up(a, stream)) return MOE_EHIP;
+        stage++;
+        if (run(stage) && launch_down(a, stream)) return MOE_EHIP;
+        stage++;
+    }
+    return MOE_OK;
+}
+
+int moe_rmsnorm(const float *x, const float *g, double eps, int32_t T, int32_t H, float *out, hipStream_t stream)
+{
+    if (T < 0 || H <= 0 || !(eps >= 0.0)) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !g || !out) return MOE_EINVAL;
+    return hip_rc(launch_rmsnorm(x, g, eps, T, H, out, stream));
+}
+
+size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E)
+{
+    if (T < 0 || k <= 0 || E <= 0) return 0;
+    const size_t tiles = ((size_t)T * k + 255) / 256;
+    return align256(sizeof(int32_t) * (tiles ? tiles : 1) * E);
+}
+
+int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *perm, int32_t *off, int32_t *inv,
+                void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (T < 0 || k <= 0 || E <= 0) return MOE_EINVAL;
+    if (E > kMaxExperts) return MOE_EUNSUPPORTED;
+    if (!off || !ws || (T > 0 && (!idx || !perm || !inv))) return MOE_EINVAL;
+    if (ws_bytes < moe_permute_workspace_bytes(T, k, E)) return MOE_EWORKSPACE;
+    return hip_rc(launch_permute(idx, T, k, E, perm, off, inv, static_cast<int32_t *>(ws), stream));
+}
+
+} // extern "C"

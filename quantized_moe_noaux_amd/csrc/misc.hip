@@ -1,0 +1,180 @@
+// RMSNorm of the decode stack, the block-dot test export and the token
+// permutation of the grouped path.
+#include "moe_dev.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- rmsnorm
+// out = x / sqrt(mean(x^2) + eps) * g, one workgroup per row; the sum of
+// squares and the scaling in fp64 with a fixed reduction order.
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, const float *__restrict__ g,
+                                                 double eps, int H, float *out)
+{
+    __shared__ double red[4];
+    const float *xr = x + (size_t)blockIdx.x * H;
+    double ss = 0.0;
+    for (int j = threadIdx.x; j < H; j += 256) ss = fma((double)xr[j], (double)xr[j], ss);
+    ss = wave_sum_d(ss);
+    if (lane_id() == 0) red[wave_id()] = ss;
+    __syncthreads();
+    const double r = 1.0 / sqrt(((red[0] + red[1]) + (red[2] + red[3])) / H + eps);
+    for (int j = threadIdx.x; j < H; j += 256)
+        out[(size_t)blockIdx.x * H + j] = (float)((double)xr[j] * r * (double)g[j]);
+}
+
+int launch_rmsnorm(const float *x, const float *g, double eps, int T, int H, float *out, hipStream_t st)
+{
+    k_rmsnorm<<<T, 256, 0, st>>>(x, g, eps, H, out);
+    return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------- block dots
+// One thread per (token, row, 16-byte chunk): the same chunk arithmetic the
+// expert kernels use, with the activation block sums formed on the fly.
+template <int WB>
+__global__ __launch_bounds__(256) void k_block_dots(const uint8_t *__restrict__ codes, int rows, int D,
+                                                    const int8_t *__restrict__ q, int T, int32_t *__restrict__ out)
+{
+    const int cpr = D * WB / 128;  // chunks per row
+    const long n = (long)T * rows * cpr;
+    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= n) return;
+    const int c = (int)(gid % cpr);
+    const long tr = gid / cpr;
+    const int r = (int)(tr % rows), t = (int)(tr / rows);
+    const uint4 w = *reinterpret_cast<const uint4 *>(codes + ((size_t)r * cpr + c) * 16);
+    const int8_t *qt = q + (size_t)t * D;
+    int32_t *o = out + ((size_t)t * rows + r) * (D / 32);
+    if constexpr (WB == 8) {
+        Act<8> A;
+        const uint4 v = reinterpret_cast<const uint4 *>(qt)[c];
+        A.a[0] = v.x; A.a[1] = v.y; A.a[2] = v.z; A.a[3] = v.w;
+        A.d = 0.f;
+        // two chunks make one block: the even chunk adds its partner's half
+        if (c & 1) return;
+        const uint4 w2 = *reinterpret_cast<const uint4 *>(codes + ((size_t)r * cpr + c + 1) * 16);
+        Act<8> B;
+        const uint4 v2 = reinterpret_cast<const uint4 *>(qt)[c + 1];
+        B.a[0] = v2.x; B.a[1] = v2.y; B.a[2] = v2.z; B.a[3] = v2.w;
+        B.d = 0.f;
+        o[c >> 1] = A.isum(w) + B.isum(w2);
+    } else if constexpr (WB == 4) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(qt + 32 * c);
+        const uint4 v0 = p[0], v1 = p[1];
+        uint32_t nn[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        int qs = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) qs = sdot4(nn[i], 0x01010101u, qs);
+        Act<4> A;
+        A.set(nn, 0.f, qs);
+        o[c] = A.isum(w);
+    } else {
+        const uint4 *p = reinterpret_cast<const uint4 *>(qt + 64 * c);
+        uint32_t nn[16];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint4 v = p[i];
+            nn[4 * i] = v.x; nn[4 * i + 1] = v.y; nn[4 * i + 2] = v.z; nn[4 * i + 3] = v.w;
+        }
+        int qs0 = 0, qs1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            qs0 = sdot4(nn[i], 0x01010101u, qs0);
+            qs1 = sdot4(nn[8 + i], 0x01010101u, qs1);
+        }
+        Act<2> A;
+        A.set(nn, 0.f, 0.f, qs0, qs1);
+        int i0, i1;
+        A.isum2(w, i0, i1);
+        o[2 * c] = i0;
+        o[2 * c + 1] = i1;
+    }
+}
+
+int launch_block_dots(int wbits, const uint8_t *codes, int rows, int D, const int8_t *q, int T,
+                      int32_t *out, hipStream_t st)
+{
+    const long n = (long)T * rows * (D * wbits / 128);
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (wbits == 8) k_block_dots<8><<<grid, 256, 0, st>>>(codes, rows, D, q, T, out);
+    else if (wbits == 4) k_block_dots<4><<<grid, 256, 0, st>>>(codes, rows, D, q, T, out);
+    else k_block_dots<2><<<grid, 256, 0, st>>>(codes, rows, D, q, T, out);
+    return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------- permutation
+// Stable counting sort of the T*k assignments by expert (batch-union MoE,
+// GeekNews #31297 implemented features), in three launches:
+//  k_perm_count  tile j of 256 assignments writes its per-expert counts
+//  k_perm_scan   one block: per expert, running sums over tiles, then the
+//                exclusive scan over experts gives off[] and tile bases
+//  k_perm_place  each assignment's row = its tile base + the number of
+//                earlier assignments of the same expert in its tile
+__global__ __launch_bounds__(256) void k_perm_count(const int32_t *__restrict__ idx, int n, int E,
+                                                    int32_t *__restrict__ cnt /*[tiles][E]*/)
+{
+    __shared__ int c[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += 256) c[e] = 0;
+    __syncthreads();
+    const int a = blockIdx.x * 256 + threadIdx.x;
+    if (a < n) atomicAdd(&c[idx[a]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) cnt[(size_t)blockIdx.x * E + e] = c[e];
+}
+
+__global__ __launch_bounds__(512) void k_perm_scan(int tiles, int E, int32_t *__restrict__ cnt,
+                                                   int32_t *__restrict__ off)
+{
+    __shared__ int tot[kMaxExperts + 1];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E)
+        for (int j = 0; j < tiles; j++) {
+            const int v = cnt[(size_t)j * E + e];
+            cnt[(size_t)j * E + e] = run;
+            run += v;
+        }
+    if (e < E) tot[e] = run;
+    __syncthreads();
+    if (e == 0) {
+        int s = 0;
+        for (int i = 0; i < E; i++) { const int v = tot[i]; tot[i] = s; s += v; }
+        tot[E] = s;
+    }
+    __syncthreads();
+    if (e < E) {
+        off[e] = tot[e];
+        for (int j = 0; j < tiles; j++) cnt[(size_t)j * E + e] += tot[e];
+    }
+    if (e == 0) off[E] = tot[E];
+}
+
+__global__ __launch_bounds__(256) void k_perm_place(const int32_t *__restrict__ idx, int n, int E,
+                                                    const int32_t *__restrict__ base, int32_t *__restrict__ perm,
+                                                    int32_t *__restrict__ inv)
+{
+    __shared__ int s_e[256];
+    const int a0 = blockIdx.x * 256, a = a0 + threadIdx.x;
+    s_e[threadIdx.x] = (a < n) ? idx[a] : -1;
+    __syncthreads();
+    if (a >= n) return;
+    const int e = s_e[threadIdx.x];
+    int r = 0;
+    for (int j = 0; j < (int)threadIdx.x; j++) r += (s_e[j] == e);
+    const int row = base[(size_t)blockIdx.x * E + e] + r;
+    perm[row] = a;
+    inv[a] = row;
+}
+
+int launch_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32_t *off, int32_t *inv,
+                   int32_t *scratch, hipStream_t st)
+{
+    const int n = T * k, tiles = (n + 255) / 256;
+    if (tiles) k_perm_count<<<tiles, 256, 0, st>>>(idx, n, E, scratch);
+    k_perm_scan<<<1, 512, 0, st>>>(tiles, E, scratch, off);
+    if (tiles) k_perm_place<<<tiles, 256, 0, st>>>(idx, n, E, scratch, perm, inv);
+    return (int)hipGetLastError();
+}
+
+} // namespace moe

@@ -1,0 +1,220 @@
+// Device building blocks shared by the MoE kernels (gfx950, wave64).
+//
+// Integer dots.  A weight row is consumed in 16-byte "chunks" (one
+// global_load_dwordx4 per lane).  A chunk holds 128/wbits codes: 16 int8
+// codes (half an activation block), 32 int4 codes (one block) or 64 int2
+// codes (two blocks).  Packed codes are turned into non-negative bytes by an
+// XOR that maps two's complement c to c + 2^(b-1) (0..15 for int4, 0..3 for
+// int2) and multiplied against the int8 activations with v_dot4_i32_i8; the
+// offset is removed with the activation block sum:
+//     sum c*q = sum (c + 2^(b-1))*q - 2^(b-1) * sum q.
+// The activation bytes are pre-permuted once (v_perm_b32) so that each
+// masked nibble / 2-bit field lines up with its activation byte.  Every
+// block sum is exact in int32, as the integer-dot formulation requires
+// (GeekNews #31297, implemented features: Q8_0-style int8 activations,
+// integer-dot kernels, packed int4 / int2 weights with per-row scales).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
+{
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ double wave_max_d(double v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+    return v;
+}
+
+// ---------------------------------------------------------------- activation chunks
+// Activation operand of one weight chunk, held in registers.
+template <int WB> struct Act;
+
+// int8 weights: 16 codes = half a block; activations in natural order.
+template <> struct Act<8> {
+    uint32_t a[4];
+    float d;
+    __device__ __forceinline__ void load(const int8_t *q, const float *dblk, int chunk)
+    {
+        uint4 v = *reinterpret_cast<const uint4 *>(q + 16 * chunk);
+        a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
+        d = dblk[chunk >> 1];
+    }
+    __device__ __forceinline__ int isum(const uint4 &w) const
+    {
+        int acc = sdot4(w.x, a[0], 0);
+        acc = sdot4(w.y, a[1], acc);
+        acc = sdot4(w.z, a[2], acc);
+        return sdot4(w.w, a[3], acc);
+    }
+    __device__ __forceinline__ float dot(const uint4 &w) const { return d * (float)isum(w); }
+};
+
+// int4 weights: 32 codes = one block.  Per weight dword (8 codes) the even
+// codes meet activation bytes {0,2,4,6} and the odd codes {1,3,5,7}.
+template <> struct Act<4> {
+    uint32_t a[8];
+    float d;
+    int qs;
+    __device__ __forceinline__ void set(const uint32_t *n, float d_, int qs_)
+    {
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            a[2 * k] = perm(n[2 * k + 1], n[2 * k], 0x06040200u);
+            a[2 * k + 1] = perm(n[2 * k + 1], n[2 * k], 0x07050301u);
+        }
+        d = d_;
+        qs = qs_;
+    }
+    __device__ __forceinline__ void load(const int8_t *q, const float *dblk, int chunk)
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(q + 32 * chunk);
+        uint4 v0 = p[0], v1 = p[1];
+        uint32_t n[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        int qs = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) qs = sdot4(n[i], 0x01010101u, qs);  // block sum of q
+        set(n, dblk[chunk], qs);
+    }
+    __device__ __forceinline__ int isum(const uint4 &w) const
+    {
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        int acc = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            uint32_t t = ww[k] ^ 0x88888888u;
+            acc = sdot4(t & 0x0F0F0F0Fu, a[2 * k], acc);
+            acc = sdot4((t >> 4) & 0x0F0F0F0Fu, a[2 * k + 1], acc);
+        }
+        return acc - 8 * qs;
+    }
+    __device__ __forceinline__ float dot(const uint4 &w) const { return d * (float)isum(w); }
+};
+
+// int2 weights: 64 codes = two blocks.  Weight dword k holds codes
+// 16k + 4j + i at byte j, bits 2i; field i of all four bytes meets the
+// activation bytes {i, 4+i, 8+i, 12+i} (a 4x4 byte transpose).
+template <> struct Act<2> {
+    uint32_t a[16];
+    float d0, d1;
+    int qs0, qs1;
+    __device__ __forceinline__ void set(const uint32_t *n, float d0_, float d1_, int qs0_, int qs1_)
+    {
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            uint32_t q0 = n[4 * k], q1 = n[4 * k + 1], q2 = n[4 * k + 2], q3 = n[4 * k + 3];
+            uint32_t lo01 = perm(q1, q0, 0x05010400u), lo23 = perm(q3, q2, 0x05010400u);
+            uint32_t hi01 = perm(q1, q0, 0x07030602u), hi23 = perm(q3, q2, 0x07030602u);
+            a[4 * k + 0] = perm(lo23, lo01, 0x05040100u);
+            a[4 * k + 1] = perm(lo23, lo01, 0x07060302u);
+            a[4 * k + 2] = perm(hi23, hi01, 0x05040100u);
+            a[4 * k + 3] = perm(hi23, hi01, 0x07060302u);
+        }
+        d0 = d0_; d1 = d1_; qs0 = qs0_; qs1 = qs1_;
+    }
+    __device__ __forceinline__ void load(const int8_t *q, const float *dblk, int chunk)
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(q + 64 * chunk);
+        uint32_t n[16];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint4 v = p[i];
+            n[4 * i] = v.x; n[4 * i + 1] = v.y; n[4 * i + 2] = v.z; n[4 * i + 3] = v.w;
+        }
+        int qs0 = 0, qs1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            qs0 = sdot4(n[i], 0x01010101u, qs0);
+            qs1 = sdot4(n[8 + i], 0x01010101u, qs1);
+        }
+        set(n, dblk[2 * chunk], dblk[2 * chunk + 1], qs0, qs1);
+    }
+    __device__ __forceinline__ int part(uint32_t w, int k) const
+    {
+        uint32_t t = w ^ 0xAAAAAAAAu;
+        int acc = sdot4(t & 0x03030303u, a[4 * k], 0);
+        acc = sdot4((t >> 2) & 0x03030303u, a[4 * k + 1], acc);
+        acc = sdot4((t >> 4) & 0x03030303u, a[4 * k + 2], acc);
+        return sdot4((t >> 6) & 0x03030303u, a[4 * k + 3], acc);
+    }
+    __device__ __forceinline__ void isum2(const uint4 &w, int &i0, int &i1) const
+    {
+        i0 = part(w.x, 0) + part(w.y, 1) - 2 * qs0;
+        i1 = part(w.z, 2) + part(w.w, 3) - 2 * qs1;
+    }
+    __device__ __forceinline__ float dot(const uint4 &w) const
+    {
+        int i0, i1;
+        isum2(w, i0, i1);
+        return d0 * (float)i0 + d1 * (float)i1;
+    }
+};
+
+// ---------------------------------------------------------------- quantiser
+// Q8_0-style block quantiser spread over 8 consecutive lanes, 4 elements
+// per lane (lanes 8j..8j+7 of a wave hold one block of 32).  d = amax/127
+// and q = rint(x/d) use IEEE fp32 division and round-half-even (the build
+// keeps -fno-fast-math, so '/' is the correctly rounded division and rintf
+// is v_rndne_f32).  Returns the 4 codes packed in a dword; the block's d
+// comes back in every lane of the 8.
+__device__ __forceinline__ uint32_t quant_block8(float4 v, float &d_out)
+{
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    float d = amax / 127.0f;
+    float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        float r = (d == 0.0f) ? 0.0f : rintf(e[j] / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        packed |= ((uint32_t)((int)r & 0xFF)) << (8 * j);
+    }
+    d_out = d;
+    return packed;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g / (1.0f + expf(-g)) * u;
+}
+
+} // namespace moe

@@ -1,0 +1,111 @@
+// Host-side internals shared by the MoE entry points and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxGroups = 64;
+constexpr int kMaxTopK = 32;
+constexpr int kGemvMaxT = 8;          // the batch-union GEMV path takes T <= 8
+constexpr int kGemvMaxLdsAct = 64 * 1024;
+
+// Router layout: each lane of a wave holds `epl` consecutive experts and a
+// group spans `lpg` lanes (a power of two), so group top-2 sums are lane
+// butterflies.  Chosen on the host by route_cfg().
+struct RouteCfg {
+    int E, G, tg, k, epl, lpg;
+    float rsf;
+};
+
+bool route_cfg(const moe_shape_t &s, RouteCfg &rc);
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Packing of one weight row into 16-byte chunks processed by a wave: a wave
+// tile covers `rw` rows = 64 * `cpl` chunks (cpl chunks per lane).
+struct ChunkCfg {
+    int cpr;  // chunks per row
+    int rw;   // rows per wave tile
+    int cpl;  // chunks per lane
+};
+bool chunk_cfg(int in_dim, int wbits, ChunkCfg &cc);
+
+// Plan of the batch-union GEMV path (written to the workspace by the
+// gate/up kernel, read by the down/combine kernel).  Flat int32 array:
+//   [0]                n_slots
+//   [1 ..]             slot_e[S]    expert of slot (-1 = shared)
+//                      slot_n[S]    tokens routed to slot
+//                      slot_p0[S]   first pair of slot
+//                      pair_t[P]    token of pair
+//                      pair_w[P]    combine weight of pair (fp32 bits)
+struct PlanDims {
+    int S, P;
+    int o_e, o_n, o_p0, o_t, o_w, words;
+};
+inline PlanDims plan_dims(int T, int k, int n_shared, bool single)
+{
+    PlanDims d;
+    d.S = single ? 1 : T * k + n_shared;
+    d.P = single ? T : T * (k + n_shared);
+    d.o_e = 1;
+    d.o_n = d.o_e + d.S;
+    d.o_p0 = d.o_n + d.S;
+    d.o_t = d.o_p0 + d.S;
+    d.o_w = d.o_t + d.P;
+    d.words = d.o_w + d.P;
+    return d;
+}
+
+struct GemvWs {
+    size_t logits, xq, xd, plan, qh, dh, total;
+};
+GemvWs gemv_ws(const moe_shape_t &s, int T, bool single);
+
+// ---------------------------------------------------------------- launchers
+// (each returns hipGetLastError() as an int after its launch)
+int launch_router_logits(const float *x, int T, int H, const float *gate_w, int E, double *logits,
+                         int8_t *xq, float *xd, hipStream_t st);
+int launch_router_logits_tiled(const float *x, int T, int H, const float *gate_w, int E, double *logits,
+                               hipStream_t st);
+int launch_topk(const RouteCfg &rc, const double *logits, const float *bias, int T, int32_t *idx,
+                float *w, hipStream_t st);
+int launch_quant(const float *x, int T, int D, int8_t *q, float *d, hipStream_t st);
+
+struct GemvArgs {
+    // shape
+    int T, H, I, E, wbits, n_shared;
+    RouteCfg rc;
+    // routing (logits == nullptr: single-expert mode on expert `single`)
+    const double *logits;
+    const float *bias;
+    int single;
+    // weights
+    moe_weights_t routed, shared;
+    // int8 activations of x (natural order) and their block scales
+    const int8_t *xq;
+    const float *xd;
+    // workspace: plan and the quantised h of every (slot, token) pair
+    int *plan;
+    int8_t *qh;
+    float *dh;
+    // layer outputs
+    float *y;
+    int32_t *idx_out;
+    float *w_out;
+    int accumulate;
+};
+int launch_gate_up(const GemvArgs &a, hipStream_t st);
+int launch_down(const GemvArgs &a, hipStream_t st);
+
+int launch_rmsnorm(const float *x, const float *g, double eps, int T, int H, float *out, hipStream_t st);
+int launch_block_dots(int wbits, const uint8_t *codes, int rows, int D, const int8_t *q, int T,
+                      int32_t *out, hipStream_t st);
+int launch_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32_t *off, int32_t *inv,
+                   int32_t *scratch, hipStream_t st);
+
+} // namespace moe

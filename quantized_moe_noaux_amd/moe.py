@@ -1,0 +1,185 @@
+"""ctypes binding of libmoe.so (include/moe.h), same names as the C ABI.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe.so.  Tensors are torch tensors on the GPU (PyTorch provides device
+memory and streams); each wrapper checks dtype / device / contiguity, passes
+data_ptr()s and the current HIP stream, and raises MoeError on a non-zero
+return code.  If libmoe.so is missing the import fails loudly: there is no
+fallback implementation.
+"""
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GROUPED, MOE_ACCUMULATE = 0, 1, 2, 4
+
+
+def MOE_STAGE(n):
+    return 1 << (8 + n)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__("%s failed: %s (%d)" % (fn, strerror(code), code))
+        self.code = code
+
+
+class moe_shape_t(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_float)]
+
+
+class moe_weights_t(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(_build.LIB):
+        raise ImportError("libmoe.so is not built (%s); run __graft_entry__.build()" % _build.LIB)
+    L = ctypes.CDLL(_build.LIB)
+    vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_route": (ctypes.c_int, [P(moe_shape_t), vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_route_workspace_bytes": (sz, [P(moe_shape_t), i32]),
+        "moe_quant_act": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
+        "moe_block_dots": (ctypes.c_int, [i32, vp, i32, i32, vp, i32, vp, vp]),
+        "moe_expert_ffn": (ctypes.c_int, [P(moe_shape_t), P(moe_weights_t), i32, vp, vp, i32, vp, vp, sz, vp]),
+        "moe_layer_forward": (ctypes.c_int, [P(moe_shape_t), vp, i32, vp, vp, P(moe_weights_t),
+                                             P(moe_weights_t), vp, vp, vp, u32, vp, sz, vp]),
+        "moe_workspace_bytes": (sz, [P(moe_shape_t), i32, u32]),
+        "moe_layer_stage_count": (ctypes.c_int, [P(moe_shape_t), i32, u32]),
+        "moe_rmsnorm": (ctypes.c_int, [vp, vp, ctypes.c_double, i32, i32, vp, vp]),
+        "moe_permute": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "moe_permute_workspace_bytes": (sz, [i32, i32, i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
+
+
+lib = _load()
+
+
+def strerror(code):
+    return lib.moe_strerror(code).decode()
+
+
+def _chk(fn, rc):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def _ptr(t, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("expected %s, got %s" % (dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def shape(hidden, inter, n_experts, n_group, topk_group, top_k, n_shared, wbits, rsf):
+    return moe_shape_t(hidden, inter, n_experts, n_group, topk_group, top_k, n_shared, wbits, rsf)
+
+
+def shape_of(wl, rsf=None):
+    """moe_shape_t from an object with the workload fields (hidden, inter, ...)."""
+    return shape(wl.hidden, wl.inter, wl.n_experts, wl.n_group, wl.topk_group, wl.top_k,
+                 wl.n_shared, wl.wbits, wl.rsf if rsf is None else rsf)
+
+
+def weights(w):
+    """moe_weights_t from an object with gate/up/down (uint8) and *_s (float32) tensors."""
+    return moe_weights_t(_ptr(w.gate, torch.uint8), _ptr(w.up, torch.uint8), _ptr(w.down, torch.uint8),
+                         _ptr(w.gate_s, torch.float32), _ptr(w.up_s, torch.float32),
+                         _ptr(w.down_s, torch.float32))
+
+
+def workspace(nbytes, device="cuda"):
+    """A device buffer for the *_workspace_bytes sizes (torch keeps 256-byte alignment)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route_workspace_bytes(sh, T):
+    return lib.moe_route_workspace_bytes(ctypes.byref(sh), T)
+
+
+def moe_route(sh, x, gate_w, bias, idx, w, ws, stream=None):
+    _chk("moe_route", lib.moe_route(ctypes.byref(sh), _ptr(x, torch.float32), x.shape[0],
+                                    _ptr(gate_w, torch.float32), _ptr(bias, torch.float32),
+                                    _ptr(idx, torch.int32), _ptr(w, torch.float32),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_quant_act(x, q, d, stream=None):
+    T, D = x.shape
+    _chk("moe_quant_act", lib.moe_quant_act(_ptr(x, torch.float32), T, D, _ptr(q, torch.int8),
+                                            _ptr(d, torch.float32), _stream(stream)))
+
+
+def moe_block_dots(wbits, codes, D, q, out, stream=None):
+    _chk("moe_block_dots", lib.moe_block_dots(wbits, _ptr(codes, torch.uint8), codes.shape[0], D,
+                                              _ptr(q, torch.int8), q.shape[0], _ptr(out, torch.int32),
+                                              _stream(stream)))
+
+
+def moe_expert_ffn(sh, w, expert, q, d, y, ws, stream=None):
+    wt = weights(w)
+    _chk("moe_expert_ffn", lib.moe_expert_ffn(ctypes.byref(sh), ctypes.byref(wt), expert,
+                                              _ptr(q, torch.int8), _ptr(d, torch.float32), q.shape[0],
+                                              _ptr(y, torch.float32), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_workspace_bytes(sh, T, flags=0):
+    return lib.moe_workspace_bytes(ctypes.byref(sh), T, flags)
+
+
+def moe_layer_stage_count(sh, T, flags=0):
+    return lib.moe_layer_stage_count(ctypes.byref(sh), T, flags)
+
+
+def moe_layer_forward(sh, x, gate_w, bias, routed, shared, y, ws, idx_out=None, w_out=None, flags=0,
+                      stream=None):
+    rw = weights(routed)
+    sw = weights(shared) if shared is not None else None
+    _chk("moe_layer_forward", lib.moe_layer_forward(
+        ctypes.byref(sh), _ptr(x, torch.float32), x.shape[0], _ptr(gate_w, torch.float32),
+        _ptr(bias, torch.float32), ctypes.byref(rw), ctypes.byref(sw) if sw is not None else None,
+        _ptr(y, torch.float32), _ptr(idx_out, torch.int32), _ptr(w_out, torch.float32), flags,
+        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_rmsnorm(x, g, eps, out, stream=None):
+    T, H = x.shape
+    _chk("moe_rmsnorm", lib.moe_rmsnorm(_ptr(x, torch.float32), _ptr(g, torch.float32), eps, T, H,
+                                        _ptr(out, torch.float32), _stream(stream)))
+
+
+def moe_permute_workspace_bytes(T, k, E):
+    return lib.moe_permute_workspace_bytes(T, k, E)
+
+
+def moe_permute(idx, E, perm, off, inv, ws, stream=None):
+    T, k = idx.shape
+    _chk("moe_permute", lib.moe_permute(_ptr(idx, torch.int32), T, k, E, _ptr(perm, torch.int32),
+                                        _ptr(off, torch.int32), _ptr(inv, torch.int32), _ptr(ws),
+                                        ws.numel(), _stream(stream)))

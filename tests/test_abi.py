@@ -1,0 +1,113 @@
+"""The C ABI library without a GPU: it loads, exports what include/moe.h
+declares, sizes workspaces, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    from quantized_moe_noaux_amd import moe
+    return moe
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for f in ("moe_route", "moe_quant_act", "moe_expert_ffn", "moe_layer_forward", "moe_workspace_bytes",
+              "moe_rmsnorm", "moe_block_dots", "moe_permute", "moe_strerror"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(m):
+    lib = ctypes.CDLL(m._build.LIB)
+    missing = [f for f in header_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+
+
+def test_strerror(m):
+    assert m.strerror(0) == "success"
+    assert m.strerror(m.MOE_EWORKSPACE) == "workspace too small"
+    assert m.strerror(99) == "unknown error"
+
+
+def big_shape(m, **kw):
+    d = dict(hidden=6144, inter=2048, n_experts=256, n_group=8, topk_group=4, top_k=8, n_shared=1,
+             wbits=4, rsf=2.5)
+    d.update(kw)
+    return m.shape(**d)
+
+
+def test_workspace_sizes(m):
+    sh = big_shape(m)
+    ws1 = m.moe_workspace_bytes(sh, 1)
+    assert ws1 > 0 and ws1 % 256 == 0
+    assert m.moe_workspace_bytes(sh, 3) > ws1
+    assert m.moe_route_workspace_bytes(sh, 2048) == 2048 * 256 * 8
+    assert m.moe_workspace_bytes(big_shape(m, wbits=3), 1) == 0          # unsupported shape
+    assert m.moe_workspace_bytes(big_shape(m, n_group=7), 1) == 0        # E % G != 0
+    assert m.moe_permute_workspace_bytes(2048, 8, 256) == 64 * 256 * 4
+
+
+def test_stage_count(m):
+    sh = big_shape(m)
+    assert m.moe_layer_stage_count(sh, 1) == 3          # router+quant, gate/up, down
+    assert m.moe_layer_stage_count(sh, 0) == 0
+    assert m.moe_layer_stage_count(big_shape(m, top_k=40), 1) < 0
+
+
+NULL = None
+
+
+def call_layer(m, sh, T=1, flags=0, ws_bytes=1 << 20, x=1 << 12, y=2 << 12, shared=True, gate_w=3 << 12,
+               bias=4 << 12):
+    w = m.moe_weights_t(16, 32, 48, 64, 80, 96)
+    sw = m.moe_weights_t(16, 32, 48, 64, 80, 96) if shared else None
+    return m.lib.moe_layer_forward(ctypes.byref(sh), x, T, gate_w, bias, ctypes.byref(w),
+                                   ctypes.byref(sw) if sw else None, y, None, None, flags, 1 << 20,
+                                   ws_bytes, None)
+
+
+def test_layer_argument_errors_launch_nothing(m):
+    sh = big_shape(m)
+    assert call_layer(m, sh, T=-1) == m.MOE_EINVAL
+    assert call_layer(m, sh, ws_bytes=16) == m.MOE_EWORKSPACE
+    assert call_layer(m, sh, x=0) == m.MOE_EINVAL
+    assert call_layer(m, sh, x=(1 << 12) + 4) == m.MOE_EINVAL              # x not 16-byte aligned
+    assert call_layer(m, sh, x=1 << 12, y=1 << 12) == m.MOE_EINVAL         # y aliases x
+    assert call_layer(m, sh, shared=False) == m.MOE_EINVAL                 # n_shared = 1 needs it
+    assert call_layer(m, sh, flags=3) == m.MOE_EINVAL
+    assert call_layer(m, sh, flags=1 << 20) == m.MOE_EINVAL
+    assert call_layer(m, big_shape(m, wbits=3)) == m.MOE_EUNSUPPORTED
+    assert call_layer(m, big_shape(m, n_shared=2)) == m.MOE_EUNSUPPORTED
+    assert call_layer(m, big_shape(m, hidden=6000)) == m.MOE_EINVAL       # not a multiple of 32
+    assert call_layer(m, big_shape(m, top_k=33, topk_group=8)) == m.MOE_EUNSUPPORTED
+    assert call_layer(m, big_shape(m, n_experts=1024, n_group=8)) == m.MOE_EUNSUPPORTED
+    assert call_layer(m, sh, T=0) == m.MOE_OK                               # no-op
+
+
+def test_other_entry_point_errors(m):
+    L = m.lib
+    assert L.moe_quant_act(1 << 12, 4, 48, 2 << 12, 3 << 12, None) == m.MOE_EINVAL   # D % 32
+    assert L.moe_quant_act(None, 4, 64, 2 << 12, 3 << 12, None) == m.MOE_EINVAL
+    assert L.moe_quant_act(None, 0, 64, None, None, None) == m.MOE_OK
+    assert L.moe_block_dots(3, 1 << 12, 4, 64, 2 << 12, 1, 3 << 12, None) == m.MOE_EUNSUPPORTED
+    assert L.moe_block_dots(2, 1 << 12, 4, 32, 2 << 12, 1, 3 << 12, None) == m.MOE_EUNSUPPORTED  # 8-byte rows
+    assert L.moe_rmsnorm(1 << 12, 2 << 12, -1.0, 1, 64, 3 << 12, None) == m.MOE_EINVAL
+    sh = big_shape(m)
+    assert L.moe_route(ctypes.byref(sh), 1 << 12, 1, 2 << 12, 3 << 12, 4 << 12, 5 << 12, 1 << 20, 8,
+                       None) == m.MOE_EWORKSPACE
+    w = m.moe_weights_t(16, 32, 48, 64, 80, 96)
+    assert L.moe_expert_ffn(ctypes.byref(sh), ctypes.byref(w), 256, 1 << 12, 2 << 12, 1, 3 << 12,
+                            1 << 20, 1 << 30, None) == m.MOE_EINVAL      # expert out of range
+    assert L.moe_permute(1 << 12, 4, 8, 600, 1 << 13, 1 << 14, 1 << 15, 1 << 20, 1 << 20,
+                         None) == m.MOE_EUNSUPPORTED

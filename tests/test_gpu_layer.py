@@ -1,0 +1,156 @@
+"""GPU parity of the whole MoE layer (and the single-expert entry point)
+against the CPU oracle, through the C ABI.  Expert indices are bit-exact;
+float outputs are held to max-abs error <= 1e-3 x max|ref|."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DevLayer, assert_close, dev_expert, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m(dev):
+    from quantized_moe_noaux_amd import moe
+    return moe
+
+
+def forward(m, L, T=None, flags=0, y=None, rsf=None):
+    wl = L.wl
+    T = L.x.shape[0] if T is None else T
+    sh = m.shape_of(wl, rsf=rsf)
+    dev = L.x.device
+    y = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev) if y is None else y
+    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, wl.top_k), dtype=torch.float32, device=dev)
+    ws = m.workspace(m.moe_workspace_bytes(sh, T, flags), dev)
+    m.moe_layer_forward(sh, L.x[:T], L.gate_w, L.bias, L.routed, L.shared, y, ws, idx, w, flags=flags)
+    torch.cuda.synchronize()
+    return y, idx.cpu().numpy(), w.cpu().numpy()
+
+
+def reference(L, T=None, rsf=None):
+    wl, H = L.wl, L.host
+    T = H.x.shape[0] if T is None else T
+    sh = oracle.shape_of(wl, rsf=rsf)
+    idx, _ = oracle.route(sh, H.x[:T], H.gate_w, H.bias)
+    return oracle.layer_forward(sh, H.x[:T], H.gate_w, H.bias, oracle.layer_experts(H, idx), H.shared)
+
+
+def check(m, L, T=None, flags=0):
+    y, idx, w = forward(m, L, T, flags)
+    y_ref, idx_ref, w_ref = reference(L, T)
+    assert np.array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=1e-6)
+    return assert_close(y.cpu().numpy(), y_ref)
+
+
+# ---------------------------------------------------------------- tiny layer
+@pytest.mark.parametrize("wbits", [4, 8, 2])
+def test_tiny_layer(dev, m, wbits):
+    L = DevLayer(synth.workload("tiny", wbits=wbits), dev)
+    for T in (8, 1, 3, 5):
+        check(m, L, T)
+
+
+def test_tiny_layer_no_shared(dev, m):
+    L = DevLayer(synth.workload("tiny", n_shared=0), dev)
+    check(m, L)
+
+
+def test_tiny_layer_chunked_tokens(dev, m):
+    # more tokens than one batch-union chunk: the GEMV path runs in chunks of 8
+    wl = synth.workload("tiny", T=21)
+    L = DevLayer(wl, dev)
+    assert m.moe_layer_stage_count(m.shape_of(wl), 21) == 2 + 2 * 3
+    check(m, L)
+
+
+# ---------------------------------------------------------------- full-size layers
+def test_decode_int4_full(dev, m):
+    L = DevLayer(synth.workload("decode_int4"), dev)
+    rel = check(m, L)
+    print("decode_int4: max rel err %.3g" % rel)
+
+
+def test_decode_int4_other_tokens(dev, m):
+    # a few more seeds of the decode token through the same weights
+    wl = synth.workload("decode_int4")
+    L = DevLayer(wl, dev)
+    for s in (1, 2, 3):
+        xs = synth.host_normals(s, synth.stream_id(0, synth.X), wl.hidden, 1.0).reshape(1, -1)
+        L.host.x = xs
+        L.x = to_dev(xs, dev)
+        check(m, L)
+
+
+def test_verify_int8_full(dev, m):
+    L = DevLayer(synth.workload("verify_int8"), dev)
+    rel = check(m, L)
+    print("verify_int8: max rel err %.3g" % rel)
+
+
+def test_stack_int2_layer(dev, m):
+    L = DevLayer(synth.workload("stack_int2"), dev, layer=5)
+    check(m, L)
+
+
+# ---------------------------------------------------------------- semantics
+def test_accumulate_flag(dev, m):
+    L = DevLayer(synth.workload("tiny"), dev)
+    y0 = torch.randn((8, 256), dtype=torch.float32, device=dev)
+    y_plain, _, _ = forward(m, L)
+    y_acc, _, _ = forward(m, L, flags=m.MOE_ACCUMULATE, y=y0.clone())
+    assert torch.equal(y_acc, y0 + y_plain)
+
+
+def test_deterministic(dev, m):
+    L = DevLayer(synth.workload("verify_int8"), dev)
+    a, ia, wa = forward(m, L)
+    b, ib, wb = forward(m, L)
+    assert torch.equal(a, b) and np.array_equal(ia, ib) and np.array_equal(wa, wb)
+
+
+def test_stages_one_by_one(dev, m):
+    wl = synth.workload("decode_int4")
+    L = DevLayer(wl, dev)
+    sh = m.shape_of(wl)
+    y_full, _, _ = forward(m, L)
+    n = m.moe_layer_stage_count(sh, 1)
+    ws = m.workspace(m.moe_workspace_bytes(sh, 1), dev)
+    y = torch.empty_like(y_full)
+    for s in range(n):
+        m.moe_layer_forward(sh, L.x, L.gate_w, L.bias, L.routed, L.shared, y, ws, flags=m.MOE_STAGE(s))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_full)
+
+
+def test_rsf_zero_is_shared_expert(dev, m):
+    wl = synth.workload("tiny")
+    L = DevLayer(wl, dev)
+    y0, _, _ = forward(m, L, rsf=0.0)
+    q, d = oracle.quant_act(L.host.x)
+    ysh = oracle.expert_ffn(oracle.shape_of(wl), L.host.shared, q, d)
+    assert_close(y0.cpu().numpy(), ysh)
+
+
+# ---------------------------------------------------------------- single expert
+@pytest.mark.parametrize("name,T", [("tiny", 8), ("decode_int4", 1), ("verify_int8", 3), ("tiny", 13)])
+def test_expert_ffn(dev, m, name, T):
+    wl = synth.workload(name)
+    H = synth.HostLayer(wl, T=T)
+    e = 3
+    ex = H.expert(e)
+    sh = m.shape_of(wl)
+    w = dev_expert(synth.HostExpert(*[getattr(ex, f)[None] for f in
+                                      ("gate", "up", "down", "gate_s", "up_s", "down_s")]), dev)
+    q, d = oracle.quant_act(H.x)
+    y = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
+    ws = m.workspace(m.moe_workspace_bytes(sh, T), dev)
+    shape1 = m.shape(wl.hidden, wl.inter, 1, 1, 1, 1, 0, wl.wbits, 1.0)
+    m.moe_expert_ffn(shape1, w, 0, to_dev(q, dev), to_dev(d, dev), y, ws)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), oracle.expert_ffn(oracle.shape_of(wl), ex, q, d))
