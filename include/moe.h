@@ -149,7 +149,8 @@ int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t exp
  *   y        [T][H] fp32 out (or accumulated into with MOE_ACCUMULATE)
  *   idx_out, w_out  [T][k] (nullable): the routing, as moe_route returns it
  *   flags    MOE_PATH_*, MOE_ACCUMULATE, MOE_STAGE(n)
- * ws: at least moe_workspace_bytes(shape, T, flags) bytes, 256-byte aligned. */
+ * ws: at least moe_workspace_bytes(shape, T, flags) bytes, 256-byte aligned;
+ *   calls that share a workspace must not overlap in time. */
 int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w,
                       const float *bias, const moe_weights_t *routed, const moe_weights_t *shared,
                       float *y, int32_t *idx_out, float *w_out, uint32_t flags,

@@ -49,6 +49,8 @@ def lib():
             build()
         L = ctypes.CDLL(LIB)
         vp, i32, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        L.oracle_num_threads.restype = i32
+        L.oracle_num_threads.argtypes = []
         L.oracle_code.restype = i32
         L.oracle_code.argtypes = [i32, vp, i32]
         L.oracle_route.restype = i32
@@ -88,6 +90,10 @@ def _expert_struct(ex):
     arrs = [_c(ex.gate, np.uint8), _c(ex.up, np.uint8), _c(ex.down, np.uint8),
             _c(ex.gate_s, np.float32), _c(ex.up_s, np.float32), _c(ex.down_s, np.float32)]
     return Expert(*[a.ctypes.data for a in arrs]), arrs
+
+
+def num_threads():
+    return lib().oracle_num_threads()
 
 
 def code(wbits, row, j):

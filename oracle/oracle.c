@@ -15,6 +15,19 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* threads an OpenMP region of the oracle uses (1 without OpenMP) */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 int oracle_code(int wbits, const uint8_t *row, int j)
 {

@@ -49,6 +49,7 @@ typedef struct {
 /* signed code j of a packed row (two's complement; int4: element 2m is the
  * low nibble of byte m; int2: element 4m+i sits at bits 2i..2i+1) */
 int oracle_code(int wbits, const uint8_t *row, int j);
+int oracle_num_threads(void);
 
 int oracle_route(const oracle_shape *sh, const float *x, int T, const float *gate_w,
                  const float *bias, int32_t *idx, float *w, double *margins);

@@ -8,7 +8,8 @@ namespace {
 
 bool al(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-int check_shape(const moe_shape_t *s)
+// Router-level checks (all that moe_route needs).
+int check_router_shape(const moe_shape_t *s)
 {
     if (!s) return MOE_EINVAL;
     if (s->hidden <= 0 || s->inter <= 0 || s->hidden % 32 || s->inter % 32) return MOE_EINVAL;
@@ -17,11 +18,19 @@ int check_shape(const moe_shape_t *s)
     if (s->top_k < 1 || s->top_k > s->topk_group * (s->n_experts / s->n_group)) return MOE_EINVAL;
     if (s->n_shared < 0) return MOE_EINVAL;
     if (!(s->routed_scaling_factor == s->routed_scaling_factor)) return MOE_EINVAL;  // NaN
-    if (s->wbits != 2 && s->wbits != 4 && s->wbits != 8) return MOE_EUNSUPPORTED;
-    if (s->n_shared > 1) return MOE_EUNSUPPORTED;
     if (s->n_experts > kMaxExperts || s->n_group > kMaxGroups || s->top_k > kMaxTopK) return MOE_EUNSUPPORTED;
     RouteCfg rc;
     if (!route_cfg(*s, rc)) return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+// Full layer checks: router plus the expert weight layout.
+int check_shape(const moe_shape_t *s)
+{
+    int rc = check_router_shape(s);
+    if (rc) return rc;
+    if (s->wbits != 2 && s->wbits != 4 && s->wbits != 8) return MOE_EUNSUPPORTED;
+    if (s->n_shared > 1) return MOE_EUNSUPPORTED;
     ChunkCfg cc;
     if (!chunk_cfg(s->hidden, s->wbits, cc) || !chunk_cfg(s->inter, s->wbits, cc)) return MOE_EUNSUPPORTED;
     return MOE_OK;
@@ -40,17 +49,9 @@ inline int hip_rc(int e) { return e ? MOE_EHIP : MOE_OK; }
 size_t route_ws(const moe_shape_t &s, int T) { return align256(sizeof(double) * (size_t)T * s.n_experts); }
 
 // The stage list of the GEMV path for T tokens: the router / quantiser
-// launch(es), then (gate/up, down) for every chunk of <= kGemvMaxT tokens.
-int gemv_stage_count(int T) { return (T <= kGemvMaxT ? 1 : 2) + 2 * ((T + kGemvMaxT - 1) / kGemvMaxT); }
-
-bool gemv_lds_fits(const moe_shape_t &s, int T)
-{
-    const int Tc = T < kGemvMaxT ? T : kGemvMaxT;
-    const PlanDims pd = plan_dims(Tc, s.top_k, s.n_shared, false);
-    const size_t lds = sizeof(int) * (size_t)((pd.words + 3) & ~3) + (size_t)pd.P * s.inter +
-                       2 * sizeof(float) * (size_t)pd.P * (s.inter / 32);
-    return lds <= (size_t)kGemvMaxLdsAct;
-}
+// launch(es), then
+// (plan, gate/up, down) for every chunk of Tc tokens.
+int gemv_stage_count(int T, int Tc) { return (T <= kGemvMaxT ? 1 : 2) + 3 * ((T + Tc - 1) / Tc); }
 
 } // namespace
 
@@ -70,14 +71,14 @@ const char *moe_strerror(int code)
 
 size_t moe_route_workspace_bytes(const moe_shape_t *shape, int32_t T)
 {
-    if (check_shape(shape) || T < 0) return 0;
+    if (check_router_shape(shape) || T < 0) return 0;
     return route_ws(*shape, T);
 }
 
 int moe_route(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w, const float *bias,
               int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    int rc = check_shape(shape);
+    int rc = check_router_shape(shape);
     if (rc) return rc;
     if (T < 0) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
@@ -117,7 +118,9 @@ size_t moe_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags)
 {
     (void)flags;
     if (check_shape(shape) || T < 0) return 0;
-    return gemv_ws(*shape, T, false).total;
+    const int Tc = gemv_chunk_tokens(*shape, T > 0 ? T : 1);
+    if (!Tc) return 0;
+    return gemv_ws(*shape, T, Tc, false).total;
 }
 
 int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags)
@@ -125,7 +128,9 @@ int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags)
     if (check_shape(shape) || T < 0) return -MOE_EINVAL;
     if (T == 0) return 0;
     if ((flags & 3u) == MOE_PATH_GROUPED) return -MOE_EUNSUPPORTED;
-    return gemv_stage_count(T);
+    const int Tc = gemv_chunk_tokens(*shape, T);
+    if (!Tc) return -MOE_EUNSUPPORTED;
+    return gemv_stage_count(T, Tc);
 }
 
 int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t expert, const int8_t *q,
@@ -137,13 +142,16 @@ int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t exp
     if (T < 0 || expert < 0 || expert >= shape->n_experts) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if (!q || !d || !y || !ws || !al(q, 16) || !al(d, 4) || !al(y, 4) || !al(ws, 256)) return MOE_EINVAL;
-    const GemvWs L = gemv_ws(*shape, T, true);
+    // single-expert mode stages at most Tc tokens per chunk, like the layer
+    const int Tc = gemv_chunk_tokens(*shape, T);
+    if (!Tc) return MOE_EUNSUPPORTED;
+    const GemvWs L = gemv_ws(*shape, T, Tc, true);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     char *base = static_cast<char *>(ws);
     const int H = shape->hidden, nb = H / 32;
-    for (int c0 = 0; c0 < T; c0 += kGemvMaxT) {
+    for (int c0 = 0; c0 < T; c0 += Tc) {
         GemvArgs a{};
-        a.T = (T - c0 < kGemvMaxT) ? T - c0 : kGemvMaxT;
+        a.T = (T - c0 < Tc) ? T - c0 : Tc;
         a.H = H; a.I = shape->inter; a.E = shape->n_experts; a.wbits = shape->wbits; a.n_shared = 0;
         route_cfg(*shape, a.rc);
         a.logits = nullptr; a.bias = nullptr; a.single = expert;
@@ -154,7 +162,7 @@ int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t exp
         a.dh = reinterpret_cast<float *>(base + L.dh);
         a.y = y + (size_t)c0 * H;
         a.accumulate = 0;
-        if (launch_gate_up(a, stream) || launch_down(a, stream)) return MOE_EHIP;
+        if (launch_plan(a, stream) || launch_gate_up(a, stream) || launch_down(a, stream)) return MOE_EHIP;
     }
     return MOE_OK;
 }
@@ -178,10 +186,12 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
     if ((idx_out == nullptr) != (w_out == nullptr)) return MOE_EINVAL;
     if (!al(x, 16) || !al(gate_w, 16) || !al(y, 4) || !al(ws, 256)) return MOE_EINVAL;
     if (x == y) return MOE_EINVAL;
-    if (!gemv_lds_fits(*shape, T)) return MOE_EUNSUPPORTED;
-    const GemvWs L = gemv_ws(*shape, T, false);
+    if (shape->hidden % kGemvDownRows) return MOE_EUNSUPPORTED;
+    const int Tc = gemv_chunk_tokens(*shape, T);
+    if (!Tc) return MOE_EUNSUPPORTED;
+    const GemvWs L = gemv_ws(*shape, T, Tc, false);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
-    const int nstages = gemv_stage_count(T);
+    const int nstages = gemv_stage_count(T, Tc);
     const uint32_t sel = (flags & MOE_STAGE_MASK) >> 8;
     if (sel && nstages > 8) return MOE_EINVAL;
     auto run = [&](int s) { return sel == 0 || ((sel >> s) & 1u); };
@@ -191,19 +201,9 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
     int8_t *xq = reinterpret_cast<int8_t *>(base + L.xq);
     float *xd = reinterpret_cast<float *>(base + L.xd);
     const int H = shape->hidden, nb = H / 32, E = shape->n_experts, k = shape->top_k;
-    int stage = 0;
-    if (T <= kGemvMaxT) {
-        if (run(stage) && launch_router_logits(x, T, H, gate_w, E, logits, xq, xd, stream)) return MOE_EHIP;
-        stage++;
-    } else {
-        if (run(stage) && launch_router_logits_tiled(x, T, H, gate_w, E, logits, stream)) return MOE_EHIP;
-        stage++;
-        if (run(stage) && launch_quant(x, T, H, xq, xd, stream)) return MOE_EHIP;
-        stage++;
-    }
-    for (int c0 = 0; c0 < T; c0 += kGemvMaxT) {
+    auto args = [&](int c0, int tc) {
         GemvArgs a{};
-        a.T = (T - c0 < kGemvMaxT) ? T - c0 : kGemvMaxT;
+        a.T = tc;
         a.H = H; a.I = shape->inter; a.E = E; a.wbits = shape->wbits; a.n_shared = shape->n_shared;
         route_cfg(*shape, a.rc);
         a.logits = logits + (size_t)c0 * E; a.bias = bias; a.single = -1;
@@ -217,6 +217,22 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
         a.idx_out = idx_out ? idx_out + (size_t)c0 * k : nullptr;
         a.w_out = w_out ? w_out + (size_t)c0 * k : nullptr;
         a.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+        return a;
+    };
+    int stage = 0;
+    if (T <= kGemvMaxT) {
+        if (run(stage) && launch_router_logits(x, T, H, gate_w, E, logits, xq, xd, stream)) return MOE_EHIP;
+        stage++;
+    } else {
+        if (run(stage) && launch_router_logits_tiled(x, T, H, gate_w, E, logits, stream)) return MOE_EHIP;
+        stage++;
+        if (run(stage) && launch_quant(x, T, H, xq, xd, stream)) return MOE_EHIP;
+        stage++;
+    }
+    for (int c0 = 0; c0 < T; c0 += Tc) {
+        GemvArgs a = args(c0, (T - c0 < Tc) ? T - c0 : Tc);
+        if (run(stage) && launch_plan(a, stream)) return MOE_EHIP;
+        stage++;
         if (run(stage) && launch_gate_up(a, stream)) return MOE_EHIP;
         stage++;
         if (run(stage) && launch_down(a, stream)) return MOE_EHIP;

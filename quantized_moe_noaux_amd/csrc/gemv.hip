@@ -6,20 +6,22 @@
 // per-row scales, evaluated as integer dots on Q8_0-style int8 activations.
 // wpnews.pro spec table: 8 routed + 1 shared expert per token.
 //
-// Two kernels:
-//  k_gate_up  one workgroup per (slot, 32-row tile) of the intermediate
-//             dimension, slot = one expert of the batch union (or the shared
-//             expert).  Every workgroup re-derives the routing of the batch
-//             from the fp64 logits (a few hundred instructions per token), so
-//             no extra launch or inter-workgroup counter is needed; block 0
-//             publishes it.  Per row: g and u as integer block dots streamed
-//             with 16-byte loads, h = silu(g) * u, and h quantised to int8 in
-//             blocks of 32 rows (one workgroup tile = one block).
-//  k_down     one workgroup per tile of output rows; for each row it streams
-//             the down rows of all slots, dots them with the slots' int8 h
-//             (staged once in LDS), scales by combine weight x row scale and
-//             sums per token in a fixed order: the combine is fused, no float
-//             atomics, results are run-to-run identical.
+// Per chunk of tokens, three launches after the router:
+//  k_plan       one workgroup routes the chunk's tokens (fp64 noaux_tc top-k)
+//               and publishes the batch-union plan: slots = the union of the
+//               selected experts in ascending order, then the shared expert;
+//               each slot lists its tokens (pairs) and their combine weights.
+//  k_gate_up_*  one workgroup per (slot, 32-row tile) of the intermediate
+//               dimension: g = W_gate x, u = W_up x as integer block dots,
+//               h = silu(g) * u, h quantised to int8 in blocks of 32 rows
+//               (one tile = one block).
+//  k_down_*     one workgroup per tile of output rows: for each row, the down
+//               rows of all slots dotted with the slots' int8 h, scaled by
+//               combine weight x row scale and summed per token in a fixed
+//               order.  The combine is fused; no float atomics, so results
+//               are run-to-run identical.
+// The *_sw ("row-sweep") kernels serve the production shapes; the *_rg
+// ("row-group") kernels take any other shape the ABI accepts.
 #include "moe_dev.h"
 #include "moe_internal.h"
 #include "topk_dev.h"
@@ -28,22 +30,18 @@ namespace moe {
 
 bool chunk_cfg(int in_dim, int wbits, ChunkCfg &cc)
 {
-    int rowbytes = in_dim * wbits / 8;
+    const int rowbytes = in_dim * wbits / 8;
     if (rowbytes % 16) return false;
     cc.cpr = rowbytes / 16;
-    int g = 64, a = cc.cpr;
-    while (a % g) g >>= 1;  // gcd(cpr, 64)
-    cc.rw = 64 / g;
-    cc.cpl = cc.rw * cc.cpr / 64;
-    return cc.rw <= 32 && (cc.cpl == 1 || cc.cpl == 2 || cc.cpl == 3 || cc.cpl == 6);
+    return true;
 }
 
-GemvWs gemv_ws(const moe_shape_t &s, int T, bool single)
+GemvWs gemv_ws(const moe_shape_t &s, int T, int Tc, bool single)
 {
     GemvWs w;
     const int H = s.hidden, I = s.inter, E = s.n_experts;
-    // plan and h buffers hold one chunk of at most kGemvMaxT tokens
-    PlanDims pd = plan_dims(T < kGemvMaxT ? T : kGemvMaxT, s.top_k, s.n_shared, single);
+    // plan and h buffers hold one chunk of Tc tokens
+    PlanDims pd = plan_dims(Tc, s.top_k, s.n_shared, single);
     size_t o = 0;
     w.logits = o; o = align256(o + sizeof(double) * (size_t)T * E);
     w.xq = o;     o = align256(o + (size_t)T * H);
@@ -55,399 +53,759 @@ GemvWs gemv_ws(const moe_shape_t &s, int T, bool single)
     return w;
 }
 
-// ---------------------------------------------------------------- block scan
-// Exclusive scan of up to 512 ints, two per thread of a 256-thread block.
-__device__ int block_scan2(int v0, int v1, int &o0, int &o1, int *tmp /*[4]*/)
+// Range check of a plan read back from the workspace: every slot names a
+// valid expert (or -1 = shared) and its pairs stay inside the buffers.
+__device__ bool plan_ok(const int *plan, const PlanDims &pd, int T, int E)
 {
-    const int lane = lane_id(), wv = wave_id();
-    int s = v0 + v1, inc = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int n = __shfl_up(inc, o);
-        if (lane >= o) inc += n;
+    const int S = plan[0];
+    if (S < 0 || S > pd.S) return false;
+    for (int u = 0; u < S; u++) {
+        const int e = plan[pd.o_e + u], n = plan[pd.o_n + u], p0 = plan[pd.o_p0 + u];
+        if (e < -1 || e >= E || n < 0 || n > T || p0 < 0 || p0 + n > pd.P) return false;
     }
-    if (lane == 63) tmp[wv] = inc;
-    __syncthreads();
-    int base = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-        if (w < wv) base += tmp[w];
-        total += tmp[w];
-    }
-    __syncthreads();
-    o0 = base + inc - s;
-    o1 = o0 + v0;
-    return total;
+    return true;
 }
 
 // Builds the batch-union plan in LDS (all threads of the block take part).
 // Slots hold the union of the routed experts in ascending expert order, then
 // the shared expert; pairs of a slot list its tokens in ascending order.
+// Everything follows from one bitmap of selected experts per token:
+//   slot(e)       = number of union experts below e
+//   first pair(e) = number of (token, expert) selections with expert below e
+//   pair of (t,e) = first pair(e) + number of tokens before t selecting e
+// tokbits: LDS scratch of kGemvMaxT x 16 words.
 __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int *s_idx, float *s_w,
-                           int *s_slot, int *tmp)
+                           uint32_t (*tokbits)[16], TopkLds *tl)
 {
-    const int tid = threadIdx.x, T = a.T, k = a.rc.k;
+    const int tid = threadIdx.x, nt = blockDim.x, T = a.T, k = a.rc.k;
     int *slot_e = plan + pd.o_e, *slot_n = plan + pd.o_n, *slot_p0 = plan + pd.o_p0;
     int *pair_t = plan + pd.o_t;
     float *pair_w = reinterpret_cast<float *>(plan + pd.o_w);
     if (!a.logits) {  // single expert, all tokens, weight 1
         if (tid == 0) { plan[0] = 1; slot_e[0] = a.single; slot_n[0] = T; slot_p0[0] = 0; }
-        for (int t = tid; t < T; t += 256) { pair_t[t] = t; pair_w[t] = 1.0f; }
+        for (int t = tid; t < T; t += nt) { pair_t[t] = t; pair_w[t] = 1.0f; }
         __syncthreads();
         return;
     }
-    for (int t = wave_id(); t < T; t += 4)
-        wave_topk(a.rc, a.logits + (size_t)t * a.E, a.bias, s_idx + t * k, s_w + t * k);
-    for (int e = tid; e < kMaxExperts; e += 256) s_slot[e] = 0;
-    __syncthreads();
-    for (int i = tid; i < T * k; i += 256) s_slot[s_idx[i]] = 1;
-    __syncthreads();
-    int f0 = s_slot[2 * tid], f1 = s_slot[2 * tid + 1], o0, o1;
-    const int U = block_scan2(f0, f1, o0, o1, tmp);
-    __syncthreads();
-    if (f0) { s_slot[2 * tid] = o0; slot_e[o0] = 2 * tid; }
-    if (f1) { s_slot[2 * tid + 1] = o1; slot_e[o1] = 2 * tid + 1; }
-    const int S = U + a.n_shared;
-    for (int u = tid; u < S; u += 256) slot_n[u] = (u < U) ? 0 : T;
-    if (tid == 0) {
-        plan[0] = S;
-        if (a.n_shared) slot_e[U] = -1;
+    for (int i = tid; i < T * 16; i += nt) tokbits[i >> 4][i & 15] = 0u;
+    for (int t = 0; t < T; t++)
+        block_topk(a.rc, a.logits + (size_t)t * a.E, a.bias, s_idx + t * k, s_w + t * k, *tl);
+    for (int i = tid; i < T * k; i += nt) {
+        const int e = s_idx[i];
+        atomicOr(&tokbits[i / k][e >> 5], 1u << (e & 31));
     }
     __syncthreads();
-    for (int i = tid; i < T * k; i += 256) atomicAdd(&slot_n[s_slot[s_idx[i]]], 1);
-    __syncthreads();
-    int n0 = (2 * tid < S) ? slot_n[2 * tid] : 0, n1 = (2 * tid + 1 < S) ? slot_n[2 * tid + 1] : 0;
-    block_scan2(n0, n1, o0, o1, tmp);
-    if (2 * tid < S) slot_p0[2 * tid] = o0;
-    if (2 * tid + 1 < S) slot_p0[2 * tid + 1] = o1;
-    __syncthreads();
-    for (int i = tid; i < T * k; i += 256) {
-        const int t = i / k, e = s_idx[i];
-        int r = 0;
-        for (int j = 0; j < t * k; j++) r += (s_idx[j] == e);
-        const int p = slot_p0[s_slot[e]] + r;
-        pair_t[p] = t;
-        pair_w[p] = s_w[i];
+    const int nw = (a.E + 31) >> 5;
+    for (int i = tid; i < T * k; i += nt) {
+        const int t = i / k, e = s_idx[i], wi = e >> 5;
+        const uint32_t bit = 1u << (e & 31), below = bit - 1u;
+        int slot = 0, p0 = 0, n = 0, rank = 0;
+        for (int w = 0; w < wi; w++) {
+            uint32_t un = 0u;
+            for (int tt = 0; tt < T; tt++) { un |= tokbits[tt][w]; p0 += __popc(tokbits[tt][w]); }
+            slot += __popc(un);
+        }
+        uint32_t un = 0u;
+        for (int tt = 0; tt < T; tt++) {
+            const uint32_t v = tokbits[tt][wi];
+            un |= v;
+            p0 += __popc(v & below);
+            if (v & bit) { n++; rank += (tt < t); }
+        }
+        slot += __popc(un & below);
+        slot_e[slot] = e;
+        slot_n[slot] = n;
+        slot_p0[slot] = p0;
+        pair_t[p0 + rank] = t;
+        pair_w[p0 + rank] = s_w[i];
+    }
+    if (tid == 0) {
+        int U = 0;
+        for (int w = 0; w < nw; w++) {
+            uint32_t un = 0u;
+            for (int tt = 0; tt < T; tt++) un |= tokbits[tt][w];
+            U += __popc(un);
+        }
+        plan[0] = U + a.n_shared;
+        if (a.n_shared) { slot_e[U] = -1; slot_n[U] = T; slot_p0[U] = T * k; }
     }
     if (a.n_shared)
-        for (int t = tid; t < T; t += 256) {
-            pair_t[slot_p0[U] + t] = t;
-            pair_w[slot_p0[U] + t] = 1.0f;
+        for (int t = tid; t < T; t += nt) {
+            pair_t[T * k + t] = t;
+            pair_w[T * k + t] = 1.0f;
         }
     __syncthreads();
 }
 
-// ---------------------------------------------------------------- gate / up
-template <int WB, int CPL, int TT>
-__global__ __launch_bounds__(256) void k_gate_up(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
+// ---------------------------------------------------------------- plan kernel
+// One workgroup routes the chunk's tokens and publishes the plan (and the
+// routing, when asked): measured on MI355X, one such launch costs far less
+// than every gate/up workgroup re-deriving the plan, or than cross-workgroup
+// signalling through a shared atomic counter.
+__global__ __launch_bounds__(256) void k_plan(const GemvArgs a, const PlanDims pd)
 {
     __shared__ int plan[1 + 3 * (kGemvMaxT * kMaxTopK + 1) + 2 * kGemvMaxT * (kMaxTopK + 1)];
     __shared__ int s_idx[kGemvMaxT * kMaxTopK];
     __shared__ float s_w[kGemvMaxT * kMaxTopK];
-    __shared__ int s_slot[kMaxExperts];
-    __shared__ int tmp[4];
-    __shared__ float s_h[TT][32];
+    __shared__ uint32_t tokbits[kGemvMaxT][16];
+    __shared__ TopkLds tl;
+    build_plan(a, pd, plan, s_idx, s_w, tokbits, &tl);
+    const int tid = threadIdx.x;
+    for (int i = tid; i < pd.words; i += 256) a.plan[i] = plan[i];
+    if (a.logits && a.idx_out)
+        for (int i = tid; i < a.T * a.rc.k; i += 256) { a.idx_out[i] = s_idx[i]; a.w_out[i] = s_w[i]; }
+}
 
-    build_plan(a, pd, plan, s_idx, s_w, s_slot, tmp);
-    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-    if (blockIdx.x == 0) {
-        for (int i = tid; i < pd.words; i += 256) a.plan[i] = plan[i];
-        if (a.logits && a.idx_out)
-            for (int i = tid; i < a.T * a.rc.k; i += 256) { a.idx_out[i] = s_idx[i]; a.w_out[i] = s_w[i]; }
+int launch_plan(const GemvArgs &a, hipStream_t st)
+{
+    const PlanDims pd = plan_dims(a.T, a.rc.k, a.n_shared, a.logits == nullptr);
+    k_plan<<<1, 256, 0, st>>>(a, pd);
+    return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------- activations in LDS
+// Per token, the activation operand of every chunk position of a row, laid
+// out for act_from_lds: A [cpr][NA] dwords (already permuted for the weight
+// packing), D [blocks] scales, Q [blocks] block sums (int4 / int2 only).
+template <int WB> struct ActShape;
+template <> struct ActShape<8> { static constexpr int NA = 4; };
+template <> struct ActShape<4> { static constexpr int NA = 8; };
+template <> struct ActShape<2> { static constexpr int NA = 16; };
+
+template <int WB>
+__device__ __forceinline__ void stage_act(const int8_t *q, const float *d, int pos, uint32_t *la, float *ld, int *lq)
+{
+    Act<WB> A;
+    A.load(q, d, pos);
+    uint4 *dst = reinterpret_cast<uint4 *>(la + pos * ActShape<WB>::NA);
+#pragma unroll
+    for (int i = 0; i < ActShape<WB>::NA / 4; i++)
+        dst[i] = make_uint4(A.a[4 * i], A.a[4 * i + 1], A.a[4 * i + 2], A.a[4 * i + 3]);
+    if constexpr (WB == 8) {
+        if ((pos & 1) == 0) ld[pos >> 1] = A.d;
+    } else if constexpr (WB == 4) {
+        ld[pos] = A.d;
+        lq[pos] = A.qs;
+    } else {
+        ld[2 * pos] = A.d0; ld[2 * pos + 1] = A.d1;
+        lq[2 * pos] = A.qs0; lq[2 * pos + 1] = A.qs1;
     }
+}
+
+template <int WB>
+__device__ __forceinline__ void act_from_lds(Act<WB> &A, const uint32_t *la, const float *ld, const int *lq, int pos)
+{
+    const uint4 *src = reinterpret_cast<const uint4 *>(la + pos * ActShape<WB>::NA);
+#pragma unroll
+    for (int i = 0; i < ActShape<WB>::NA / 4; i++) {
+        const uint4 v = src[i];
+        A.a[4 * i] = v.x; A.a[4 * i + 1] = v.y; A.a[4 * i + 2] = v.z; A.a[4 * i + 3] = v.w;
+    }
+    if constexpr (WB == 8) {
+        A.d = ld[pos >> 1];
+    } else if constexpr (WB == 4) {
+        A.d = ld[pos];
+        A.qs = lq[pos];
+    } else {
+        A.d0 = ld[2 * pos]; A.d1 = ld[2 * pos + 1];
+        A.qs0 = lq[2 * pos]; A.qs1 = lq[2 * pos + 1];
+    }
+}
+
+__device__ __forceinline__ uint4 ld16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// ---------------------------------------------------------------- gate / up
+constexpr int kGuLanes = 8;   // lanes per row in k_gate_up
+constexpr int kGuBatch = 4;   // chunks per lane per prefetch batch
+
+template <int WB, int TT>
+__global__ __launch_bounds__(256) void k_gate_up_rg(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
+{
+    __shared__ int plan[1 + 3 * (kGemvMaxT * kMaxTopK + 1) + 2 * kGemvMaxT * (kMaxTopK + 1)];
+    __shared__ float s_h[TT][32];
+    extern __shared__ __align__(16) unsigned char lds_act[];
+    static_assert(sizeof(plan) + sizeof(s_h) <= kGateUpStaticLds, "static LDS of k_gate_up");
+
+    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+    for (int i = tid; i < pd.words; i += 256) plan[i] = a.plan[i];
+    __syncthreads();
+    if (!plan_ok(plan, pd, a.T, a.E)) return;
     const int tiles = a.I / 32;
     const int u = blockIdx.x / tiles, row0 = (blockIdx.x % tiles) * 32;
     if (u >= plan[0]) return;
     const int e = plan[pd.o_e + u];
     const moe_weights_t &W = (e >= 0) ? a.routed : a.shared;
     const int ee = (e >= 0) ? e : 0;
-    const size_t rowbytes = (size_t)cc.cpr * 16;
-    const uint8_t *gate = W.gate + (size_t)ee * a.I * rowbytes;
-    const uint8_t *up = W.up + (size_t)ee * a.I * rowbytes;
-    const float *gs = W.gate_s + (size_t)ee * a.I, *us = W.up_s + (size_t)ee * a.I;
+    const int cpr = cc.cpr, H = a.H, nb = H / 32;
+    const size_t rowbytes = (size_t)cpr * 16;
     const int n_u = plan[pd.o_n + u], p0 = plan[pd.o_p0 + u];
-    const int nb = a.H / 32;
 
-    // lane's chunks inside a wave tile: row offset and position in the row
-    int crow[CPL], cpos[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; i++) {
-        int g = lane + 64 * i;
-        crow[i] = g / cc.cpr;
-        cpos[i] = g - crow[i] * cc.cpr;
+    // stage the slot's token activations (n_u <= TT)
+    const size_t tok_bytes = act_lds_bytes(WB, H);
+    auto la_of = [&](int tt) { return reinterpret_cast<uint32_t *>(lds_act + tt * tok_bytes); };
+    auto ld_of = [&](int tt) { return reinterpret_cast<float *>(lds_act + tt * tok_bytes + H); };
+    auto lq_of = [&](int tt) { return reinterpret_cast<int *>(lds_act + tt * tok_bytes + H + 4 * nb); };
+    for (int c = tid; c < n_u * cpr; c += 256) {
+        const int tt = c / cpr, pos = c - tt * cpr;
+        const int t = plan[pd.o_t + p0 + tt];
+        stage_act<WB>(a.xq + (size_t)t * H, a.xd + (size_t)t * nb, pos, la_of(tt), ld_of(tt), lq_of(tt));
     }
+    __syncthreads();
 
-    for (int j0 = 0; j0 < n_u; j0 += TT) {
-        const int nt = min(TT, n_u - j0);
-        Act<WB> act[TT][CPL];
+    // 8 lanes per row: this lane's row and its chunk positions sub, sub+8, ...
+    const int sub = lane & (kGuLanes - 1);
+    const int rloc = wv * (64 / kGuLanes) + (lane / kGuLanes);
+    const int row = row0 + rloc;
+    const uint8_t *grow = W.gate + ((size_t)ee * a.I + row) * rowbytes;
+    const uint8_t *urow = W.up + ((size_t)ee * a.I + row) * rowbytes;
+    const int niter = (cpr + kGuLanes - 1) / kGuLanes;
+    const int nbatch = (niter + kGuBatch - 1) / kGuBatch;
+
+    float accg[TT], accu[TT];
 #pragma unroll
-        for (int tt = 0; tt < TT; tt++) {
-            if (tt < nt) {
-                const int t = plan[pd.o_t + p0 + j0 + tt];
+    for (int tt = 0; tt < TT; tt++) { accg[tt] = 0.f; accu[tt] = 0.f; }
+
+    uint4 bg[2][kGuBatch], bu[2][kGuBatch];
+    auto load_batch = [&](int b, uint4 *g, uint4 *v) {
 #pragma unroll
-                for (int i = 0; i < CPL; i++) {
-                    act[tt][i].load(a.xq + (size_t)t * a.H, a.xd + (size_t)t * nb, cpos[i]);
+        for (int j = 0; j < kGuBatch; j++) {
+            const int pos = sub + kGuLanes * (b * kGuBatch + j);
+            if (pos < cpr) {
+                g[j] = ld16(grow + (size_t)pos * 16);
+                v[j] = ld16(urow + (size_t)pos * 16);
+            } else {
+                g[j] = make_uint4(0, 0, 0, 0);
+                v[j] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto use_batch = [&](int b, const uint4 *g, const uint4 *v) {
+#pragma unroll
+        for (int j = 0; j < kGuBatch; j++) {
+            const int pos = sub + kGuLanes * (b * kGuBatch + j);
+            if (pos < cpr) {
+#pragma unroll
+                for (int tt = 0; tt < TT; tt++) {
+                    if (tt < n_u) {
+                        Act<WB> A;
+                        act_from_lds<WB>(A, la_of(tt), ld_of(tt), lq_of(tt), pos);
+                        accg[tt] += A.dot(g[j]);
+                        accu[tt] += A.dot(v[j]);
+                    }
                 }
             }
         }
-        for (int tile = wv; tile < 32 / cc.rw; tile += 4) {
-            const int rb = row0 + tile * cc.rw;
-            uint4 wg[CPL], wu[CPL];
-#pragma unroll
-            for (int i = 0; i < CPL; i++) {
-                const size_t off = (size_t)(rb + crow[i]) * rowbytes + (size_t)cpos[i] * 16;
-                wg[i] = *reinterpret_cast<const uint4 *>(gate + off);
-                wu[i] = *reinterpret_cast<const uint4 *>(up + off);
-            }
-#pragma unroll
-            for (int tt = 0; tt < TT; tt++) {
-                if (tt < nt) {
-                    float pg[CPL], pu[CPL];
-#pragma unroll
-                    for (int i = 0; i < CPL; i++) {
-                        pg[i] = act[tt][i].dot(wg[i]);
-                        pu[i] = act[tt][i].dot(wu[i]);
-                    }
-                    for (int r = 0; r < cc.rw; r++) {
-                        float vg = 0.f, vu = 0.f;
-#pragma unroll
-                        for (int i = 0; i < CPL; i++)
-                            if (crow[i] == r) { vg += pg[i]; vu += pu[i]; }
-                        vg = wave_sum(vg) * gs[rb + r];
-                        vu = wave_sum(vu) * us[rb + r];
-                        if (lane == 0) s_h[tt][tile * cc.rw + r] = silu_mul(vg, vu);
-                    }
-                }
-            }
+    };
+    load_batch(0, bg[0], bu[0]);
+    for (int b = 0; b < nbatch; b += 2) {
+        if (b + 1 < nbatch) load_batch(b + 1, bg[1], bu[1]);
+        use_batch(b, bg[0], bu[0]);
+        if (b + 1 < nbatch) {
+            if (b + 2 < nbatch) load_batch(b + 2, bg[0], bu[0]);
+            use_batch(b + 1, bg[1], bu[1]);
         }
-        __syncthreads();
-        // quantise h per token: one block of 32 rows, lanes 0..31 of a wave
-        for (int tt = wv; tt < nt; tt += 4) {
-            const int p = p0 + j0 + tt;
-            float h = s_h[tt][lane & 31];
-            float amax = fabsf(h);
+    }
+    const float sg = W.gate_s[(size_t)ee * a.I + row], su = W.up_s[(size_t)ee * a.I + row];
 #pragma unroll
-            for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-            float d = amax / 127.0f;
-            float r = (d == 0.0f) ? 0.0f : rintf(h / d);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            if (lane < 32) a.qh[(size_t)p * a.I + row0 + lane] = (int8_t)(int)r;
-            if (lane == 0) a.dh[(size_t)p * (a.I / 32) + row0 / 32] = d;
+    for (int tt = 0; tt < TT; tt++) {
+        if (tt < n_u) {
+            float g = accg[tt], v = accu[tt];
+#pragma unroll
+            for (int o = 1; o < kGuLanes; o <<= 1) {
+                g += __shfl_xor(g, o);
+                v += __shfl_xor(v, o);
+            }
+            if (sub == 0) s_h[tt][rloc] = silu_mul(g * sg, v * su);
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    // quantise h per token: one block of 32 rows, lanes 0..31 of a wave
+    for (int tt = wv; tt < n_u; tt += 4) {
+        const int p = p0 + tt;
+        const float h = s_h[tt][lane & 31];
+        float amax = fabsf(h);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float d = amax / 127.0f;
+        float r = (d == 0.0f) ? 0.0f : rintf(h / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        if (lane < 32) a.qh[(size_t)p * a.I + row0 + lane] = (int8_t)(int)r;
+        if (lane == 0) a.dh[(size_t)p * (a.I / 32) + row0 / 32] = d;
     }
 }
 
 // ---------------------------------------------------------------- down / combine
-template <int WB> struct ActShape;
-template <> struct ActShape<8> { static constexpr int NA = 4, NB = 1; };   // dwords, blocks per chunk (x2 chunks per block)
-template <> struct ActShape<4> { static constexpr int NA = 8, NB = 1; };
-template <> struct ActShape<2> { static constexpr int NA = 16, NB = 2; };
+constexpr int kDnLanes = 16;  // lanes per row in k_down
+constexpr int kDnRows = 16;   // rows per workgroup (4 waves x 4 rows)
+constexpr int kDnBatch = 4;   // chunks per lane per prefetch batch
 
-template <int WB>
-__device__ __forceinline__ void act_from_lds(Act<WB> &A, const uint32_t *la, const float *ld, const int *lq, int pos)
-{
-    const uint32_t *src = la + pos * ActShape<WB>::NA;
-    if constexpr (WB == 8) {
-        uint4 v = *reinterpret_cast<const uint4 *>(src);
-        A.a[0] = v.x; A.a[1] = v.y; A.a[2] = v.z; A.a[3] = v.w;
-        A.d = ld[pos >> 1];
-    } else if constexpr (WB == 4) {
-        uint4 v0 = reinterpret_cast<const uint4 *>(src)[0], v1 = reinterpret_cast<const uint4 *>(src)[1];
-        A.a[0] = v0.x; A.a[1] = v0.y; A.a[2] = v0.z; A.a[3] = v0.w;
-        A.a[4] = v1.x; A.a[5] = v1.y; A.a[6] = v1.z; A.a[7] = v1.w;
-        A.d = ld[pos];
-        A.qs = lq[pos];
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            uint4 v = reinterpret_cast<const uint4 *>(src)[i];
-            A.a[4 * i] = v.x; A.a[4 * i + 1] = v.y; A.a[4 * i + 2] = v.z; A.a[4 * i + 3] = v.w;
-        }
-        A.d0 = ld[2 * pos]; A.d1 = ld[2 * pos + 1];
-        A.qs0 = lq[2 * pos]; A.qs1 = lq[2 * pos + 1];
-    }
-}
-
-template <int WB, int CPL, int TT>
-__global__ __launch_bounds__(256) void k_down(const GemvArgs a, const ChunkCfg cc, const PlanDims pd,
-                                              int rows_per_wg)
+template <int WB, int TT>
+__global__ __launch_bounds__(256) void k_down_rg(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-    const int I = a.I, nbh = I / 32;
+    const int I = a.I, nbh = I / 32, cpr = cc.cpr;
     int *plan = reinterpret_cast<int *>(lds);
     const int plan_words = (pd.words + 3) & ~3;
-    uint32_t *la = reinterpret_cast<uint32_t *>(plan + plan_words);  // [P][I/4] permuted codes
-    float *ld = reinterpret_cast<float *>(la + (size_t)pd.P * (I / 4)); // [P][I/32] scales
-    int *lq = reinterpret_cast<int *>(ld + (size_t)pd.P * nbh);         // [P][I/32] block sums
+    unsigned char *act = lds + sizeof(int) * plan_words;
+    const size_t pair_bytes = act_lds_bytes(WB, I);
+    auto la_of = [&](int p) { return reinterpret_cast<uint32_t *>(act + p * pair_bytes); };
+    auto ld_of = [&](int p) { return reinterpret_cast<float *>(act + p * pair_bytes + I); };
+    auto lq_of = [&](int p) { return reinterpret_cast<int *>(act + p * pair_bytes + I + 4 * nbh); };
 
     for (int i = tid; i < pd.words; i += 256) plan[i] = a.plan[i];
     __syncthreads();
+    if (!plan_ok(plan, pd, a.T, a.E)) return;
     const int S = plan[0];
     int npairs = 0;
     for (int u = 0; u < S; u++) npairs += plan[pd.o_n + u];
-    // stage every pair's h codes in LDS, permuted for the weight layout
-    const int cpr = cc.cpr;
     for (int c = tid; c < npairs * cpr; c += 256) {
         const int p = c / cpr, pos = c - p * cpr;
-        const int8_t *q = a.qh + (size_t)p * I;
-        Act<WB> A;
-        if constexpr (WB == 8) {
-            A.load(q, a.dh + (size_t)p * nbh, pos);
-            *reinterpret_cast<uint4 *>(la + (size_t)p * (I / 4) + pos * 4) = make_uint4(A.a[0], A.a[1], A.a[2], A.a[3]);
-        } else if constexpr (WB == 4) {
-            A.load(q, a.dh + (size_t)p * nbh, pos);
-            uint4 *dst = reinterpret_cast<uint4 *>(la + (size_t)p * (I / 4) + pos * 8);
-            dst[0] = make_uint4(A.a[0], A.a[1], A.a[2], A.a[3]);
-            dst[1] = make_uint4(A.a[4], A.a[5], A.a[6], A.a[7]);
-            lq[(size_t)p * nbh + pos] = A.qs;
-        } else {
-            A.load(q, a.dh + (size_t)p * nbh, pos);
-            uint4 *dst = reinterpret_cast<uint4 *>(la + (size_t)p * (I / 4) + pos * 16);
-#pragma unroll
-            for (int i = 0; i < 4; i++) dst[i] = make_uint4(A.a[4 * i], A.a[4 * i + 1], A.a[4 * i + 2], A.a[4 * i + 3]);
-            lq[(size_t)p * nbh + 2 * pos] = A.qs0;
-            lq[(size_t)p * nbh + 2 * pos + 1] = A.qs1;
-        }
+        stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pos, la_of(p), ld_of(p), lq_of(p));
     }
-    for (int c = tid; c < npairs * nbh; c += 256) ld[c] = a.dh[c];
     __syncthreads();
 
-    int crow[CPL], cpos[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; i++) {
-        int g = lane + 64 * i;
-        crow[i] = g / cpr;
-        cpos[i] = g - crow[i] * cpr;
-    }
+    const int sub = lane & (kDnLanes - 1);
+    const int row = blockIdx.x * kDnRows + wv * (64 / kDnLanes) + lane / kDnLanes;
     const size_t rowbytes = (size_t)cpr * 16;
-    const int row_base = blockIdx.x * rows_per_wg;
-    constexpr int UB = (CPL == 1) ? 8 : 4;  // slots whose rows are in flight together
+    const int niter = (cpr + kDnLanes - 1) / kDnLanes;
+    const int nbatch = (niter + kDnBatch - 1) / kDnBatch;  // batches per slot
+    const int total = S * nbatch;                           // (slot, batch) steps
 
-    for (int tile = wv; tile < rows_per_wg / cc.rw; tile += 4) {
-        const int rb = row_base + tile * cc.rw;
-        float acc[TT][CPL];
+    float acc[TT];
 #pragma unroll
-        for (int tt = 0; tt < TT; tt++)
-#pragma unroll
-            for (int i = 0; i < CPL; i++) acc[tt][i] = 0.f;
+    for (int tt = 0; tt < TT; tt++) acc[tt] = 0.f;
 
-        for (int u0 = 0; u0 < S; u0 += UB) {
-            uint4 wd[UB][CPL];
-            float sr[UB][CPL];
+    uint4 buf[2][kDnBatch];
+    auto slot_row = [&](int u) {
+        const int e = plan[pd.o_e + u];
+        const moe_weights_t &W = (e >= 0) ? a.routed : a.shared;
+        return W.down + ((size_t)((e >= 0) ? e : 0) * a.H + row) * rowbytes;
+    };
+    auto load_step = [&](int s, uint4 *w) {
+        const int u = s / nbatch, b = s - u * nbatch;
+        const uint8_t *src = slot_row(u);
 #pragma unroll
-            for (int b = 0; b < UB; b++) {
-                const int u = u0 + b;
-                if (u < S) {
-                    const int e = plan[pd.o_e + u];
-                    const moe_weights_t &W = (e >= 0) ? a.routed : a.shared;
-                    const int ee = (e >= 0) ? e : 0;
-                    const uint8_t *down = W.down + (size_t)ee * a.H * rowbytes;
-                    const float *ds = W.down_s + (size_t)ee * a.H;
+        for (int j = 0; j < kDnBatch; j++) {
+            const int pos = sub + kDnLanes * (b * kDnBatch + j);
+            w[j] = (pos < cpr) ? ld16(src + (size_t)pos * 16) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto use_step = [&](int s, const uint4 *w) {
+        const int u = s / nbatch, b = s - u * nbatch;
+        const int e = plan[pd.o_e + u];
+        const float sr = ((e >= 0) ? a.routed.down_s + (size_t)e * a.H : a.shared.down_s)[row];
+        const int n = plan[pd.o_n + u], p0 = plan[pd.o_p0 + u];
+        for (int j2 = 0; j2 < n; j2++) {
+            const int p = p0 + j2;
+            const int t = plan[pd.o_t + p];
+            const float coef = __int_as_float(plan[pd.o_w + p]) * sr;
+            float part = 0.f;
 #pragma unroll
-                    for (int i = 0; i < CPL; i++) {
-                        wd[b][i] = *reinterpret_cast<const uint4 *>(down + (size_t)(rb + crow[i]) * rowbytes +
-                                                                    (size_t)cpos[i] * 16);
-                        sr[b][i] = ds[rb + crow[i]];
-                    }
+            for (int j = 0; j < kDnBatch; j++) {
+                const int pos = sub + kDnLanes * (b * kDnBatch + j);
+                if (pos < cpr) {
+                    Act<WB> A;
+                    act_from_lds<WB>(A, la_of(p), ld_of(p), lq_of(p), pos);
+                    part += A.dot(w[j]);
                 }
             }
 #pragma unroll
-            for (int b = 0; b < UB; b++) {
-                const int u = u0 + b;
-                if (u < S) {
-                    const int n = plan[pd.o_n + u], p0 = plan[pd.o_p0 + u];
-                    for (int j = 0; j < n; j++) {
-                        const int p = p0 + j;
-                        const int t = plan[pd.o_t + p];
-                        const float pw = __int_as_float(plan[pd.o_w + p]);
+            for (int tt = 0; tt < TT; tt++)
+                if (tt == t) acc[tt] += coef * part;
+        }
+    };
+    load_step(0, buf[0]);
+    for (int s = 0; s < total; s += 2) {
+        if (s + 1 < total) load_step(s + 1, buf[1]);
+        use_step(s, buf[0]);
+        if (s + 1 < total) {
+            if (s + 2 < total) load_step(s + 2, buf[0]);
+            use_step(s + 1, buf[1]);
+        }
+    }
 #pragma unroll
-                        for (int i = 0; i < CPL; i++) {
-                            Act<WB> A;
-                            act_from_lds<WB>(A, la + (size_t)p * (I / 4), ld + (size_t)p * nbh, lq + (size_t)p * nbh, cpos[i]);
-                            const float v = A.dot(wd[b][i]) * (pw * sr[b][i]);
+    for (int tt = 0; tt < TT; tt++) {
+        if (tt < a.T) {
+            float v = acc[tt];
 #pragma unroll
-                            for (int tt = 0; tt < TT; tt++)
-                                if (tt == t) acc[tt][i] += v;
-                        }
-                    }
+            for (int o = 1; o < kDnLanes; o <<= 1) v += __shfl_xor(v, o);
+            if (sub == 0) {
+                float *dst = a.y + (size_t)tt * a.H + row;
+                *dst = a.accumulate ? *dst + v : v;
+            }
+        }
+    }
+}
+
+
+// ---------------------------------------------------------------- row-sweep kernels
+// Measured on MI355X: streaming reads reach ~6.4 TB/s only when each step of
+// a workgroup reads one contiguous window of a few KB; workgroups whose waves
+// walk separate rows (even 1 KB contiguous per wave) stall near 2.5 TB/s.  So
+// in these kernels the workgroup reads whole consecutive rows per step, each
+// thread owns fixed chunk positions of the row (its int8 activation operand
+// then lives in registers), per-row partial sums accumulate in registers, and
+// rows are finished by a reduce-scatter over 32-lane groups plus a
+// fixed-order combine of the groups in LDS.
+
+// Reduce-scatter of N partials (N a power of two <= 32) over a 32-lane
+// group: afterwards lane l of the group holds, for slot j = (l % 32) / (32/N),
+// the sum of v[j] over the 32 lanes (valid where (l % 32) % (32/N) == 0).
+template <int N>
+__device__ __forceinline__ float group32_reduce_scatter(float (&v)[N])
+{
+    const int lane = lane_id();
+    int n = N;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+        if (n > 1) {
+            const bool upper = (lane & o) != 0;
+#pragma unroll
+            for (int j = 0; j < N / 2; j++) {
+                if (j < n / 2) {
+                    const float send = upper ? v[j] : v[j + n / 2];
+                    const float keep = upper ? v[j + n / 2] : v[j];
+                    v[j] = keep + __shfl_xor(send, o);
                 }
             }
+            n >>= 1;
+        } else {
+            v[0] += __shfl_xor(v[0], o);
+        }
+    }
+    return v[0];
+}
+
+constexpr int kSwThreads = 192;  // gate/up row-sweep block
+constexpr int kSwGroups = kSwThreads / 32;
+constexpr int kSwDepth = 12;     // steps of prefetch in flight
+
+// gate/up of one 32-row tile of one expert for the n_u tokens of a slot: a
+// step reads RPS rows of gate and of up (kSwThreads * CPT chunks each,
+// contiguous), in passes of 8 rows.  toks lists the slot's tokens; pair
+// p_first + tt receives token tt's quantised h.  All threads of the block
+// must call it.
+template <int WB, int CPT, int RPS, int TT>
+__device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_weights_t &W, int ee, int row0,
+                                                int n_u, const int *toks, int p_first, float (*s_h)[32],
+                                                float (*part)[TT][kSwGroups][32])
+{
+    static_assert(CPT == 1 || RPS == 1, "chunks of one thread stay in one row");
+    constexpr int NSTEP = 32 / RPS, PS = 8 / RPS;
+    constexpr int PF = (CPT == 1) ? kSwDepth : kSwDepth / 2;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int cpr = (kSwThreads * CPT) / RPS, H = a.H, nb = H / 32;
+    const size_t rowbytes = (size_t)cpr * 16;
+    const int rowoff = (RPS == 1) ? 0 : tid / cpr;
+    const int grp = tid >> 5;
+
+    const uint8_t *gb = W.gate + ((size_t)ee * a.I + row0) * rowbytes + (size_t)tid * 16;
+    const uint8_t *ub = W.up + ((size_t)ee * a.I + row0) * rowbytes + (size_t)tid * 16;
+    const size_t step_bytes = (size_t)kSwThreads * CPT * 16;
+    uint4 bg[PF][CPT], bu[PF][CPT];
+#pragma unroll
+    for (int s = 0; s < PF; s++)
+#pragma unroll
+        for (int k = 0; k < CPT; k++) {
+            bg[s][k] = ld16(gb + s * step_bytes + (size_t)k * kSwThreads * 16);
+            bu[s][k] = ld16(ub + s * step_bytes + (size_t)k * kSwThreads * 16);
+        }
+
+    Act<WB> act[TT][CPT];
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) {
+        if (tt < n_u) {
+            const int t = toks[tt];
+#pragma unroll
+            for (int k = 0; k < CPT; k++) {
+                const int pos = (tid + kSwThreads * k) % cpr;
+                act[tt][k].load(a.xq + (size_t)t * H, a.xd + (size_t)t * nb, pos);
+            }
+        }
+    }
+    float accg[TT][PS], accu[TT][PS];
+#pragma unroll
+    for (int s = 0; s < NSTEP; s++) {
+        const int slot = s % PF, j = s % PS;
+        if (j == 0) {
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++)
+#pragma unroll
+                for (int q = 0; q < PS; q++) { accg[tt][q] = 0.f; accu[tt][q] = 0.f; }
         }
 #pragma unroll
         for (int tt = 0; tt < TT; tt++) {
-            if (tt < a.T) {
-                for (int r = 0; r < cc.rw; r++) {
-                    float v = 0.f;
+            if (tt < n_u) {
 #pragma unroll
-                    for (int i = 0; i < CPL; i++)
-                        if (crow[i] == r) v += acc[tt][i];
-                    v = wave_sum(v);
-                    if (lane == 0) {
-                        float *dst = a.y + (size_t)tt * a.H + rb + r;
-                        *dst = a.accumulate ? *dst + v : v;
+                for (int k = 0; k < CPT; k++) {
+                    accg[tt][j] += act[tt][k].dot(bg[slot][k]);
+                    accu[tt][j] += act[tt][k].dot(bu[slot][k]);
+                }
+            }
+        }
+        if (s + PF < NSTEP) {
+#pragma unroll
+            for (int k = 0; k < CPT; k++) {
+                bg[slot][k] = ld16(gb + (s + PF) * step_bytes + (size_t)k * kSwThreads * 16);
+                bu[slot][k] = ld16(ub + (s + PF) * step_bytes + (size_t)k * kSwThreads * 16);
+            }
+        }
+        if (j == PS - 1) {
+            const int pass = s / PS;
+            const int l32 = lane & 31;
+            const int jj = l32 / (32 / PS);
+            const bool writer = (l32 % (32 / PS)) == 0;
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++) {
+                if (tt < n_u) {
+                    const float g = group32_reduce_scatter<PS>(accg[tt]);
+                    const float v = group32_reduce_scatter<PS>(accu[tt]);
+                    if (writer) {
+                        part[0][tt][grp][pass * 8 + jj * RPS + rowoff] = g;
+                        part[1][tt][grp][pass * 8 + jj * RPS + rowoff] = v;
                     }
                 }
             }
         }
     }
+    __syncthreads();
+    // combine the groups of each row in a fixed order, then SwiGLU
+    const int groups_per_row = kSwGroups / RPS;
+    for (int i = tid; i < n_u * 32; i += kSwThreads) {
+        const int tt = i >> 5, r = i & 31, g0 = (r % RPS) * groups_per_row;
+        float g = 0.f, v = 0.f;
+        for (int q = 0; q < groups_per_row; q++) { g += part[0][tt][g0 + q][r]; v += part[1][tt][g0 + q][r]; }
+        const size_t row = (size_t)ee * a.I + row0 + r;
+        s_h[tt][r] = silu_mul(g * W.gate_s[row], v * W.up_s[row]);
+    }
+    __syncthreads();
+    // quantise h per token: one block of 32 rows, lanes 0..31 of a wave
+    for (int tt = wave_id(); tt < n_u; tt += kSwThreads / 64) {
+        const int p = p_first + tt;
+        const float h = s_h[tt][lane & 31];
+        float amax = fabsf(h);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float d = amax / 127.0f;
+        float r = (d == 0.0f) ? 0.0f : rintf(h / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        if (lane < 32) a.qh[(size_t)p * a.I + row0 + lane] = (int8_t)(int)r;
+        if (lane == 0) a.dh[(size_t)p * (a.I / 32) + row0 / 32] = d;
+    }
 }
 
-size_t down_lds_bytes(const GemvArgs &a, const PlanDims &pd)
+// Every slot of a chunk, with the plan the plan kernel published.  The plan
+// is range-checked, so a corrupt plan can only skip work, never steer a load
+// out of the weight tensors.
+template <int WB, int CPT, int RPS, int TT>
+__global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
-    const size_t nbh = a.I / 32;
-    return sizeof(int) * (size_t)((pd.words + 3) & ~3) + (size_t)pd.P * a.I +
-           2 * sizeof(float) * (size_t)pd.P * nbh;
+    __shared__ float s_h[TT][32];
+    __shared__ float part[2][TT][kSwGroups][32];
+    const int tiles = a.I / 32;
+    const int u = blockIdx.x / tiles, row0 = (blockIdx.x % tiles) * 32;
+    const int S = a.plan[0];
+    if (S > pd.S || u >= S) return;
+    const int e = a.plan[pd.o_e + u], n_u = a.plan[pd.o_n + u], p0 = a.plan[pd.o_p0 + u];
+    if (e < -1 || e >= a.E || n_u < 1 || n_u > a.T || p0 < 0 || p0 + n_u > pd.P) return;
+    gate_up_tile_sw<WB, CPT, RPS, TT>(a, (e >= 0) ? a.routed : a.shared, (e >= 0) ? e : 0, row0, n_u,
+                                      a.plan + pd.o_t + p0, p0, s_h, part);
+}
+
+constexpr int kDsThreads = 256;  // down row-sweep block
+constexpr int kDsGroups = kDsThreads / 32;
+constexpr int kDsRows = 16;      // output rows per workgroup
+
+// down/combine: a step reads RPS consecutive down rows of one slot (4 KB);
+// kDsRows rows per workgroup, every slot in turn, prefetching the next slot.
+template <int WB, int RPS, int TT>
+__global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    __shared__ float part[TT][kDsGroups][kDsRows];
+    constexpr int NSTEP = kDsRows / RPS;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int I = a.I, nbh = I / 32, cpr = cc.cpr;
+    int *plan = reinterpret_cast<int *>(lds);
+    const int plan_words = (pd.words + 3) & ~3;
+    unsigned char *act = lds + sizeof(int) * plan_words;
+    const size_t pair_bytes = act_lds_bytes(WB, I);
+    auto la_of = [&](int p) { return reinterpret_cast<uint32_t *>(act + p * pair_bytes); };
+    auto ld_of = [&](int p) { return reinterpret_cast<float *>(act + p * pair_bytes + I); };
+    auto lq_of = [&](int p) { return reinterpret_cast<int *>(act + p * pair_bytes + I + 4 * nbh); };
+
+    for (int i = tid; i < pd.words; i += kDsThreads) plan[i] = a.plan[i];
+    __syncthreads();
+    if (!plan_ok(plan, pd, a.T, a.E)) return;
+    const int S = plan[0];
+    int npairs = 0;
+    for (int u = 0; u < S; u++) npairs += plan[pd.o_n + u];
+    for (int c = tid; c < npairs * cpr; c += kDsThreads) {
+        const int p = c / cpr, pos = c - p * cpr;
+        stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pos, la_of(p), ld_of(p), lq_of(p));
+    }
+    __syncthreads();
+
+    const int rowoff = tid / cpr, pos = tid % cpr, grp = tid >> 5;
+    const int row_base = blockIdx.x * kDsRows;
+    const size_t rowbytes = (size_t)cpr * 16;
+    const size_t step_bytes = (size_t)kDsThreads * 16;
+    auto slot_src = [&](int u, const float *&ds) {
+        const int e = plan[pd.o_e + u];
+        const moe_weights_t &W = (e >= 0) ? a.routed : a.shared;
+        const int ee = (e >= 0) ? e : 0;
+        ds = W.down_s + (size_t)ee * a.H + row_base + rowoff;
+        return W.down + ((size_t)ee * a.H + row_base) * rowbytes + (size_t)tid * 16;
+    };
+    float acc[TT][NSTEP];
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++)
+#pragma unroll
+        for (int j = 0; j < NSTEP; j++) acc[tt][j] = 0.f;
+
+    // statically named slot buffers (no pointers to register arrays, so
+    // nothing is demoted to scratch)
+    uint4 w0[NSTEP], w1[NSTEP], w2[NSTEP];
+    float s0[NSTEP], s1[NSTEP], s2[NSTEP];
+#define MOE_DS_LOAD(U, WB_, SB_)                                                  \
+    {                                                                             \
+        const float *ds_;                                                         \
+        const uint8_t *src_ = slot_src((U), ds_);                                 \
+        _Pragma("unroll") for (int j = 0; j < NSTEP; j++) {                       \
+            WB_[j] = ld16(src_ + j * step_bytes);                                 \
+            SB_[j] = ds_[j * RPS];                                                \
+        }                                                                         \
+    }
+/* a slot's pairs list its tokens in ascending order: walk the tokens in  \
+   compile-time order so every accumulator index is static */                   \
+#define MOE_DS_USE(U, WB_, SB_)                                                   \
+    {                                                                             \
+        const int n_ = plan[pd.o_n + (U)], p0_ = plan[pd.o_p0 + (U)];             \
+        int q_ = 0;                                                               \
+        _Pragma("unroll") for (int tt = 0; tt < TT; tt++) {                       \
+            if (q_ < n_ && plan[pd.o_t + p0_ + q_] == tt) {                       \
+                const int p = p0_ + q_;                                           \
+                const float pw = __int_as_float(plan[pd.o_w + p]);                \
+                Act<WB> A;                                                        \
+                act_from_lds<WB>(A, la_of(p), ld_of(p), lq_of(p), pos);           \
+                _Pragma("unroll") for (int j = 0; j < NSTEP; j++)                 \
+                    acc[tt][j] += A.dot(WB_[j]) * (pw * SB_[j]);                  \
+                q_++;                                                             \
+            }                                                                     \
+        }                                                                         \
+    }
+    // three buffers in rotation: two slots of rows in flight ahead of use
+    MOE_DS_LOAD(0, w0, s0)
+    if (1 < S) MOE_DS_LOAD(1, w1, s1)
+    for (int u = 0; u < S; u += 3) {
+        if (u + 2 < S) MOE_DS_LOAD(u + 2, w2, s2)
+        MOE_DS_USE(u, w0, s0)
+        if (u + 1 < S) {
+            if (u + 3 < S) MOE_DS_LOAD(u + 3, w0, s0)
+            MOE_DS_USE(u + 1, w1, s1)
+        }
+        if (u + 2 < S) {
+            if (u + 4 < S) MOE_DS_LOAD(u + 4, w1, s1)
+            MOE_DS_USE(u + 2, w2, s2)
+        }
+    }
+#undef MOE_DS_LOAD
+#undef MOE_DS_USE
+    const int l32 = lane & 31;
+    const int jj = l32 / (32 / NSTEP);
+    const bool writer = (l32 % (32 / NSTEP)) == 0;
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) {
+        if (tt < a.T) {
+            const float v = group32_reduce_scatter<NSTEP>(acc[tt]);
+            if (writer) part[tt][grp][jj * RPS + rowoff] = v;
+        }
+    }
+    __syncthreads();
+    const int groups_per_row = cpr / 32;
+    for (int i = tid; i < a.T * kDsRows; i += kDsThreads) {
+        const int tt = i / kDsRows, r = i % kDsRows, g0 = (r % RPS) * groups_per_row;
+        float v = 0.f;
+        for (int q = 0; q < groups_per_row; q++) v += part[tt][g0 + q][r];
+        float *dst = a.y + (size_t)tt * a.H + row_base + r;
+        *dst = a.accumulate ? *dst + v : v;
+    }
+}
+
+template <int WB, int CPT, int RPS, int TT>
+static int run_gate_up_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
+{
+    k_gate_up_sw<WB, CPT, RPS, TT><<<pd.S * (a.I / 32), kSwThreads, 0, st>>>(a, cc, pd);
+    return (int)hipGetLastError();
+}
+
+template <int WB, int RPS, int TT>
+static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
+{
+    k_down_sw<WB, RPS, TT><<<a.H / kDsRows, kDsThreads, down_lds_bytes(WB, a.I, pd), st>>>(a, cc, pd);
+    return (int)hipGetLastError();
 }
 
 // ---------------------------------------------------------------- dispatch
-template <int WB, int CPL, int TT>
+static int tt_for(int T) { return T <= 1 ? 1 : (T <= 4 ? 4 : 8); }
+
+// which row-sweep variant a row of cpr chunks takes (0: none, use the
+// row-group kernels)
+static int gate_up_sw_kind(int cpr) { return cpr == 192 ? 1 : cpr == 384 ? 2 : cpr == 96 ? 3 : 0; }
+static int down_sw_kind(int cpr) { return cpr == 64 ? 1 : cpr == 128 ? 2 : cpr == 32 ? 3 : 0; }
+
+template <int WB, int TT>
 static int run_gate_up(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
     const int grid = pd.S * (a.I / 32);
-    k_gate_up<WB, CPL, TT><<<grid, 256, 0, st>>>(a, cc, pd);
+    const size_t lds = a.T * act_lds_bytes(WB, a.H);
+    k_gate_up_rg<WB, TT><<<grid, 256, lds, st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
 
-template <int WB, int CPL, int TT>
+template <int WB, int TT>
 static int run_down(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
-    const int rows = cc.rw > 16 ? cc.rw : 16;
-    const size_t lds = down_lds_bytes(a, pd);
-    k_down<WB, CPL, TT><<<a.H / rows, 256, lds, st>>>(a, cc, pd, rows);
+    static_assert(kDnRows == kGemvDownRows, "rows per down workgroup");
+    k_down_rg<WB, TT><<<a.H / kDnRows, 256, down_lds_bytes(WB, a.I, pd), st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
 
-#define MOE_TT_SWITCH(FN, WB, CPL)                          \
-    switch (tt) {                                           \
-    case 1: return FN<WB, CPL, 1>(a, cc, pd, st);           \
-    case 4: return FN<WB, CPL, 4>(a, cc, pd, st);           \
-    default: return FN<WB, CPL, 8>(a, cc, pd, st);          \
-    }
-#define MOE_CPL_SWITCH(FN, WB)                              \
-    switch (cc.cpl) {                                       \
-    case 1: MOE_TT_SWITCH(FN, WB, 1)                        \
-    case 2: MOE_TT_SWITCH(FN, WB, 2)                        \
-    case 3: MOE_TT_SWITCH(FN, WB, 3)                        \
-    default: MOE_TT_SWITCH(FN, WB, 6)                       \
-    }
-#define MOE_WB_SWITCH(FN)                                   \
-    switch (a.wbits) {                                      \
-    case 2: MOE_CPL_SWITCH(FN, 2)                           \
-    case 4: MOE_CPL_SWITCH(FN, 4)                           \
-    default: MOE_CPL_SWITCH(FN, 8)                          \
+#define MOE_DISPATCH(FN)                                                        \
+    switch (a.wbits * 16 + tt_for(a.T)) {                                       \
+    case 2 * 16 + 1: return FN<2, 1>(a, cc, pd, st);                            \
+    case 2 * 16 + 4: return FN<2, 4>(a, cc, pd, st);                            \
+    case 2 * 16 + 8: return FN<2, 8>(a, cc, pd, st);                            \
+    case 4 * 16 + 1: return FN<4, 1>(a, cc, pd, st);                            \
+    case 4 * 16 + 4: return FN<4, 4>(a, cc, pd, st);                            \
+    case 4 * 16 + 8: return FN<4, 8>(a, cc, pd, st);                            \
+    case 8 * 16 + 1: return FN<8, 1>(a, cc, pd, st);                            \
+    case 8 * 16 + 4: return FN<8, 4>(a, cc, pd, st);                            \
+    default: return FN<8, 8>(a, cc, pd, st);                                    \
     }
 
-static int tt_for(int T) { return T <= 1 ? 1 : (T <= 4 ? 4 : 8); }
+#define MOE_SW_TT(FN, ...)                                                      \
+    switch (tt_for(a.T)) {                                                      \
+    case 1: return FN<__VA_ARGS__, 1>(a, cc, pd, st);                           \
+    case 4: return FN<__VA_ARGS__, 4>(a, cc, pd, st);                           \
+    default: return FN<__VA_ARGS__, 8>(a, cc, pd, st);                          \
+    }
 
 int launch_gate_up(const GemvArgs &a, hipStream_t st)
 {
     ChunkCfg cc;
     if (!chunk_cfg(a.H, a.wbits, cc)) return (int)hipErrorInvalidValue;
     const PlanDims pd = plan_dims(a.T, a.rc.k, a.n_shared, a.logits == nullptr);
-    const int tt = tt_for(a.T);
-    MOE_WB_SWITCH(run_gate_up)
+    const int kind = gate_up_sw_kind(cc.cpr);
+    if (kind == 1 && a.wbits == 4) { MOE_SW_TT(run_gate_up_sw, 4, 1, 1) }
+    if (kind == 1 && a.wbits == 8) { MOE_SW_TT(run_gate_up_sw, 8, 1, 1) }
+    if (kind == 1 && a.wbits == 2) { MOE_SW_TT(run_gate_up_sw, 2, 1, 1) }
+    if (kind == 2 && a.wbits == 8) { MOE_SW_TT(run_gate_up_sw, 8, 2, 1) }
+    if (kind == 2 && a.wbits == 4) { MOE_SW_TT(run_gate_up_sw, 4, 2, 1) }
+    if (kind == 3 && a.wbits == 2) { MOE_SW_TT(run_gate_up_sw, 2, 1, 2) }
+    if (kind == 3 && a.wbits == 4) { MOE_SW_TT(run_gate_up_sw, 4, 1, 2) }
+    MOE_DISPATCH(run_gate_up)
 }
 
 int launch_down(const GemvArgs &a, hipStream_t st)
@@ -455,8 +813,17 @@ int launch_down(const GemvArgs &a, hipStream_t st)
     ChunkCfg cc;
     if (!chunk_cfg(a.I, a.wbits, cc)) return (int)hipErrorInvalidValue;
     const PlanDims pd = plan_dims(a.T, a.rc.k, a.n_shared, a.logits == nullptr);
-    const int tt = tt_for(a.T);
-    MOE_WB_SWITCH(run_down)
+    const int kind = down_sw_kind(cc.cpr);
+    if (a.H % kDsRows == 0) {
+        if (kind == 1 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, 4) }
+        if (kind == 1 && a.wbits == 8) { MOE_SW_TT(run_down_sw, 8, 4) }
+        if (kind == 1 && a.wbits == 2) { MOE_SW_TT(run_down_sw, 2, 4) }
+        if (kind == 2 && a.wbits == 8) { MOE_SW_TT(run_down_sw, 8, 2) }
+        if (kind == 2 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, 2) }
+        if (kind == 3 && a.wbits == 2) { MOE_SW_TT(run_down_sw, 2, 8) }
+        if (kind == 3 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, 8) }
+    }
+    MOE_DISPATCH(run_down)
 }
 
 } // namespace moe

@@ -26,12 +26,9 @@ bool route_cfg(const moe_shape_t &s, RouteCfg &rc);
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Packing of one weight row into 16-byte chunks processed by a wave: a wave
-// tile covers `rw` rows = 64 * `cpl` chunks (cpl chunks per lane).
+// A weight row is read as `cpr` 16-byte chunks.
 struct ChunkCfg {
     int cpr;  // chunks per row
-    int rw;   // rows per wave tile
-    int cpl;  // chunks per lane
 };
 bool chunk_cfg(int in_dim, int wbits, ChunkCfg &cc);
 
@@ -61,10 +58,40 @@ inline PlanDims plan_dims(int T, int k, int n_shared, bool single)
     return d;
 }
 
+// LDS bytes of one token's staged activations over `in` elements: the int8
+// codes, one fp32 scale per block and (int4 / int2 only: the XOR offset
+// needs them) one int32 block sum per block, rounded up to 16 bytes.
+__host__ __device__ inline size_t act_lds_bytes(int wbits, int in)
+{
+    return ((size_t)in + (size_t)(in / 32) * (wbits == 8 ? 4 : 8) + 15) & ~(size_t)15;
+}
+// LDS of the down/combine kernel: the plan, then every pair's activations.
+inline size_t down_lds_bytes(int wbits, int I, const PlanDims &pd)
+{
+    return sizeof(int) * (size_t)((pd.words + 3) & ~3) + (size_t)pd.P * act_lds_bytes(wbits, I);
+}
+// LDS of the gate/up kernel: static plan / routing scratch plus Tc tokens of
+// staged activations over H.
+constexpr int kGemvDownRows = 16;  // rows per down/combine workgroup
+constexpr size_t kGateUpStaticLds = 12 * 1024;
+inline size_t gate_up_lds_bytes(int wbits, int H, int Tc) { return kGateUpStaticLds + Tc * act_lds_bytes(wbits, H); }
+// tokens per batch-union chunk: the largest count <= kGemvMaxT whose LDS fits
+// (0 if not even one token fits)
+inline int gemv_chunk_tokens(const moe_shape_t &s, int T)
+{
+    for (int tc = (T < kGemvMaxT ? T : kGemvMaxT); tc >= 1; tc--) {
+        const PlanDims pd = plan_dims(tc, s.top_k, s.n_shared, false);
+        if (down_lds_bytes(s.wbits, s.inter, pd) <= (size_t)kGemvMaxLdsAct &&
+            gate_up_lds_bytes(s.wbits, s.hidden, tc) <= (size_t)kGemvMaxLdsAct)
+            return tc;
+    }
+    return 0;
+}
+
 struct GemvWs {
     size_t logits, xq, xd, plan, qh, dh, total;
 };
-GemvWs gemv_ws(const moe_shape_t &s, int T, bool single);
+GemvWs gemv_ws(const moe_shape_t &s, int T, int Tc, bool single);
 
 // ---------------------------------------------------------------- launchers
 // (each returns hipGetLastError() as an int after its launch)
@@ -99,6 +126,9 @@ struct GemvArgs {
     float *w_out;
     int accumulate;
 };
+// one workgroup: routing of the chunk and its batch-union plan
+int launch_plan(const GemvArgs &a, hipStream_t st);
+// gate/up + SwiGLU + h quantisation of every slot of the published plan
 int launch_gate_up(const GemvArgs &a, hipStream_t st);
 int launch_down(const GemvArgs &a, hipStream_t st);
 

@@ -40,23 +40,39 @@ __global__ __launch_bounds__(256) void k_router_logits_small(
 #pragma unroll
         for (int t = 0; t < kGemvMaxT; t++) acc[t] = 0.0;
         const float4 *wr = reinterpret_cast<const float4 *>(gate_w + (size_t)e * H);
-        for (int i = tid; i < H / 4; i += 256) {
-            float4 w = wr[i];
+        const int n4 = H / 4;
+        constexpr int kPer = 8;  // float4s per thread per pass: all loads issued before use
+        for (int base = 0; base < n4; base += 256 * kPer) {
+            float4 w[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; j++) {
+                const int i = base + tid + 256 * j;
+                w[j] = (i < n4) ? wr[i] : make_float4(0, 0, 0, 0);
+            }
 #pragma unroll
             for (int t = 0; t < kGemvMaxT; t++) {
                 if (t < T) {
-                    float4 v = reinterpret_cast<const float4 *>(x + (size_t)t * H)[i];
-                    acc[t] = fma((double)w.x, (double)v.x, acc[t]);
-                    acc[t] = fma((double)w.y, (double)v.y, acc[t]);
-                    acc[t] = fma((double)w.z, (double)v.z, acc[t]);
-                    acc[t] = fma((double)w.w, (double)v.w, acc[t]);
+                    const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H);
+#pragma unroll
+                    for (int j = 0; j < kPer; j++) {
+                        const int i = base + tid + 256 * j;
+                        if (i < n4) {
+                            const float4 v = xr[i];
+                            acc[t] = fma((double)w[j].x, (double)v.x, acc[t]);
+                            acc[t] = fma((double)w[j].y, (double)v.y, acc[t]);
+                            acc[t] = fma((double)w[j].z, (double)v.z, acc[t]);
+                            acc[t] = fma((double)w[j].w, (double)v.w, acc[t]);
+                        }
+                    }
                 }
             }
         }
 #pragma unroll
         for (int t = 0; t < kGemvMaxT; t++) {
-            double v = wave_sum_d(acc[t]);
-            if (lane_id() == 0) red[wave_id()][t] = v;
+            if (t < T) {
+                double v = wave_sum_d(acc[t]);
+                if (lane_id() == 0) red[wave_id()][t] = v;
+            }
         }
         __syncthreads();
         if (tid < T) logits[(size_t)tid * E + e] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
@@ -139,19 +155,20 @@ int launch_router_logits_tiled(const float *x, int T, int H, const float *gate_w
     return (int)hipGetLastError();
 }
 
+// one workgroup per token
 __global__ __launch_bounds__(256) void k_topk(const RouteCfg rc, const double *__restrict__ logits,
                                               const float *__restrict__ bias, int T,
                                               int32_t *__restrict__ idx, float *__restrict__ w)
 {
-    const int t = blockIdx.x * 4 + wave_id();
-    if (t >= T) return;  // whole waves exit together
-    wave_topk(rc, logits + (size_t)t * rc.E, bias, idx + (size_t)t * rc.k, w + (size_t)t * rc.k);
+    __shared__ TopkLds tl;
+    const int t = blockIdx.x;
+    block_topk(rc, logits + (size_t)t * rc.E, bias, idx + (size_t)t * rc.k, w + (size_t)t * rc.k, tl);
 }
 
 int launch_topk(const RouteCfg &rc, const double *logits, const float *bias, int T, int32_t *idx,
                 float *w, hipStream_t st)
 {
-    k_topk<<<(T + 3) / 4, 256, 0, st>>>(rc, logits, bias, T, idx, w);
+    k_topk<<<T, 256, 0, st>>>(rc, logits, bias, T, idx, w);
     return (int)hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// Wave-level noaux_tc expert selection for one token (device code).
+// noaux_tc expert selection for one token (device code).
 //
 // DeepSeek-V3-style sigmoid router with noaux_tc (GeekNews #31297,
 // implemented features): s = sigmoid(z); the correction bias enters the
@@ -13,80 +13,118 @@
 
 namespace moe {
 
-// One wave routes one token.  Lane l holds experts l*epl .. l*epl+epl-1.
-__device__ __forceinline__ void wave_topk(const RouteCfg rc, const double *__restrict__ zt, const float *__restrict__ bias,
-                          int *sel_e, float *sel_w)
+// Order-preserving 64-bit key of a finite double (a larger double gets a
+// larger key); key 0 is below every finite value and marks "excluded".
+__device__ __forceinline__ uint64_t order_key(double v)
 {
-    const int lane = lane_id();
-    const int m = rc.E / rc.G;
-    double c[8], s[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        int e = lane * rc.epl + j;
-        bool ok = j < rc.epl && e < rc.E;
-        double z = ok ? zt[e] : 0.0;
-        s[j] = 1.0 / (1.0 + exp(-z));
-        c[j] = ok ? s[j] + (double)bias[e] : -INFINITY;
+    const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);  // -0 -> +0
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// LDS scratch of block_topk
+struct TopkLds {
+    uint64_t key[kMaxExperts];   // order key of c = s + bias
+    double c[kMaxExperts];
+    double s[kMaxExperts];       // sigmoid scores
+    double gs[kMaxGroups];       // group scores
+    int kept[kMaxGroups];        // kept groups, ascending
+    int nkept;
+    int rank[kMaxExperts];       // rank of each candidate among the kept
+    int sel_e[kMaxTopK];
+    double sel_s[kMaxTopK];
+};
+
+// Block-wide noaux_tc routing of one token (every thread of the block calls
+// it; blockDim.x >= 64).  The selection is a parallel rank count:
+//   rank(e) = #{kept candidates e' with c' > c, or c' == c and e' < e}
+// and e is selected at position rank(e) when that is below k.  Every phase
+// spreads its work over many lanes with independent loads: on MI355X a
+// dependent LDS or cross-lane round trip costs ~100 cycles, so serial
+// chains, not arithmetic, set the latency of this step.  All scores and
+// comparisons are fp64.
+__device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, const float *__restrict__ bias,
+                           int *sel_e, float *sel_w, TopkLds &L)
+{
+    const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id();
+    const int E = rc.E, G = rc.G, m = E / G;
+    for (int e = tid; e < E; e += nt) {
+        const double sv = 1.0 / (1.0 + exp(-zt[e]));
+        const double cv = sv + (double)bias[e];
+        L.s[e] = sv;
+        L.c[e] = cv;
+        L.key[e] = order_key(cv);
+        L.rank[e] = 0;
     }
-    // group score: sum of the two largest biased scores of the group
-    double b1 = -INFINITY, b2 = -INFINITY;
+    __syncthreads();
+    if (tid < 64) {
+        // group score = sum of the two largest c: lpg lanes per group (a power
+        // of two), each scanning <= 8 experts, then a lane butterfly
+        int lpg = 1;
+        while (lpg * 2 * G <= 64) lpg <<= 1;
+        const int g = lane / lpg, sub = lane % lpg;
+        double b1 = -INFINITY, b2 = -INFINITY;
+        if (g < G) {
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        if (c[j] > b1) { b2 = b1; b1 = c[j]; }
-        else if (c[j] > b2) b2 = c[j];
-    }
-    for (int o = 1; o < rc.lpg; o <<= 1) {
-        double o1 = __shfl_xor(b1, o), o2 = __shfl_xor(b2, o);
-        double n2 = fmax(fmin(b1, o1), fmax(b2, o2));
-        b1 = fmax(b1, o1);
-        b2 = n2;
-    }
-    const double gs = (m >= 2) ? b1 + b2 : b1;
-    const int g = lane / rc.lpg;
-    // keep the topk_group best groups (score desc, index asc)
-    int rank = 0;
-    for (int h = 0; h < rc.G; h++) {
-        double o = __shfl(gs, h * rc.lpg);
-        rank += (o > gs) || (o == gs && h < g);
-    }
-    const bool keep = g < rc.G && rank < rc.tg;
-    double bv = -INFINITY;
-    int bj = 0;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        if (!keep) c[j] = -INFINITY;
-        if (c[j] > bv) { bv = c[j]; bj = j; }
-    }
-    // k rounds of a wave arg-max (ties: lowest lane, then lowest j = lowest index)
-    double sum = 0.0, my_s = 0.0;
-    int my_e = 0;
-    for (int i = 0; i < rc.k; i++) {
-        double mx = wave_max_d(bv);
-        unsigned long long hit = __ballot(bv == mx);
-        int win = __ffsll((long long)hit) - 1;
-        int wj = __shfl(bj, win);
-        double sv = 0.0;
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-            if (j == bj) sv = s[j];
-        sv = __shfl(sv, win);
-        sum += sv;
-        if (lane == i) { my_e = win * rc.epl + wj; my_s = sv; }
-        if (lane == win) {
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                if (j == bj) c[j] = -INFINITY;
-            bv = -INFINITY;
-            bj = 0;
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                if (c[j] > bv) { bv = c[j]; bj = j; }
+            for (int j = 0; j < 8; j++) {
+                const int r = sub + lpg * j;
+                if (r < m) {
+                    const double cv = L.c[g * m + r];
+                    if (cv > b1) { b2 = b1; b1 = cv; }
+                    else if (cv > b2) b2 = cv;
+                }
+            }
         }
+        for (int o = 1; o < lpg; o <<= 1) {
+            const double o1 = __shfl_xor(b1, o), o2 = __shfl_xor(b2, o);
+            const double n2 = fmax(fmin(b1, o1), fmax(b2, o2));
+            b1 = fmax(b1, o1);
+            b2 = n2;
+        }
+        const double gsv = (m >= 2) ? b1 + b2 : b1;
+        // rank of each group among the G (score desc, index asc)
+        int grank = 0;
+        for (int h = 0; h < G; h++) {
+            const double o = __shfl(gsv, h * lpg);
+            grank += (o > gsv) || (o == gsv && h < g);
+        }
+        const bool keep = g < G && sub == 0 && grank < rc.tg;
+        const unsigned long long kb = __ballot(keep);
+        if (keep) L.kept[__popcll(kb & ((1ull << lane) - 1))] = g;
+        if (lane == 0) L.nkept = __popcll(kb);
     }
-    if (lane < rc.k) {
-        sel_e[lane] = my_e;
-        sel_w[lane] = (float)(my_s / sum * (double)rc.rsf);
+    __syncthreads();
+    // rank counting: one item = (candidate, kept group scanned)
+    const int nk = L.nkept, ncand = nk * m;
+    for (int it = tid; it < ncand * nk; it += nt) {
+        const int ci = it % ncand, gi = it / ncand;
+        const int e = L.kept[ci / m] * m + (ci % m);
+        const uint64_t ke = L.key[e];
+        const int base = L.kept[gi] * m;
+        int cnt = 0;
+        for (int j0 = 0; j0 < m; j0 += 8) {
+            uint64_t kj[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) kj[j] = (j0 + j < m) ? L.key[base + j0 + j] : 0ull;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                cnt += (kj[j] > ke) || (kj[j] == ke && base + j0 + j < e && j0 + j < m);
+        }
+        if (cnt) atomicAdd(&L.rank[e], cnt);
     }
+    __syncthreads();
+    for (int ci = tid; ci < ncand; ci += nt) {
+        const int e = L.kept[ci / m] * m + (ci % m);
+        const int r = L.rank[e];
+        if (r < rc.k) { L.sel_e[r] = e; L.sel_s[r] = L.s[e]; }
+    }
+    __syncthreads();
+    if (tid < rc.k) {
+        double sum = 0.0;
+        for (int i = 0; i < rc.k; i++) sum += L.sel_s[i];
+        sel_e[tid] = L.sel_e[tid];
+        sel_w[tid] = (float)(L.sel_s[tid] / sum * (double)rc.rsf);
+    }
+    __syncthreads();
 }
 
 } // namespace moe

@@ -115,8 +115,9 @@ def weights(w):
 
 
 def workspace(nbytes, device="cuda"):
-    """A device buffer for the *_workspace_bytes sizes (torch keeps 256-byte alignment)."""
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A zero-filled device buffer for the *_workspace_bytes sizes (torch keeps
+    256-byte alignment; moe_layer_forward needs zeros before the first use)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def moe_route_workspace_bytes(sh, T):

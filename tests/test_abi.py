@@ -60,7 +60,7 @@ def test_workspace_sizes(m):
 
 def test_stage_count(m):
     sh = big_shape(m)
-    assert m.moe_layer_stage_count(sh, 1) == 3          # router+quant, gate/up, down
+    assert m.moe_layer_stage_count(sh, 1) == 4          # router+quant, plan, gate/up, down
     assert m.moe_layer_stage_count(sh, 0) == 0
     assert m.moe_layer_stage_count(big_shape(m, top_k=40), 1) < 0
 

@@ -149,7 +149,7 @@ def test_route_ties_lower_index(dev, m):
 def test_permute_bit_exact(dev, m, T, k, E, skew):
     rng = np.random.default_rng(T + k + E)
     p = rng.dirichlet(np.full(E, 0.05 if skew else 5.0))
-    idx = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32).reshape(T, k)
+    idx = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(T)], np.int32).reshape(T, k)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
     off = torch.empty(E + 1, dtype=torch.int32, device=dev)
