@@ -53,6 +53,71 @@ size_t route_ws(const moe_shape_t &s, int T) { return align256(sizeof(double) * 
 // (plan, gate/up, down) for every chunk of Tc tokens.
 int gemv_stage_count(int T, int Tc) { return (T <= kGemvMaxT ? 1 : 2) + 3 * ((T + Tc - 1) / Tc); }
 
+// The grouped path's stages: router logits, top-k, quantiser, permutation
+// (three launches), gate/up, down, combine.
+constexpr int kGgStages = 7;
+
+// Which path serves a call: GEMV / GROUPED as asked; AUTO takes the grouped
+// path above kGemvMaxT tokens when its kernels take the shape.
+bool use_grouped(const moe_shape_t &s, int T, uint32_t flags)
+{
+    const uint32_t path = flags & 3u;
+    if (path == MOE_PATH_GROUPED) return true;
+    if (path == MOE_PATH_GEMV) return false;
+    return T > kGemvMaxT && gg_shape_ok(s);
+}
+
+// moe_layer_forward on the expert-grouped path (arguments already checked)
+int layer_grouped(const moe_shape_t &s, const float *x, int T, const float *gate_w, const float *bias,
+                  const moe_weights_t &routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
+                  float *w_out, uint32_t flags, void *ws, size_t ws_bytes, hipStream_t st)
+{
+    const GgWs L = gg_ws(s, T);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    const uint32_t sel = (flags & MOE_STAGE_MASK) >> 8;
+    auto run = [&](int stage) { return sel == 0 || ((sel >> stage) & 1u); };
+    char *base = static_cast<char *>(ws);
+    auto at = [&](size_t o) { return static_cast<void *>(base + o); };
+    const int H = s.hidden, E = s.n_experts, k = s.top_k;
+    RouteCfg rc;
+    route_cfg(s, rc);
+    double *logits = static_cast<double *>(at(L.logits));
+    int32_t *idx = idx_out ? idx_out : static_cast<int32_t *>(at(L.idx));
+    float *w = w_out ? w_out : static_cast<float *>(at(L.w));
+    GgArgs a{};
+    a.T = T; a.H = H; a.I = s.inter; a.E = E; a.k = k; a.n_shared = s.n_shared; a.wbits = s.wbits;
+    a.Tk = T * k;
+    a.tiles = static_cast<const int4 *>(at(L.tiles));
+    a.perm = static_cast<const int32_t *>(at(L.perm));
+    a.inv = static_cast<const int32_t *>(at(L.inv));
+    a.w = w;
+    a.routed = routed;
+    if (shared) a.shared = *shared;
+    a.xq = static_cast<const int8_t *>(at(L.xq));
+    a.xd = static_cast<const float *>(at(L.xd));
+    a.xs = static_cast<const float *>(at(L.xs));
+    a.qh = static_cast<int8_t *>(at(L.qh));
+    a.dh = static_cast<float *>(at(L.dh));
+    a.zh = static_cast<float *>(at(L.zh));
+    a.yrows = static_cast<float *>(at(L.y));
+    a.y = y;
+    a.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+    const int max_tiles = gg_max_tiles(s, T);
+    if (run(0) && launch_router_logits_tiled(x, T, H, gate_w, E, logits, st)) return MOE_EHIP;
+    if (run(1) && launch_topk(rc, logits, bias, T, idx, w, st)) return MOE_EHIP;
+    if (run(2) && launch_gg_quant(x, T, H, const_cast<int8_t *>(a.xq), const_cast<float *>(a.xd),
+                                  const_cast<float *>(a.xs), st))
+        return MOE_EHIP;
+    if (run(3) && launch_permute(idx, T, k, E, const_cast<int32_t *>(a.perm), static_cast<int32_t *>(at(L.off)),
+                                 const_cast<int32_t *>(a.inv), static_cast<int32_t *>(at(L.pscr)),
+                                 const_cast<int4 *>(a.tiles), s.n_shared, st))
+        return MOE_EHIP;
+    if (run(4) && launch_gg_gate_up(a, max_tiles, st)) return MOE_EHIP;
+    if (run(5) && launch_gg_down(a, max_tiles, st)) return MOE_EHIP;
+    if (run(6) && launch_gg_combine(a, st)) return MOE_EHIP;
+    return MOE_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -116,8 +181,8 @@ int moe_block_dots(int32_t wbits, const uint8_t *codes, int32_t rows, int32_t D,
 
 size_t moe_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags)
 {
-    (void)flags;
-    if (check_shape(shape) || T < 0) return 0;
+    if (check_shape(shape) || T < 0 || (flags & 3u) == 3u) return 0;
+    if (use_grouped(*shape, T, flags)) return gg_shape_ok(*shape) ? gg_ws(*shape, T > 0 ? T : 1).total : 0;
     const int Tc = gemv_chunk_tokens(*shape, T > 0 ? T : 1);
     if (!Tc) return 0;
     return gemv_ws(*shape, T, Tc, false).total;
@@ -127,7 +192,8 @@ int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags)
 {
     if (check_shape(shape) || T < 0) return -MOE_EINVAL;
     if (T == 0) return 0;
-    if ((flags & 3u) == MOE_PATH_GROUPED) return -MOE_EUNSUPPORTED;
+    if ((flags & 3u) == 3u) return -MOE_EINVAL;
+    if (use_grouped(*shape, T, flags)) return gg_shape_ok(*shape) ? kGgStages : -MOE_EUNSUPPORTED;
     const int Tc = gemv_chunk_tokens(*shape, T);
     if (!Tc) return -MOE_EUNSUPPORTED;
     return gemv_stage_count(T, Tc);
@@ -180,12 +246,15 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
     if (flags & ~(3u | MOE_ACCUMULATE | MOE_STAGE_MASK)) return MOE_EINVAL;
     const uint32_t path = flags & 3u;
     if (path == 3u) return MOE_EINVAL;
-    if (path == MOE_PATH_GROUPED) return MOE_EUNSUPPORTED;
+    if (path == MOE_PATH_GROUPED && !gg_shape_ok(*shape)) return MOE_EUNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!x || !gate_w || !bias || !y || !ws) return MOE_EINVAL;
     if ((idx_out == nullptr) != (w_out == nullptr)) return MOE_EINVAL;
     if (!al(x, 16) || !al(gate_w, 16) || !al(y, 4) || !al(ws, 256)) return MOE_EINVAL;
     if (x == y) return MOE_EINVAL;
+    if (use_grouped(*shape, T, flags))
+        return layer_grouped(*shape, x, T, gate_w, bias, *routed, shared, y, idx_out, w_out, flags, ws, ws_bytes,
+                             stream);
     if (shape->hidden % kGemvDownRows) return MOE_EUNSUPPORTED;
     const int Tc = gemv_chunk_tokens(*shape, T);
     if (!Tc) return MOE_EUNSUPPORTED;
@@ -263,7 +332,7 @@ int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *pe
     if (E > kMaxExperts) return MOE_EUNSUPPORTED;
     if (!off || !ws || (T > 0 && (!idx || !perm || !inv))) return MOE_EINVAL;
     if (ws_bytes < moe_permute_workspace_bytes(T, k, E)) return MOE_EWORKSPACE;
-    return hip_rc(launch_permute(idx, T, k, E, perm, off, inv, static_cast<int32_t *>(ws), stream));
+    return hip_rc(launch_permute(idx, T, k, E, perm, off, inv, static_cast<int32_t *>(ws), nullptr, 0, stream));
 }
 
 } // extern "C"

@@ -107,10 +107,12 @@ int launch_block_dots(int wbits, const uint8_t *codes, int rows, int D, const in
 // Stable counting sort of the T*k assignments by expert (batch-union MoE,
 // GeekNews #31297 implemented features), in three launches:
 //  k_perm_count  tile j of 256 assignments writes its per-expert counts
-//  k_perm_scan   one block: per expert, running sums over tiles, then the
-//                exclusive scan over experts gives off[] and tile bases
-//  k_perm_place  each assignment's row = its tile base + the number of
-//                earlier assignments of the same expert in its tile
+//  k_perm_scan   one block: per expert, the running sum over tiles (each
+//                tile's start within its expert), then the exclusive scan
+//                over experts gives off[]; optionally the grouped path's
+//                tile list
+//  k_perm_place  each assignment's row = off[e] + its tile's start + the
+//                number of earlier assignments of the same expert in its tile
 __global__ __launch_bounds__(256) void k_perm_count(const int32_t *__restrict__ idx, int n, int E,
                                                     int32_t *__restrict__ cnt /*[tiles][E]*/)
 {
@@ -123,35 +125,69 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t *__restrict__ 
     for (int e = threadIdx.x; e < E; e += 256) cnt[(size_t)blockIdx.x * E + e] = c[e];
 }
 
-__global__ __launch_bounds__(512) void k_perm_scan(int tiles, int E, int32_t *__restrict__ cnt,
-                                                   int32_t *__restrict__ off)
+// exclusive prefix sum over the 512 threads of a block (wave scans, then the
+// eight wave totals); `tot` receives the block total
+__device__ int block_scan_512(int v, int *wsum, int &tot)
 {
-    __shared__ int tot[kMaxExperts + 1];
+    const int l = lane_id(), w = wave_id();
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (l >= o) x += y;
+    }
+    if (l == kWave - 1) wsum[w] = x;
+    __syncthreads();
+    int pre = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int s = wsum[i];
+        pre += (i < w) ? s : 0;
+        all += s;
+    }
+    tot = all;
+    return pre + x - v;
+}
+
+__global__ __launch_bounds__(512) void k_perm_scan(int tiles, int E, int32_t *__restrict__ cnt,
+                                                   int32_t *__restrict__ off, int4 *__restrict__ gtiles, int T,
+                                                   int k, int n_shared)
+{
+    __shared__ int ws0[8], ws1[8];
     const int e = threadIdx.x;
     int run = 0;
-    if (e < E)
-        for (int j = 0; j < tiles; j++) {
-            const int v = cnt[(size_t)j * E + e];
-            cnt[(size_t)j * E + e] = run;
-            run += v;
-        }
-    if (e < E) tot[e] = run;
-    __syncthreads();
-    if (e == 0) {
-        int s = 0;
-        for (int i = 0; i < E; i++) { const int v = tot[i]; tot[i] = s; s += v; }
-        tot[E] = s;
-    }
-    __syncthreads();
     if (e < E) {
-        off[e] = tot[e];
-        for (int j = 0; j < tiles; j++) cnt[(size_t)j * E + e] += tot[e];
+        for (int j0 = 0; j0 < tiles; j0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) v[u] = (j0 + u < tiles) ? cnt[(size_t)(j0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                if (j0 + u < tiles) {
+                    cnt[(size_t)(j0 + u) * E + e] = run;
+                    run += v[u];
+                }
+        }
     }
-    if (e == 0) off[E] = tot[E];
+    int total;
+    const int base = block_scan_512(run, ws0, total);
+    if (e < E) off[e] = base;
+    if (e == 0) off[E] = total;
+    if (!gtiles) return;
+    const int nte = (e < E) ? (run + kGgTN - 1) / kGgTN : 0;
+    int ntr;
+    const int tb = block_scan_512(nte, ws1, ntr);
+    for (int j = 0; j < nte; j++)
+        gtiles[1 + tb + j] = make_int4(e, base + j * kGgTN, min(kGgTN, run - j * kGgTN), 0);
+    const int Tk = T * k, ns = n_shared ? (T + kGgTN - 1) / kGgTN : 0;
+    for (int j = e; j < ns; j += 512)
+        gtiles[1 + ntr + j] = make_int4(E, Tk + j * kGgTN, min(kGgTN, T - j * kGgTN), 0);
+    if (e == 0) gtiles[0] = make_int4(ntr + ns, 0, 0, 0);
 }
 
 __global__ __launch_bounds__(256) void k_perm_place(const int32_t *__restrict__ idx, int n, int E,
-                                                    const int32_t *__restrict__ base, int32_t *__restrict__ perm,
+                                                    const int32_t *__restrict__ base,
+                                                    const int32_t *__restrict__ off, int32_t *__restrict__ perm,
                                                     int32_t *__restrict__ inv)
 {
     __shared__ int s_e[256];
@@ -162,18 +198,18 @@ __global__ __launch_bounds__(256) void k_perm_place(const int32_t *__restrict__ 
     const int e = s_e[threadIdx.x];
     int r = 0;
     for (int j = 0; j < (int)threadIdx.x; j++) r += (s_e[j] == e);
-    const int row = base[(size_t)blockIdx.x * E + e] + r;
+    const int row = off[e] + base[(size_t)blockIdx.x * E + e] + r;
     perm[row] = a;
     inv[a] = row;
 }
 
 int launch_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32_t *off, int32_t *inv,
-                   int32_t *scratch, hipStream_t st)
+                   int32_t *scratch, int4 *tiles, int n_shared, hipStream_t st)
 {
-    const int n = T * k, tiles = (n + 255) / 256;
-    if (tiles) k_perm_count<<<tiles, 256, 0, st>>>(idx, n, E, scratch);
-    k_perm_scan<<<1, 512, 0, st>>>(tiles, E, scratch, off);
-    if (tiles) k_perm_place<<<tiles, 256, 0, st>>>(idx, n, E, scratch, perm, inv);
+    const int n = T * k, nt = perm_tiles(n);
+    if (nt) k_perm_count<<<nt, 256, 0, st>>>(idx, n, E, scratch);
+    k_perm_scan<<<1, 512, 0, st>>>(nt, E, scratch, off, tiles, T, k, n_shared);
+    if (nt) k_perm_place<<<nt, 256, 0, st>>>(idx, n, E, scratch, off, perm, inv);
     return (int)hipGetLastError();
 }
 

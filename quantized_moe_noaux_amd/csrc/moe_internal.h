@@ -132,10 +132,56 @@ int launch_plan(const GemvArgs &a, hipStream_t st);
 int launch_gate_up(const GemvArgs &a, hipStream_t st);
 int launch_down(const GemvArgs &a, hipStream_t st);
 
+// ---------------------------------------------------------------- grouped path
+constexpr int kGgTN = 64;  // rows (token, expert assignments) per grouped-GEMM tile
+
+// 256-assignment tiles of the permutation's counting sort
+inline int perm_tiles(int n) { return (n + 255) / 256; }
+// rows of the grouped problem: T*k routed assignments, then T shared rows
+inline size_t gg_rows(const moe_shape_t &s, int T) { return (size_t)T * s.top_k + (size_t)s.n_shared * T; }
+// upper bound of the tile count: sum_e ceil(n_e / TN) <= T*k/TN + (experts used)
+inline int gg_max_tiles(const moe_shape_t &s, int T)
+{
+    const long tk = (long)T * s.top_k;
+    const long used = tk < s.n_experts ? tk : s.n_experts;
+    return (int)(tk / kGgTN + used + 1 + (s.n_shared ? (T + kGgTN - 1) / kGgTN : 0));
+}
+// shapes the grouped kernels take: 64-channel gate/up tiles, 128-channel down
+// tiles, K in steps of 64
+inline bool gg_shape_ok(const moe_shape_t &s) { return s.hidden % 128 == 0 && s.inter % 64 == 0; }
+
+struct GgWs {
+    size_t logits, idx, w, xq, xd, xs, perm, off, inv, pscr, tiles, qh, dh, zh, y, total;
+};
+GgWs gg_ws(const moe_shape_t &s, int T);
+
+struct GgArgs {
+    int T, H, I, E, k, n_shared, wbits, Tk;
+    const int4 *tiles;      // [0].x = count, then {expert (E = shared), first row, rows, 0}
+    const int32_t *perm;    // row -> assignment t*k + slot
+    const int32_t *inv;     // assignment -> row
+    const float *w;         // combine weight of each assignment
+    moe_weights_t routed, shared;
+    const int8_t *xq;       // [T][H] int8 x, block scales xd, offset sums xs
+    const float *xd, *xs;
+    int8_t *qh;             // [rows][I] int8 h, block scales dh, zh = dh * code sum
+    float *dh, *zh;
+    float *yrows;           // [rows][H] weighted expert outputs
+    float *y;               // [T][H] layer output
+    int accumulate;
+};
+int launch_gg_quant(const float *x, int T, int D, int8_t *q, float *d, float *xs, hipStream_t st);
+int launch_gg_gate_up(const GgArgs &a, int max_tiles, hipStream_t st);
+int launch_gg_down(const GgArgs &a, int max_tiles, hipStream_t st);
+int launch_gg_combine(const GgArgs &a, hipStream_t st);
+
 int launch_rmsnorm(const float *x, const float *g, double eps, int T, int H, float *out, hipStream_t st);
 int launch_block_dots(int wbits, const uint8_t *codes, int rows, int D, const int8_t *q, int T,
                       int32_t *out, hipStream_t st);
+// Stable counting sort of the T*k assignments by expert.  With tiles != null
+// it also writes the grouped path's tile list (kGgTN rows per tile, then the
+// n_shared * T shared rows).
 int launch_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32_t *off, int32_t *inv,
-                   int32_t *scratch, hipStream_t st);
+                   int32_t *scratch, int4 *tiles, int n_shared, hipStream_t st);
 
 } // namespace moe

@@ -63,6 +63,25 @@ def test_stage_count(m):
     assert m.moe_layer_stage_count(sh, 1) == 4          # router+quant, plan, gate/up, down
     assert m.moe_layer_stage_count(sh, 0) == 0
     assert m.moe_layer_stage_count(big_shape(m, top_k=40), 1) < 0
+    # grouped path: logits, top-k, quant, permute, gate/up, down, combine
+    assert m.moe_layer_stage_count(sh, 2048) == 7
+    assert m.moe_layer_stage_count(sh, 1, m.MOE_PATH_GROUPED) == 7
+    assert m.moe_layer_stage_count(sh, 2048, m.MOE_PATH_GEMV) > 2 + 3 * 256   # chunks of <= 8 tokens
+    assert m.moe_layer_stage_count(sh, 1, 3) < 0
+
+
+def test_grouped_workspace(m):
+    sh = big_shape(m)
+    G = m.MOE_PATH_GROUPED
+    ws = m.moe_workspace_bytes(sh, 2048)                 # AUTO -> grouped
+    assert ws == m.moe_workspace_bytes(sh, 2048, G)
+    rows = 2048 * 9
+    assert ws > rows * 6144 * 4 + rows * 2048            # expert outputs + int8 h
+    assert ws % 256 == 0
+    assert m.moe_workspace_bytes(sh, 1, G) > 0
+    assert m.moe_workspace_bytes(big_shape(m, hidden=6080), 2048, G) == 0   # 6080 % 128 != 0
+    # AUTO falls back to the GEMV path where the grouped kernels do not fit
+    assert m.moe_workspace_bytes(big_shape(m, hidden=6080), 2048) > 0
 
 
 NULL = None
@@ -93,6 +112,8 @@ def test_layer_argument_errors_launch_nothing(m):
     assert call_layer(m, big_shape(m, top_k=33, topk_group=8)) == m.MOE_EUNSUPPORTED
     assert call_layer(m, big_shape(m, n_experts=1024, n_group=8)) == m.MOE_EUNSUPPORTED
     assert call_layer(m, sh, T=0) == m.MOE_OK                               # no-op
+    assert call_layer(m, big_shape(m, hidden=6080), flags=m.MOE_PATH_GROUPED) == m.MOE_EUNSUPPORTED
+    assert call_layer(m, sh, T=2048, ws_bytes=1 << 20) == m.MOE_EWORKSPACE  # grouped sizes
 
 
 def test_other_entry_point_errors(m):

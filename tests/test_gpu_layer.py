@@ -65,8 +65,8 @@ def test_tiny_layer_chunked_tokens(dev, m):
     # more tokens than one batch-union chunk: the GEMV path runs in chunks of 8
     wl = synth.workload("tiny", T=21)
     L = DevLayer(wl, dev)
-    assert m.moe_layer_stage_count(m.shape_of(wl), 21) == 2 + 3 * 3
-    check(m, L)
+    assert m.moe_layer_stage_count(m.shape_of(wl), 21, m.MOE_PATH_GEMV) == 2 + 3 * 3
+    check(m, L, flags=m.MOE_PATH_GEMV)
 
 
 # ---------------------------------------------------------------- full-size layers
