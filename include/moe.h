@@ -78,9 +78,19 @@ enum {
 const char *moe_strerror(int code);
 
 /* ---------------------------------------------------------------- flags */
-#define MOE_PATH_AUTO     0u  /* GEMV for small T, grouped GEMM otherwise */
-#define MOE_PATH_GEMV     1u  /* batch-union GEMV (T <= 8) */
-#define MOE_PATH_GROUPED  2u  /* token-permuted expert-grouped int8 MFMA GEMM */
+/* Paths.  GEMV: the batch-union plan of up to 8 tokens at a time, each
+ * selected expert's rows streamed once per chunk and dotted against every
+ * token of the chunk routed to it (HBM-bound decode and verify batches).
+ * GROUPED: the T*k (token, expert) assignments are sorted by expert (as
+ * moe_permute) and each expert's rows run as int8 MFMA GEMMs in tiles of 64
+ * assignments, with a separate fixed-order combine (prefill); it takes
+ * shapes with H a multiple of 128 and I a multiple of 64 and returns
+ * MOE_EUNSUPPORTED otherwise.  AUTO: GEMV up to 8 tokens, GROUPED above
+ * when the shape allows it, else GEMV.  Both paths give the same routing
+ * bit for bit; their float outputs differ only by rounding order. */
+#define MOE_PATH_AUTO     0u
+#define MOE_PATH_GEMV     1u
+#define MOE_PATH_GROUPED  2u
 #define MOE_ACCUMULATE    4u  /* y += layer(x) instead of y = layer(x) */
 /* Stage selection, for timing one kernel of the path in isolation: when any
  * MOE_STAGE bit is set, only the selected launches of the path run, in
@@ -156,8 +166,12 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
                       float *y, int32_t *idx_out, float *w_out, uint32_t flags,
                       void *ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags);
-/* number of kernel launches moe_layer_forward makes for these arguments
- * (the n of MOE_STAGE(n) runs from 0 to this minus 1); < 0 on bad arguments */
+/* number of stages moe_layer_forward runs for these arguments (the n of
+ * MOE_STAGE(n) runs from 0 to this minus 1); < 0 on bad arguments.
+ * GEMV path: router + quantiser (one launch for T <= 8, else two), then
+ * plan, gate/up, down per chunk of tokens.  GROUPED path: 7 stages -- router
+ * logits, top-k, quantiser, permutation (three launches), gate/up, down,
+ * combine. */
 int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags);
 
 /* ---------------------------------------------------------------- stack */

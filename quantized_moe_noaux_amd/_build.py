@@ -14,6 +14,9 @@ FLAGS = [
     "-fno-gpu-rdc", "-ffp-contract=fast", "-Wall", "-Wno-unused-function",
     # keep packed fp32 instructions out of the code objects
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the grouped GEMMs rescale every int32 block
+    # result on the VALU, which cannot read accumulation registers directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -46,7 +46,7 @@ int check_weights(const moe_weights_t *w)
 
 inline int hip_rc(int e) { return e ? MOE_EHIP : MOE_OK; }
 
-size_t route_ws(const moe_shape_t &s, int T) { return align256(sizeof(double) * (size_t)T * s.n_experts); }
+size_t route_ws(const moe_shape_t &s, int T) { return align256(router_logit_bytes(s, T)); }
 
 // The stage list of the GEMV path for T tokens: the router / quantiser
 // launch(es), then
@@ -103,8 +103,9 @@ int layer_grouped(const moe_shape_t &s, const float *x, int T, const float *gate
     a.y = y;
     a.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
     const int max_tiles = gg_max_tiles(s, T);
-    if (run(0) && launch_router_logits_tiled(x, T, H, gate_w, E, logits, st)) return MOE_EHIP;
-    if (run(1) && launch_topk(rc, logits, bias, T, idx, w, st)) return MOE_EHIP;
+    const int ksplit = router_ksplit(T, H, E);
+    if (run(0) && launch_router_logits_mfma(x, T, H, gate_w, E, ksplit, logits, st)) return MOE_EHIP;
+    if (run(1) && launch_topk(rc, logits, ksplit, bias, T, idx, w, st)) return MOE_EHIP;
     if (run(2) && launch_gg_quant(x, T, H, const_cast<int8_t *>(a.xq), const_cast<float *>(a.xd),
                                   const_cast<float *>(a.xs), st))
         return MOE_EHIP;
@@ -153,11 +154,12 @@ int moe_route(const moe_shape_t *shape, const float *x, int32_t T, const float *
     RouteCfg rcfg;
     route_cfg(*shape, rcfg);
     double *logits = static_cast<double *>(ws);
+    const int ksplit = router_ksplit(T, shape->hidden, shape->n_experts);
     int e = (T <= kGemvMaxT)
                 ? launch_router_logits(x, T, shape->hidden, gate_w, shape->n_experts, logits, nullptr, nullptr, stream)
-                : launch_router_logits_tiled(x, T, shape->hidden, gate_w, shape->n_experts, logits, stream);
+                : launch_router_logits_mfma(x, T, shape->hidden, gate_w, shape->n_experts, ksplit, logits, stream);
     if (e) return MOE_EHIP;
-    return hip_rc(launch_topk(rcfg, logits, bias, T, topk_idx, topk_w, stream));
+    return hip_rc(launch_topk(rcfg, logits, ksplit, bias, T, topk_idx, topk_w, stream));
 }
 
 int moe_quant_act(const float *x, int32_t T, int32_t D, int8_t *q, float *d, hipStream_t stream)
@@ -270,12 +272,14 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
     int8_t *xq = reinterpret_cast<int8_t *>(base + L.xq);
     float *xd = reinterpret_cast<float *>(base + L.xd);
     const int H = shape->hidden, nb = H / 32, E = shape->n_experts, k = shape->top_k;
+    const int ksplit = router_ksplit(T, H, E);
     auto args = [&](int c0, int tc) {
         GemvArgs a{};
         a.T = tc;
         a.H = H; a.I = shape->inter; a.E = E; a.wbits = shape->wbits; a.n_shared = shape->n_shared;
         route_cfg(*shape, a.rc);
         a.logits = logits + (size_t)c0 * E; a.bias = bias; a.single = -1;
+        a.lstride = (size_t)T * E; a.lparts = ksplit;
         a.routed = *routed;
         if (shared) a.shared = *shared;
         a.xq = xq + (size_t)c0 * H; a.xd = xd + (size_t)c0 * nb;
@@ -293,7 +297,7 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
         if (run(stage) && launch_router_logits(x, T, H, gate_w, E, logits, xq, xd, stream)) return MOE_EHIP;
         stage++;
     } else {
-        if (run(stage) && launch_router_logits_tiled(x, T, H, gate_w, E, logits, stream)) return MOE_EHIP;
+        if (run(stage) && launch_router_logits_mfma(x, T, H, gate_w, E, ksplit, logits, stream)) return MOE_EHIP;
         stage++;
         if (run(stage) && launch_quant(x, T, H, xq, xd, stream)) return MOE_EHIP;
         stage++;

@@ -43,7 +43,7 @@ GemvWs gemv_ws(const moe_shape_t &s, int T, int Tc, bool single)
     // plan and h buffers hold one chunk of Tc tokens
     PlanDims pd = plan_dims(Tc, s.top_k, s.n_shared, single);
     size_t o = 0;
-    w.logits = o; o = align256(o + sizeof(double) * (size_t)T * E);
+    w.logits = o; o = align256(o + router_logit_bytes(s, T));
     w.xq = o;     o = align256(o + (size_t)T * H);
     w.xd = o;     o = align256(o + sizeof(float) * (size_t)T * (H / 32));
     w.plan = o;   o = align256(o + sizeof(int) * (size_t)pd.words);
@@ -89,7 +89,7 @@ __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int
     }
     for (int i = tid; i < T * 16; i += nt) tokbits[i >> 4][i & 15] = 0u;
     for (int t = 0; t < T; t++)
-        block_topk(a.rc, a.logits + (size_t)t * a.E, a.bias, s_idx + t * k, s_w + t * k, *tl);
+        block_topk(a.rc, a.logits + (size_t)t * a.E, a.lstride, a.lparts, a.bias, s_idx + t * k, s_w + t * k, *tl);
     for (int i = tid; i < T * k; i += nt) {
         const int e = s_idx[i];
         atomicOr(&tokbits[i / k][e >> 5], 1u << (e & 31));

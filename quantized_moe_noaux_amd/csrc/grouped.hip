@@ -49,7 +49,7 @@ GgWs gg_ws(const moe_shape_t &s, int T)
     const int H = s.hidden, I = s.inter, E = s.n_experts, k = s.top_k;
     const size_t Tk = (size_t)T * k, R = gg_rows(s, T);
     size_t o = 0;
-    w.logits = o; o = align256(o + sizeof(double) * (size_t)T * E);
+    w.logits = o; o = align256(o + router_logit_bytes(s, T));
     w.idx = o;    o = align256(o + sizeof(int32_t) * Tk);
     w.w = o;      o = align256(o + sizeof(float) * Tk);
     w.xq = o;     o = align256(o + (size_t)T * H);
@@ -150,16 +150,16 @@ template <> struct GgW<4> {
 
 template <> struct GgW<8> {
     static constexpr int kOff = 0;
-    uint4 r0, r1;
+    v4i r0, r1;
     __device__ __forceinline__ void load(const uint8_t *row, int k0, int half)
     {
-        const uint4 *p = reinterpret_cast<const uint4 *>(row + k0 + 32 * half);
+        const v4i *p = reinterpret_cast<const v4i *>(row + k0 + 32 * half);
         r0 = p[0];
         r1 = p[1];
     }
     __device__ __forceinline__ void store(uint8_t *lds_row, int half) const
     {
-        uint4 *p = reinterpret_cast<uint4 *>(lds_row + 32 * half);
+        v4i *p = reinterpret_cast<v4i *>(lds_row + 32 * half);
         p[0] = r0;
         p[1] = r1;
     }
@@ -219,7 +219,8 @@ struct GgLds {
 
 __device__ __forceinline__ v4i lds16(const uint8_t *p) { return *reinterpret_cast<const v4i *>(p); }
 
-// Main loop shared by both GEMMs.  L.arow must be set.  Thread tid loads
+// Main loop shared by both GEMMs (n = live rows of the tile).  L.arow must
+// be set.  Thread tid loads
 // weight row tid/2 (wsrc), half tid%2 of each step; activation row tid/4,
 // 16-byte part tid%4; and (tid < 128) the scale of row tid/2, block tid%2.
 // Wave w computes activation rows 32*nt .. +32 of the tile against weight
@@ -228,9 +229,11 @@ __device__ __forceinline__ v4i lds16(const uint8_t *p) { return *reinterpret_cas
 // activation row l%32.
 template <int WB>
 __device__ __forceinline__ void gg_mainloop(GgLds &L, const uint8_t *wsrc, const int8_t *__restrict__ aq,
-                                            const float *__restrict__ ad, int K, int nt, int m0, int m1,
+                                            const float *__restrict__ ad, int K, int nt, int m0, int m1, int n,
                                             float (&acc0)[16], float (&acc1)[16])
 {
+    // a wave whose 32 rows are all padding only loads and stages
+    const bool live = 32 * nt < n;
     const int tid = threadIdx.x, l = lane_id();
     const int nbk = K / 32, nsteps = K / kGgKS;
     const int wr = tid >> 1, wh = tid & 1;
@@ -266,7 +269,7 @@ __device__ __forceinline__ void gg_mainloop(GgLds &L, const uint8_t *wsrc, const
         const int buf = s & 1;
         if (s + 1 < nsteps) fetch(s + 1);
 #pragma unroll
-        for (int b = 0; b < 2; b++) {
+        for (int b = 0; b < 2 && live; b++) {
             const int koff = 32 * b + 16 * (l >> 5);
             const v4i a0 = lds16(&L.w[buf][32 * m0 + (l & 31)][koff]);
             const v4i a1 = lds16(&L.w[buf][32 * m1 + (l & 31)][koff]);
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(kGgThreads) void k_gg_gate_up(const GgArgs a)
     const uint8_t *wsrc = (wr < 64) ? W.gate + (eo * I + c0 + wr) * rb : W.up + (eo * I + c0 + wr - 64) * rb;
     const int wv = wave_id(), nt = wv >> 1, mh = wv & 1;
     float ag[16], au[16];
-    gg_mainloop<WB>(L, wsrc, a.xq, a.xd, H, nt, mh, 2 + mh, ag, au);
+    gg_mainloop<WB>(L, wsrc, a.xq, a.xd, H, nt, mh, 2 + mh, n, ag, au);
 
     // epilogue: lane = (tile row i, channel half hf); 16 channels of the
     // wave's 32-channel block cb
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(kGgThreads) void k_gg_down(const GgArgs a)
     const uint8_t *wsrc = W.down + (eo * H + n0 + (tid >> 1)) * rb;
     const int wv = wave_id(), nt = wv >> 1, m0 = 2 * (wv & 1);
     float y0[16], y1[16];
-    gg_mainloop<WB>(L, wsrc, a.qh, a.dh, I, nt, m0, m0 + 1, y0, y1);
+    gg_mainloop<WB>(L, wsrc, a.qh, a.dh, I, nt, m0, m0 + 1, n, y0, y1);
 
     const int l = lane_id(), i = 32 * nt + (l & 31), hf = l >> 5;
     if (i >= n) return;

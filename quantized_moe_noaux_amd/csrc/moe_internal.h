@@ -97,9 +97,17 @@ GemvWs gemv_ws(const moe_shape_t &s, int T, int Tc, bool single);
 // (each returns hipGetLastError() as an int after its launch)
 int launch_router_logits(const float *x, int T, int H, const float *gate_w, int E, double *logits,
                          int8_t *xq, float *xd, hipStream_t st);
-int launch_router_logits_tiled(const float *x, int T, int H, const float *gate_w, int E, double *logits,
-                               hipStream_t st);
-int launch_topk(const RouteCfg &rc, const double *logits, const float *bias, int T, int32_t *idx,
+// Router logits of more than kGemvMaxT tokens: fp64 MFMA over `ksplit`
+// slices of the hidden dimension, partial sums in part[ksplit][T][E]
+// (router_ksplit picks the slice count; 1 for T <= kGemvMaxT).
+int router_ksplit(int T, int H, int E);
+inline size_t router_logit_bytes(const moe_shape_t &s, int T)
+{
+    return sizeof(double) * (size_t)router_ksplit(T, s.hidden, s.n_experts) * T * s.n_experts;
+}
+int launch_router_logits_mfma(const float *x, int T, int H, const float *gate_w, int E, int ksplit, double *part,
+                              hipStream_t st);
+int launch_topk(const RouteCfg &rc, const double *logits, int nparts, const float *bias, int T, int32_t *idx,
                 float *w, hipStream_t st);
 int launch_quant(const float *x, int T, int D, int8_t *q, float *d, hipStream_t st);
 
@@ -107,8 +115,11 @@ struct GemvArgs {
     // shape
     int T, H, I, E, wbits, n_shared;
     RouteCfg rc;
-    // routing (logits == nullptr: single-expert mode on expert `single`)
+    // routing (logits == nullptr: single-expert mode on expert `single`);
+    // a token's logits are the sum of lparts slices lstride apart
     const double *logits;
+    size_t lstride;
+    int lparts;
     const float *bias;
     int single;
     // weights

@@ -101,74 +101,131 @@ int launch_router_logits(const float *x, int T, int H, const float *gate_w, int 
 }
 
 // ---------------------------------------------------------------- logits, any T
-// 64 tokens x 64 experts per workgroup, 4 x 4 per thread, K in steps of 16
-// staged in LDS already widened to fp64.
-__global__ __launch_bounds__(256) void k_router_logits_tiled(
-    const float *__restrict__ x, int T, int H, const float *__restrict__ gate_w, int E,
-    double *__restrict__ logits)
+// fp64 matrix cores: v_mfma_f64_16x16x4f64 on x (tokens) and gate_w
+// (experts), both widened from fp32 in registers (exact).  One wave owns 32
+// tokens x 64 experts over one of `ksplit` equal K slices; the partial sums
+// land in part[slice][T][E] and the top-k kernel adds the slices in order.
+// Lane l feeds row / column l%16 of each 16x16 tile with k = 4*(l/16) + s of
+// every 16-wide K block (s = 0..3: one float4 per lane and operand); the
+// result of lane l, register v is row l/16 + 4v, column l%16.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+int router_ksplit(int T, int H, int E)
 {
-    __shared__ double sx[16][64 + 2], sw[16][64 + 2];
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-    const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row lr, k offset lk
-    double acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = 0.0;
-    for (int k0 = 0; k0 < H; k0 += 16) {
-        float4 xv = (t0 + lr < T) ? *reinterpret_cast<const float4 *>(x + (size_t)(t0 + lr) * H + k0 + lk)
-                                  : make_float4(0, 0, 0, 0);
-        float4 wv = (e0 + lr < E) ? *reinterpret_cast<const float4 *>(gate_w + (size_t)(e0 + lr) * H + k0 + lk)
-                                  : make_float4(0, 0, 0, 0);
-        sx[lk][lr] = xv.x; sx[lk + 1][lr] = xv.y; sx[lk + 2][lr] = xv.z; sx[lk + 3][lr] = xv.w;
-        sw[lk][lr] = wv.x; sw[lk + 1][lr] = wv.y; sw[lk + 2][lr] = wv.z; sw[lk + 3][lr] = wv.w;
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 16; kk++) {
-            double a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) { a[i] = sx[kk][ty * 4 + i]; b[i] = sw[kk][tx * 4 + i]; }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) acc[i][j] = fma(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int t = t0 + ty * 4 + i;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int e = e0 + tx * 4 + j;
-            if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j];
-        }
-    }
+    if (T <= kGemvMaxT) return 1;
+    const long tiles = (long)((T + 31) / 32) * ((E + 63) / 64);
+    const int kb = H / 16;
+    int ks = 1;
+    while (ks < 32 && tiles * ks < 2048 && kb % (2 * ks) == 0 && kb / (2 * ks) >= 4) ks *= 2;
+    return ks;
 }
 
-int launch_router_logits_tiled(const float *x, int T, int H, const float *gate_w, int E, double *logits,
-                               hipStream_t st)
+__device__ __forceinline__ float f4c(const float4 &v, int s)
 {
-    dim3 grid((T + 63) / 64, (E + 63) / 64);
-    k_router_logits_tiled<<<grid, 256, 0, st>>>(x, T, H, gate_w, E, logits);
+    return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+}
+
+__global__ __launch_bounds__(256) void k_router_logits_mfma(const float *__restrict__ x, int T, int H,
+                                                            const float *__restrict__ gate_w, int E, int ksplit,
+                                                            double *__restrict__ part)
+{
+    const int l = lane_id();
+    const int wv = blockIdx.x * 4 + wave_id();
+    const int et = (E + 63) / 64, tt = (T + 31) / 32;
+    const int ks = wv % ksplit, te = wv / ksplit;
+    const int ei = te % et, ti = te / et;
+    if (ti >= tt) return;
+    const int t0 = ti * 32, e0 = ei * 64;
+    const int kq = H / ksplit, kbeg = ks * kq;
+    const int r = l & 15, g = l >> 4;
+    const float *pa[2], *pb[4];
+    bool va[2], vb[4];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int t = t0 + 16 * i + r;
+        va[i] = t < T;
+        pa[i] = x + (size_t)(va[i] ? t : 0) * H + kbeg + 4 * g;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int e = e0 + 16 * j + r;
+        vb[j] = e < E;
+        pb[j] = gate_w + (size_t)(vb[j] ? e : 0) * H + kbeg + 4 * g;
+    }
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    v4d acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
+    float4 a[2], b[4];
+#pragma unroll
+    for (int i = 0; i < 2; i++) a[i] = va[i] ? *reinterpret_cast<const float4 *>(pa[i]) : z4;
+#pragma unroll
+    for (int j = 0; j < 4; j++) b[j] = vb[j] ? *reinterpret_cast<const float4 *>(pb[j]) : z4;
+    for (int kk = 0; kk < kq; kk += 16) {
+        // next K block in flight while this one is multiplied
+        float4 an[2], bn[4];
+        const bool more = kk + 16 < kq;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            an[i] = (more && va[i]) ? *reinterpret_cast<const float4 *>(pa[i] + kk + 16) : z4;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            bn[j] = (more && vb[j]) ? *reinterpret_cast<const float4 *>(pb[j] + kk + 16) : z4;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            double da[2], db[4];
+#pragma unroll
+            for (int i = 0; i < 2; i++) da[i] = (double)f4c(a[i], s);
+#pragma unroll
+            for (int j = 0; j < 4; j++) db[j] = (double)f4c(b[j], s);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(da[i], db[j], acc[i][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; i++) a[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < 4; j++) b[j] = bn[j];
+    }
+    double *o = part + (size_t)ks * T * E;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int t = t0 + 16 * i + g + 4 * v, e = e0 + 16 * j + r;
+                if (t < T && e < E) o[(size_t)t * E + e] = acc[i][j][v];
+            }
+}
+
+int launch_router_logits_mfma(const float *x, int T, int H, const float *gate_w, int E, int ksplit, double *part,
+                              hipStream_t st)
+{
+    const long waves = (long)((T + 31) / 32) * ((E + 63) / 64) * ksplit;
+    k_router_logits_mfma<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(x, T, H, gate_w, E, ksplit, part);
     return (int)hipGetLastError();
 }
 
-// one workgroup per token
-__global__ __launch_bounds__(256) void k_topk(const RouteCfg rc, const double *__restrict__ logits,
+// one workgroup per token; the logits are the sum of `nparts` slices
+__global__ __launch_bounds__(256) void k_topk(const RouteCfg rc, const double *__restrict__ logits, int nparts,
                                               const float *__restrict__ bias, int T,
                                               int32_t *__restrict__ idx, float *__restrict__ w)
 {
     __shared__ TopkLds tl;
     const int t = blockIdx.x;
-    block_topk(rc, logits + (size_t)t * rc.E, bias, idx + (size_t)t * rc.k, w + (size_t)t * rc.k, tl);
+    block_topk(rc, logits + (size_t)t * rc.E, (size_t)T * rc.E, nparts, bias, idx + (size_t)t * rc.k,
+               w + (size_t)t * rc.k, tl);
 }
 
-int launch_topk(const RouteCfg &rc, const double *logits, const float *bias, int T, int32_t *idx,
+int launch_topk(const RouteCfg &rc, const double *logits, int nparts, const float *bias, int T, int32_t *idx,
                 float *w, hipStream_t st)
 {
-    k_topk<<<T, 256, 0, st>>>(rc, logits, bias, T, idx, w);
+    k_topk<<<T, 256, 0, st>>>(rc, logits, nparts, bias, T, idx, w);
     return (int)hipGetLastError();
 }
 

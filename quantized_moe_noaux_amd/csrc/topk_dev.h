@@ -42,13 +42,17 @@ struct TopkLds {
 // dependent LDS or cross-lane round trip costs ~100 cycles, so serial
 // chains, not arithmetic, set the latency of this step.  All scores and
 // comparisons are fp64.
-__device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, const float *__restrict__ bias,
-                           int *sel_e, float *sel_w, TopkLds &L)
+//   zt: the token's logits, as the sum of nparts slices pstride apart
+//   (added in slice order)
+__device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, size_t pstride, int nparts,
+                           const float *__restrict__ bias, int *sel_e, float *sel_w, TopkLds &L)
 {
     const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id();
     const int E = rc.E, G = rc.G, m = E / G;
     for (int e = tid; e < E; e += nt) {
-        const double sv = 1.0 / (1.0 + exp(-zt[e]));
+        double z = zt[e];
+        for (int p = 1; p < nparts; p++) z += zt[p * pstride + e];
+        const double sv = 1.0 / (1.0 + exp(-z));
         const double cv = sv + (double)bias[e];
         L.s[e] = sv;
         L.c[e] = cv;

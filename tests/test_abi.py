@@ -52,7 +52,9 @@ def test_workspace_sizes(m):
     ws1 = m.moe_workspace_bytes(sh, 1)
     assert ws1 > 0 and ws1 % 256 == 0
     assert m.moe_workspace_bytes(sh, 3) > ws1
-    assert m.moe_route_workspace_bytes(sh, 2048) == 2048 * 256 * 8
+    # fp64 partial logits of the K-split router (8 slices at this size)
+    assert m.moe_route_workspace_bytes(sh, 2048) == 8 * 2048 * 256 * 8
+    assert m.moe_route_workspace_bytes(sh, 8) == 8 * 256 * 8
     assert m.moe_workspace_bytes(big_shape(m, wbits=3), 1) == 0          # unsupported shape
     assert m.moe_workspace_bytes(big_shape(m, n_group=7), 1) == 0        # E % G != 0
     assert m.moe_permute_workspace_bytes(2048, 8, 256) == 64 * 256 * 4
