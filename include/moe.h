@@ -182,6 +182,31 @@ int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags);
 int moe_rmsnorm(const float *x, const float *g, double eps, int32_t T, int32_t H, float *out,
                 hipStream_t stream);
 
+/* moe_stack_forward -- a decode stack of MoE layers (wpnews.pro spec table:
+ * 75 MoE layers), each on its own weights and re-routed:
+ *   for l in 0 .. n_layers-1:   x = x + MoE_l(RMSNorm_l(x))
+ * RMSNorm as moe_rmsnorm with eps and the layer's norm weight; MoE_l as
+ * moe_layer_forward with the layer's router, correction bias and experts;
+ * the layer result is rounded to fp32 and added to x in fp32.
+ *   x        [T][H] fp32 residual stream, updated in place
+ *   layers   HOST array of n_layers descriptors (device pointers inside)
+ *   idx_out, w_out  [n_layers][T][k] (nullable): every layer's routing
+ *   flags    MOE_PATH_* (MOE_ACCUMULATE is implied; MOE_STAGE not allowed)
+ * ws: at least moe_stack_workspace_bytes(shape, T, flags) bytes, 256-byte
+ *   aligned.  The launches only read the layers array during the call, so a
+ *   stream capture of one call replays with the same device pointers. */
+typedef struct {
+    const float *gate_w;        /* [E][H] router weights */
+    const float *bias;          /* [E] correction bias */
+    const float *norm_g;        /* [H] RMSNorm weight */
+    moe_weights_t routed;       /* stack of E experts */
+    moe_weights_t shared;       /* shared expert (ignored when n_shared = 0) */
+} moe_layer_t;
+int moe_stack_forward(const moe_shape_t *shape, float *x, int32_t T, const moe_layer_t *layers,
+                      int32_t n_layers, double eps, int32_t *idx_out, float *w_out, uint32_t flags,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_stack_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags);
+
 /* ---------------------------------------------------------------- permute */
 /* moe_permute -- the token permutation of the grouped path (batch-union
  * MoE, GeekNews #31297 implemented features), exported for testing.

@@ -322,6 +322,48 @@ int moe_rmsnorm(const float *x, const float *g, double eps, int32_t T, int32_t H
     return hip_rc(launch_rmsnorm(x, g, eps, T, H, out, stream));
 }
 
+size_t moe_stack_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags)
+{
+    const size_t layer = moe_workspace_bytes(shape, T, flags);
+    if (!layer) return 0;
+    return align256(sizeof(float) * (size_t)(T > 0 ? T : 1) * shape->hidden) + layer;
+}
+
+int moe_stack_forward(const moe_shape_t *shape, float *x, int32_t T, const moe_layer_t *layers, int32_t n_layers,
+                      double eps, int32_t *idx_out, float *w_out, uint32_t flags, void *ws, size_t ws_bytes,
+                      hipStream_t stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (T < 0 || n_layers < 0 || !(eps >= 0.0)) return MOE_EINVAL;
+    if (flags & ~3u) return MOE_EINVAL;
+    if ((idx_out == nullptr) != (w_out == nullptr)) return MOE_EINVAL;
+    if (T == 0 || n_layers == 0) return MOE_OK;
+    if (!x || !layers || !ws || !al(ws, 256)) return MOE_EINVAL;
+    for (int l = 0; l < n_layers; l++) {
+        const moe_layer_t &L = layers[l];
+        if (!L.gate_w || !L.bias || !L.norm_g) return MOE_EINVAL;
+        if ((rc = check_weights(&L.routed))) return rc;
+        if (shape->n_shared && (rc = check_weights(&L.shared))) return rc;
+    }
+    const size_t need = moe_stack_workspace_bytes(shape, T, flags);
+    if (!need) return MOE_EUNSUPPORTED;
+    if (ws_bytes < need) return MOE_EWORKSPACE;
+    const size_t nb = align256(sizeof(float) * (size_t)T * shape->hidden);
+    float *n = static_cast<float *>(ws);
+    void *lws = static_cast<char *>(ws) + nb;
+    const size_t tk = (size_t)T * shape->top_k;
+    for (int l = 0; l < n_layers; l++) {
+        const moe_layer_t &L = layers[l];
+        if (launch_rmsnorm(x, L.norm_g, eps, T, shape->hidden, n, stream)) return MOE_EHIP;
+        rc = moe_layer_forward(shape, n, T, L.gate_w, L.bias, &L.routed, shape->n_shared ? &L.shared : nullptr,
+                               x, idx_out ? idx_out + l * tk : nullptr, w_out ? w_out + l * tk : nullptr,
+                               flags | MOE_ACCUMULATE, lws, ws_bytes - nb, stream);
+        if (rc) return rc;
+    }
+    return MOE_OK;
+}
+
 size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E)
 {
     if (T < 0 || k <= 0 || E <= 0) return 0;

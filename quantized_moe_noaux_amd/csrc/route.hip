@@ -158,39 +158,47 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const float *__restr
     for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
-    float4 a[2], b[4];
-#pragma unroll
-    for (int i = 0; i < 2; i++) a[i] = va[i] ? *reinterpret_cast<const float4 *>(pa[i]) : z4;
-#pragma unroll
-    for (int j = 0; j < 4; j++) b[j] = vb[j] ? *reinterpret_cast<const float4 *>(pb[j]) : z4;
-    for (int kk = 0; kk < kq; kk += 16) {
-        // next K block in flight while this one is multiplied
-        float4 an[2], bn[4];
-        const bool more = kk + 16 < kq;
+    // three register sets: the K block being multiplied and the next two in
+    // flight (one wave per SIMD pair: the loads' latency is not hidden by
+    // other waves)
+    float4 a[3][2], b[3][4];
+    auto fetch = [&](int set, int kk) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
-            an[i] = (more && va[i]) ? *reinterpret_cast<const float4 *>(pa[i] + kk + 16) : z4;
+            a[set][i] = (kk < kq && va[i]) ? *reinterpret_cast<const float4 *>(pa[i] + kk) : z4;
 #pragma unroll
         for (int j = 0; j < 4; j++)
-            bn[j] = (more && vb[j]) ? *reinterpret_cast<const float4 *>(pb[j] + kk + 16) : z4;
+            b[set][j] = (kk < kq && vb[j]) ? *reinterpret_cast<const float4 *>(pb[j] + kk) : z4;
+    };
+    auto mul = [&](int set) {
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             double da[2], db[4];
 #pragma unroll
-            for (int i = 0; i < 2; i++) da[i] = (double)f4c(a[i], s);
+            for (int i = 0; i < 2; i++) da[i] = (double)f4c(a[set][i], s);
 #pragma unroll
-            for (int j = 0; j < 4; j++) db[j] = (double)f4c(b[j], s);
+            for (int j = 0; j < 4; j++) db[j] = (double)f4c(b[set][j], s);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int j = 0; j < 4; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(da[i], db[j], acc[i][j], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 2; i++) a[i] = an[i];
-#pragma unroll
-        for (int j = 0; j < 4; j++) b[j] = bn[j];
+    };
+    fetch(0, 0);
+    fetch(1, 16);
+    int kk = 0;
+    // kq is a multiple of 16; unrolled by three so the register sets stay static
+    for (; kk + 48 <= kq; kk += 48) {
+        fetch(2, kk + 32);
+        mul(0);
+        fetch(0, kk + 48);
+        mul(1);
+        fetch(1, kk + 64);
+        mul(2);
     }
+    if (kk < kq) mul(0);
+    if (kk + 16 < kq) mul(1);
     double *o = part + (size_t)ks * T * E;
 #pragma unroll
     for (int i = 0; i < 2; i++)

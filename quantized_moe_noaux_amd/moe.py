@@ -28,6 +28,10 @@ class MoeError(RuntimeError):
         self.code = code
 
 
+class moe_layer_t(ctypes.Structure):
+    pass
+
+
 class moe_shape_t(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
@@ -39,6 +43,10 @@ class moe_shape_t(ctypes.Structure):
 class moe_weights_t(ctypes.Structure):
     _fields_ = [("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+
+
+moe_layer_t._fields_ = [("gate_w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("norm_g", ctypes.c_void_p),
+                        ("routed", moe_weights_t), ("shared", moe_weights_t)]
 
 
 def _load():
@@ -61,6 +69,9 @@ def _load():
         "moe_rmsnorm": (ctypes.c_int, [vp, vp, ctypes.c_double, i32, i32, vp, vp]),
         "moe_permute": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
         "moe_permute_workspace_bytes": (sz, [i32, i32, i32]),
+        "moe_stack_forward": (ctypes.c_int, [P(moe_shape_t), vp, i32, P(moe_layer_t), i32, ctypes.c_double,
+                                             vp, vp, u32, vp, sz, vp]),
+        "moe_stack_workspace_bytes": (sz, [P(moe_shape_t), i32, u32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -184,3 +195,28 @@ def moe_permute(idx, E, perm, off, inv, ws, stream=None):
     _chk("moe_permute", lib.moe_permute(_ptr(idx, torch.int32), T, k, E, _ptr(perm, torch.int32),
                                         _ptr(off, torch.int32), _ptr(inv, torch.int32), _ptr(ws),
                                         ws.numel(), _stream(stream)))
+
+
+def layers(descs):
+    """Host array of moe_layer_t from objects with gate_w, bias, norm_g tensors
+    and routed / shared weight objects (shared may be None)."""
+    arr = (moe_layer_t * len(descs))()
+    for i, d in enumerate(descs):
+        arr[i].gate_w = _ptr(d.gate_w, torch.float32)
+        arr[i].bias = _ptr(d.bias, torch.float32)
+        arr[i].norm_g = _ptr(d.norm_g, torch.float32)
+        arr[i].routed = weights(d.routed)
+        if d.shared is not None:
+            arr[i].shared = weights(d.shared)
+    return arr
+
+
+def moe_stack_workspace_bytes(sh, T, flags=0):
+    return lib.moe_stack_workspace_bytes(ctypes.byref(sh), T, flags)
+
+
+def moe_stack_forward(sh, x, layer_array, eps, ws, idx_out=None, w_out=None, flags=0, stream=None):
+    """x [T][H] fp32 updated in place; layer_array from layers()."""
+    _chk("moe_stack_forward", lib.moe_stack_forward(
+        ctypes.byref(sh), _ptr(x, torch.float32), x.shape[0], layer_array, len(layer_array), eps,
+        _ptr(idx_out, torch.int32), _ptr(w_out, torch.float32), flags, _ptr(ws), ws.numel(), _stream(stream)))

@@ -271,3 +271,29 @@ def device_weights(wl, layer, e0, n_exp, device="cuda", seed=None):
 
     return DeviceWeights(codes(W_GATE, I, H), codes(W_UP, I, H), codes(W_DOWN, H, I),
                          scales(S_GATE, I, H), scales(S_UP, I, H), scales(S_DOWN, H, I))
+
+
+class StackLayer:
+    """One layer of a device-resident decode stack: router weights, correction
+    bias, RMSNorm weight (ones) and expert stacks, all in HBM."""
+
+    def __init__(self, gate_w, bias, norm_g, routed, shared):
+        self.gate_w, self.bias, self.norm_g = gate_w, bias, norm_g
+        self.routed, self.shared = routed, shared
+
+
+def device_stack(wl, device="cuda", layers=None):
+    """Every layer of a stack workload generated in HBM (about 2.4 GB per int2
+    layer of the GLM-5.2 shape), plus the host copies of the router weights
+    (HostLayer per layer, experts regenerated on demand)."""
+    import torch
+    n = wl.layers if layers is None else layers
+    hosts, dev_layers = [], []
+    ones = torch.ones(wl.hidden, dtype=torch.float32, device=device)
+    for l in range(n):
+        h = HostLayer(wl, layer=l)
+        hosts.append(h)
+        dev_layers.append(StackLayer(torch.from_numpy(h.gate_w).to(device), torch.from_numpy(h.bias).to(device),
+                                     ones, device_weights(wl, l, 0, wl.n_experts, device),
+                                     device_weights(wl, l, wl.n_experts, 1, device) if wl.n_shared else None))
+    return hosts, dev_layers
