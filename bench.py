@@ -78,6 +78,14 @@ def path_of(workload):
     return "grouped" if workload == "prefill_int4" else "gemv"
 
 
+def stages_of(workload):
+    if workload == "prefill_int4":
+        return GROUPED_STAGES
+    if workload == "stack_int2":
+        return [("rmsnorm", "k_rmsnorm")] + GEMV_STAGES
+    return GEMV_STAGES
+
+
 def traffic_from_profiles(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources (else None)."""
@@ -122,8 +130,7 @@ def _copy_kib(d, counter):
 
 
 def write_traffic(args):
-    stages = GROUPED_STAGES if args.workload == "prefill_int4" else GEMV_STAGES
-    kernel, match = [s for s in stages if s[0] == args.kernel][0]
+    kernel, match = [s for s in stages_of(args.workload) if s[0] == args.kernel][0]
     res = {"workload": args.workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(path_of(args.workload))}
     total = 0.0
     for counter, kdir, cdir in (("FETCH_SIZE", args.pmc_fetch, args.copy_fetch),
@@ -166,7 +173,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_int4",
-                    choices=["decode_int4", "verify_int8", "prefill_int4"])
+                    choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,6 +203,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = synth.workload(args.workload)
+    if wl.layers > 1:
+        return bench_stack(args, wl)
     T = wl.T
     grouped = wl.name == "prefill_int4"
     n_inputs = 4 if grouped else 64
@@ -349,6 +358,170 @@ def main():
                    "step_us_p10_p50_p90": [float(np.percentile(step_ms, p) * 1e3) for p in (10, 50, 90)],
                    "mean_experts_read": n_exp, "layer_weight_bytes": layer_bytes,
                    "router_weight_bytes": router_bytes, "wall_s_timed_loop_incl_flush": wall},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_stack(args, wl):
+    """One token through the whole decode stack per step (graph replay of one
+    moe_stack_forward call); per-kernel figures from single layers."""
+    import numpy as np
+    import torch
+    import synth
+    from quantized_moe_noaux_amd import moe
+
+    dev = "cuda:0"
+    eps = 1e-6
+    n_inputs = 64
+    steps = args.steps if args.steps is not None else 20
+    warmup = args.warmup if args.warmup is not None else 3
+    sh = moe.shape_of(wl)
+    log("bench: %s, %d layers, H=%d I=%d E=%d k=%d int%d; generating the layers in HBM" %
+        (wl.name, wl.layers, wl.hidden, wl.inter, wl.n_experts, wl.top_k, wl.wbits))
+    hosts, layers = synth.device_stack(wl, dev)
+    arr = moe.layers(layers)
+    ws = moe.workspace(moe.moe_stack_workspace_bytes(sh, 1), dev)
+    xs = torch.stack([torch.from_numpy(synth.host_normals(wl.seed + i, synth.stream_id(0, synth.X), wl.hidden, 1.0)
+                                       .reshape(1, wl.hidden)) for i in range(n_inputs)]).to(dev)
+    x = torch.empty((1, wl.hidden), dtype=torch.float32, device=dev)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def flush():
+        if not args.no_flush:
+            flush_buf.sum()
+
+    # the step: the token's residual stream through every layer, one graph
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        moe.moe_stack_forward(sh, x, arr, eps, ws)
+    torch.cuda.synchronize()
+
+    def step(i):
+        x.copy_(xs[i % n_inputs])
+        graph.replay()
+
+    for i in range(warmup):
+        flush()
+        step(i)
+    torch.cuda.synchronize()
+    log("bench: graph captured, %d warmup steps done" % warmup)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = float(step_ms.mean())
+
+    # per kernel: single layers (layer i % L) on a normalised token, flush-
+    # subtracted as in the layer benchmark; the RMSNorm launch included
+    names = ["rmsnorm"] + [s[0] for s in GEMV_STAGES]
+    n_stages = moe.moe_layer_stage_count(sh, 1)
+    lws = moe.workspace(moe.moe_workspace_bytes(sh, 1), dev)
+    nrm = torch.empty_like(x)
+    y = torch.empty_like(x)
+    reps = 4 * wl.layers
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    sev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_stages + 1)] for _ in range(reps)]
+    for i in range(reps):
+        L = layers[i % wl.layers]
+        fev[i][0].record(stream)
+        flush()
+        fev[i][1].record(stream)
+        sev[i][0][0].record(stream)
+        flush()
+        moe.moe_rmsnorm(xs[i % n_inputs], L.norm_g, eps, nrm)
+        sev[i][0][1].record(stream)
+        for s_ in range(n_stages):
+            sev[i][s_ + 1][0].record(stream)
+            flush()
+            moe.moe_layer_forward(sh, nrm, L.gate_w, L.bias, L.routed, L.shared, y, lws,
+                                  flags=moe.MOE_STAGE(s_))
+            sev[i][s_ + 1][1].record(stream)
+    torch.cuda.synchronize()
+    flush_ms = float(np.mean([a.elapsed_time(b) for a, b in fev]))
+    stage_ms = np.array([[sev[i][s_][0].elapsed_time(sev[i][s_][1]) for s_ in range(n_stages + 1)]
+                         for i in range(reps)]).mean(0) - flush_ms
+    log("bench: per-kernel pass done (flush %.1f us subtracted)" % (flush_ms * 1e3))
+
+    n_exp = wl.top_k + wl.n_shared
+    gate_up_bytes = 2 * (wl.gate_bytes + 4 * wl.inter)
+    down_bytes = wl.down_bytes + 4 * wl.hidden
+    token_bytes = wl.layers * n_exp * (gate_up_bytes + down_bytes)
+    router_bytes = wl.layers * 4 * wl.n_experts * wl.hidden
+    work = [None, ("hbm", 4 * wl.n_experts * wl.hidden / 1e9), None, ("hbm", n_exp * gate_up_bytes / 1e9),
+            ("hbm", n_exp * down_bytes / 1e9)]
+    cand = [j for j in range(len(names)) if work[j]]
+    dom = max(cand, key=lambda j: stage_ms[j])
+    amount = work[dom][1]
+    achieved = amount / (stage_ms[dom] * 1e-3)
+    tok_s = 1.0 / (ms * 1e-3)
+    log("bench: step %.1f us per token (%.2f us per layer), %.1f tok/s, weights %.0f GB/s = %.1f%% of HBM peak" %
+        (ms * 1e3, ms * 1e3 / wl.layers, tok_s, token_bytes / (ms * 1e-3) / 1e9,
+         100 * token_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS))
+    log("bench: per layer (us): %s" % ", ".join("%s %.2f" % (n, v * 1e3) for n, v in zip(names, stage_ms)))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        osh = oracle.shape_of(wl)
+        ones = np.ones(wl.hidden, np.float32)
+        spent, tokens, t_start = 0.0, 0, time.perf_counter()
+        while spent < args.cpu_seconds and time.perf_counter() - t_start < 4 * args.cpu_seconds:
+            xh = xs[tokens % n_inputs].cpu().numpy()
+            for H in hosts:
+                nh = oracle.rmsnorm(xh, ones, eps)
+                ridx, _ = oracle.route(osh, nh, H.gate_w, H.bias)
+                experts = oracle.layer_experts(H, ridx)      # generated outside the timing
+                c0 = time.perf_counter()
+                nh = oracle.rmsnorm(xh, ones, eps)
+                yh, _, _ = oracle.layer_forward(osh, nh, H.gate_w, H.bias, experts, H.shared)
+                xh = (xh + yh).astype(np.float32)
+                spent += time.perf_counter() - c0
+                H._experts = {}
+            tokens += 1
+        cpu = {"value": tokens / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "%d tokens through all %d layers (RMSNorm, layer forward, residual add), expert "
+                         "generation excluded" % (tokens, wl.layers), "seconds": round(spent, 2)}
+        log("bench: oracle %.3f tok/s on %d threads (%d tokens, %.1f s)" % (cpu["value"], cpu["cores"], tokens, spent))
+
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded SplitMix64 weights for %d layers and N(0,1) tokens, %d rotating inputs%s)" %
+                (wl.layers, n_inputs, "" if args.no_flush else ", caches flushed between steps"),
+        "config": {"workload": wl.name, "T": 1, "layers": wl.layers, "hidden": wl.hidden, "inter": wl.inter,
+                   "n_experts": wl.n_experts, "n_group": wl.n_group, "topk_group": wl.topk_group,
+                   "top_k": wl.top_k, "n_shared": wl.n_shared, "wbits": wl.wbits, "rsf": wl.rsf,
+                   "path": "gemv", "graph": True},
+        "effective_weight_GBps": token_bytes / (ms * 1e-3) / 1e9,
+        "effective_weight_frac": token_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(wl.name, names[dom]),
+                     "algorithmic_per_launch": amount, "avg_launch_us": float(stage_ms[dom] * 1e3)},
+        "detail": {"per_layer_us": {n: float(v * 1e3) for n, v in zip(names, stage_ms)},
+                   "step_us_p10_p50_p90": [float(np.percentile(step_ms, p) * 1e3) for p in (10, 50, 90)],
+                   "token_weight_bytes": token_bytes, "router_weight_bytes": router_bytes,
+                   "wall_s_timed_loop_incl_flush": wall},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -29,7 +29,8 @@ struct TopkLds {
     double gs[kMaxGroups];       // group scores
     int kept[kMaxGroups];        // kept groups, ascending
     int nkept;
-    int rank[kMaxExperts];       // rank of each candidate among the kept
+    uint64_t ckey[kMaxExperts];  // keys of the kept candidates, in expert order
+    int crank[2][kMaxExperts];   // partial ranks of the kept candidates
     int sel_e[kMaxTopK];
     double sel_s[kMaxTopK];
 };
@@ -37,7 +38,8 @@ struct TopkLds {
 // Block-wide noaux_tc routing of one token (every thread of the block calls
 // it; blockDim.x >= 64).  The selection is a parallel rank count:
 //   rank(e) = #{kept candidates e' with c' > c, or c' == c and e' < e}
-// and e is selected at position rank(e) when that is below k.  Every phase
+// and e is selected at position rank(e) when that is below k (key 0 = a
+// padding entry never outranks a real one: real keys are above 0).  Every phase
 // spreads its work over many lanes with independent loads: on MI355X a
 // dependent LDS or cross-lane round trip costs ~100 cycles, so serial
 // chains, not arithmetic, set the latency of this step.  All scores and
@@ -57,7 +59,6 @@ __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, siz
         L.s[e] = sv;
         L.c[e] = cv;
         L.key[e] = order_key(cv);
-        L.rank[e] = 0;
     }
     __syncthreads();
     if (tid < 64) {
@@ -97,29 +98,37 @@ __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, siz
         if (lane == 0) L.nkept = __popcll(kb);
     }
     __syncthreads();
-    // rank counting: one item = (candidate, kept group scanned)
+    // Candidates = the experts of the kept groups; kept groups ascend, so
+    // candidate order is expert order and a tie goes to the lower position.
+    // rank(ci) = #{j : key_j > key_ci, or key_j == key_ci and j < ci}, counted
+    // by two threads per candidate over halves of j (broadcast LDS reads, no
+    // atomics) and summed in a fixed order.
     const int nk = L.nkept, ncand = nk * m;
-    for (int it = tid; it < ncand * nk; it += nt) {
-        const int ci = it % ncand, gi = it / ncand;
-        const int e = L.kept[ci / m] * m + (ci % m);
-        const uint64_t ke = L.key[e];
-        const int base = L.kept[gi] * m;
+    for (int ci = tid; ci < ncand; ci += nt) L.ckey[ci] = L.key[L.kept[ci / m] * m + ci % m];
+    __syncthreads();
+    const int split = (2 * ncand <= nt) ? 2 : 1, half = ncand / split;
+    for (int item = tid; item < ncand * split; item += nt) {
+        const int ci = item % ncand, part = item / ncand;
+        const int j0 = part * half, j1 = (part + 1 == split) ? ncand : j0 + half;
+        const uint64_t ke = L.ckey[ci];
         int cnt = 0;
-        for (int j0 = 0; j0 < m; j0 += 8) {
+        for (int j = j0; j < j1; j += 8) {
             uint64_t kj[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) kj[j] = (j0 + j < m) ? L.key[base + j0 + j] : 0ull;
+            for (int u = 0; u < 8; u++) kj[u] = (j + u < j1) ? L.ckey[j + u] : 0ull;
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                cnt += (kj[j] > ke) || (kj[j] == ke && base + j0 + j < e && j0 + j < m);
+            for (int u = 0; u < 8; u++) cnt += (kj[u] > ke) || (kj[u] == ke && j + u < ci);
         }
-        if (cnt) atomicAdd(&L.rank[e], cnt);
+        L.crank[part][ci] = cnt;
     }
     __syncthreads();
     for (int ci = tid; ci < ncand; ci += nt) {
-        const int e = L.kept[ci / m] * m + (ci % m);
-        const int r = L.rank[e];
-        if (r < rc.k) { L.sel_e[r] = e; L.sel_s[r] = L.s[e]; }
+        const int r = L.crank[0][ci] + (split == 2 ? L.crank[1][ci] : 0);
+        if (r < rc.k) {
+            const int e = L.kept[ci / m] * m + ci % m;
+            L.sel_e[r] = e;
+            L.sel_s[r] = L.s[e];
+        }
     }
     __syncthreads();
     if (tid < rc.k) {
