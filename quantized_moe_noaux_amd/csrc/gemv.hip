@@ -452,34 +452,41 @@ __global__ __launch_bounds__(256) void k_down_rg(const GemvArgs a, const ChunkCf
 // Reduce-scatter of N partials (N a power of two <= 32) over a 32-lane
 // group: afterwards lane l of the group holds, for slot j = (l % 32) / (32/N),
 // the sum of v[j] over the 32 lanes (valid where (l % 32) % (32/N) == 0).
+// One level of the reduce-scatter: lanes exchange the half of their NA live
+// values they do not keep with the lane O apart and add the received half.
+// NA and O are compile-time, so every register index is static (a runtime
+// width would turn v[j + NA/2] into compare/select ladders).
+template <int N, int O, int NA>
+__device__ __forceinline__ void reduce_scatter_level(float (&v)[N], int lane)
+{
+    if constexpr (NA > 1) {
+        constexpr int HALF = NA / 2;
+        const bool upper = (lane & O) != 0;
+#pragma unroll
+        for (int j = 0; j < HALF; j++) {
+            const float send = upper ? v[j] : v[j + HALF];
+            const float keep = upper ? v[j + HALF] : v[j];
+            v[j] = keep + __shfl_xor(send, O);
+        }
+    } else {
+        v[0] += __shfl_xor(v[0], O);
+    }
+    if constexpr (O > 1) reduce_scatter_level<N, O / 2, (NA > 1 ? NA / 2 : 1)>(v, lane);
+}
+
+// Sum of N values over the 32 lanes of a half-wave, scattered: lane l ends
+// with the total of value j = l / (32 / N) (fixed pairing and order, so the
+// result is run-to-run identical).
 template <int N>
 __device__ __forceinline__ float group32_reduce_scatter(float (&v)[N])
 {
-    const int lane = lane_id();
-    int n = N;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-        if (n > 1) {
-            const bool upper = (lane & o) != 0;
-#pragma unroll
-            for (int j = 0; j < N / 2; j++) {
-                if (j < n / 2) {
-                    const float send = upper ? v[j] : v[j + n / 2];
-                    const float keep = upper ? v[j + n / 2] : v[j];
-                    v[j] = keep + __shfl_xor(send, o);
-                }
-            }
-            n >>= 1;
-        } else {
-            v[0] += __shfl_xor(v[0], o);
-        }
-    }
+    reduce_scatter_level<N, 16, N>(v, lane_id());
     return v[0];
 }
 
 constexpr int kSwThreads = 192;  // gate/up row-sweep block
 constexpr int kSwGroups = kSwThreads / 32;
-constexpr int kSwDepth = 12;     // steps of prefetch in flight
+constexpr int kSwDepth = 11;     // steps of prefetch in flight (<= 168 VGPRs: 3 waves per SIMD)
 
 // gate/up of one 32-row tile of one expert for the n_u tokens of a slot: a
 // step reads RPS rows of gate and of up (kSwThreads * CPT chunks each,
@@ -503,15 +510,9 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
     const uint8_t *gb = W.gate + ((size_t)ee * a.I + row0) * rowbytes + (size_t)tid * 16;
     const uint8_t *ub = W.up + ((size_t)ee * a.I + row0) * rowbytes + (size_t)tid * 16;
     const size_t step_bytes = (size_t)kSwThreads * CPT * 16;
-    uint4 bg[PF][CPT], bu[PF][CPT];
-#pragma unroll
-    for (int s = 0; s < PF; s++)
-#pragma unroll
-        for (int k = 0; k < CPT; k++) {
-            bg[s][k] = ld16(gb + s * step_bytes + (size_t)k * kSwThreads * 16);
-            bu[s][k] = ld16(ub + s * step_bytes + (size_t)k * kSwThreads * 16);
-        }
-
+    // Activation loads first, then PF steps of weight rows: the vector memory
+    // counter retires loads in issue order, so the first dot then waits for
+    // the activations only, not for the whole prefetch.
     Act<WB> act[TT][CPT];
 #pragma unroll
     for (int tt = 0; tt < TT; tt++) {
@@ -520,10 +521,23 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
 #pragma unroll
             for (int k = 0; k < CPT; k++) {
                 const int pos = (tid + kSwThreads * k) % cpr;
-                act[tt][k].load(a.xq + (size_t)t * H, a.xd + (size_t)t * nb, pos);
+                act[tt][k].load_raw(a.xq + (size_t)t * H, a.xd + (size_t)t * nb, pos);
             }
         }
     }
+    uint4 bg[PF][CPT], bu[PF][CPT];
+#pragma unroll
+    for (int s = 0; s < PF; s++)
+#pragma unroll
+        for (int k = 0; k < CPT; k++) {
+            bg[s][k] = ld16(gb + s * step_bytes + (size_t)k * kSwThreads * 16);
+            bu[s][k] = ld16(ub + s * step_bytes + (size_t)k * kSwThreads * 16);
+        }
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++)
+        if (tt < n_u)
+#pragma unroll
+            for (int k = 0; k < CPT; k++) act[tt][k].finish();
     float accg[TT][PS], accu[TT][PS];
 #pragma unroll
     for (int s = 0; s < NSTEP; s++) {
@@ -551,6 +565,10 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
                 bu[slot][k] = ld16(ub + (s + PF) * step_bytes + (size_t)k * kSwThreads * 16);
             }
         }
+        // keep one step's loads and dots together: without this the
+        // scheduler gathers the unrolled steps' loads into bursts and lets the
+        // number in flight drain between them
+        __builtin_amdgcn_sched_barrier(0);
         if (j == PS - 1) {
             const int pass = s / PS;
             const int l32 = lane & 31;
@@ -605,9 +623,12 @@ __global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, con
     __shared__ float part[2][TT][kSwGroups][32];
     const int tiles = a.I / 32;
     const int u = blockIdx.x / tiles, row0 = (blockIdx.x % tiles) * 32;
+    // the slot count and the slot's entries in one round trip (u < pd.S, so
+    // every entry read lies inside the plan; a stale entry of an unused slot
+    // is discarded by the checks below)
     const int S = a.plan[0];
-    if (S > pd.S || u >= S) return;
     const int e = a.plan[pd.o_e + u], n_u = a.plan[pd.o_n + u], p0 = a.plan[pd.o_p0 + u];
+    if (S > pd.S || u >= S) return;
     if (e < -1 || e >= a.E || n_u < 1 || n_u > a.T || p0 < 0 || p0 + n_u > pd.P) return;
     gate_up_tile_sw<WB, CPT, RPS, TT>(a, (e >= 0) ? a.routed : a.shared, (e >= 0) ? e : 0, row0, n_u,
                                       a.plan + pd.o_t + p0, p0, s_h, part);
@@ -639,13 +660,6 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     __syncthreads();
     if (!plan_ok(plan, pd, a.T, a.E)) return;
     const int S = plan[0];
-    int npairs = 0;
-    for (int u = 0; u < S; u++) npairs += plan[pd.o_n + u];
-    for (int c = tid; c < npairs * cpr; c += kDsThreads) {
-        const int p = c / cpr, pos = c - p * cpr;
-        stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pos, la_of(p), ld_of(p), lq_of(p));
-    }
-    __syncthreads();
 
     const int rowoff = tid / cpr, pos = tid % cpr, grp = tid >> 5;
     const int row_base = blockIdx.x * kDsRows;
@@ -695,9 +709,20 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
             }                                                                     \
         }                                                                         \
     }
-    // three buffers in rotation: two slots of rows in flight ahead of use
+    // three buffers in rotation: two slots of rows in flight ahead of use.
+    // The first two slots' rows are requested before the activations are
+    // staged, so the weight stream starts one plan round trip into the kernel.
     MOE_DS_LOAD(0, w0, s0)
     if (1 < S) MOE_DS_LOAD(1, w1, s1)
+    {
+        int npairs = 0;
+        for (int u = 0; u < S; u++) npairs += plan[pd.o_n + u];
+        for (int c = tid; c < npairs * cpr; c += kDsThreads) {
+            const int p = c / cpr, pp = c - p * cpr;
+            stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pp, la_of(p), ld_of(p), lq_of(p));
+        }
+        __syncthreads();
+    }
     for (int u = 0; u < S; u += 3) {
         if (u + 2 < S) MOE_DS_LOAD(u + 2, w2, s2)
         MOE_DS_USE(u, w0, s0)

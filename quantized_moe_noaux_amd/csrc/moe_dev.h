@@ -77,12 +77,17 @@ template <> struct Act<8> {
         a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
         d = dblk[chunk >> 1];
     }
+    // two-phase load: issue the loads now, derive the operand later (so that
+    // loads issued in between stay in flight)
+    __device__ __forceinline__ void load_raw(const int8_t *q, const float *dblk, int chunk) { load(q, dblk, chunk); }
+    __device__ __forceinline__ void finish() {}
+    // two independent partial sums (exact integer arithmetic: the grouping
+    // does not change the result, and short chains keep the issue going)
     __device__ __forceinline__ int isum(const uint4 &w) const
     {
-        int acc = sdot4(w.x, a[0], 0);
-        acc = sdot4(w.y, a[1], acc);
-        acc = sdot4(w.z, a[2], acc);
-        return sdot4(w.w, a[3], acc);
+        const int s0 = sdot4(w.y, a[1], sdot4(w.x, a[0], 0));
+        const int s1 = sdot4(w.w, a[3], sdot4(w.z, a[2], 0));
+        return s0 + s1;
     }
     __device__ __forceinline__ float dot(const uint4 &w) const { return d * (float)isum(w); }
 };
@@ -105,25 +110,39 @@ template <> struct Act<4> {
     }
     __device__ __forceinline__ void load(const int8_t *q, const float *dblk, int chunk)
     {
-        const uint4 *p = reinterpret_cast<const uint4 *>(q + 32 * chunk);
-        uint4 v0 = p[0], v1 = p[1];
-        uint32_t n[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        int qs = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) qs = sdot4(n[i], 0x01010101u, qs);  // block sum of q
-        set(n, dblk[chunk], qs);
+        load_raw(q, dblk, chunk);
+        finish();
     }
+    __device__ __forceinline__ void load_raw(const int8_t *q, const float *dblk, int chunk)
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(q + 32 * chunk);
+        const uint4 v0 = p[0], v1 = p[1];
+        a[0] = v0.x; a[1] = v0.y; a[2] = v0.z; a[3] = v0.w;
+        a[4] = v1.x; a[5] = v1.y; a[6] = v1.z; a[7] = v1.w;
+        d = dblk[chunk];
+    }
+    __device__ __forceinline__ void finish()
+    {
+        uint32_t n[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) n[i] = a[i];
+        int q = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) q = sdot4(n[i], 0x01010101u, q);  // block sum of q
+        set(n, d, q);
+    }
+    // four independent partial sums of two v_dot4 each (exact integers, so
+    // the grouping does not change the block sum)
     __device__ __forceinline__ int isum(const uint4 &w) const
     {
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-        int acc = 0;
+        int acc[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            uint32_t t = ww[k] ^ 0x88888888u;
-            acc = sdot4(t & 0x0F0F0F0Fu, a[2 * k], acc);
-            acc = sdot4((t >> 4) & 0x0F0F0F0Fu, a[2 * k + 1], acc);
+            const uint32_t t = ww[k] ^ 0x88888888u;
+            acc[k] = sdot4((t >> 4) & 0x0F0F0F0Fu, a[2 * k + 1], sdot4(t & 0x0F0F0F0Fu, a[2 * k], 0));
         }
-        return acc - 8 * qs;
+        return ((acc[0] + acc[1]) + (acc[2] + acc[3])) - 8 * qs;
     }
     __device__ __forceinline__ float dot(const uint4 &w) const { return d * (float)isum(w); }
 };
@@ -151,28 +170,40 @@ template <> struct Act<2> {
     }
     __device__ __forceinline__ void load(const int8_t *q, const float *dblk, int chunk)
     {
+        load_raw(q, dblk, chunk);
+        finish();
+    }
+    __device__ __forceinline__ void load_raw(const int8_t *q, const float *dblk, int chunk)
+    {
         const uint4 *p = reinterpret_cast<const uint4 *>(q + 64 * chunk);
-        uint32_t n[16];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            uint4 v = p[i];
-            n[4 * i] = v.x; n[4 * i + 1] = v.y; n[4 * i + 2] = v.z; n[4 * i + 3] = v.w;
+            const uint4 v = p[i];
+            a[4 * i] = v.x; a[4 * i + 1] = v.y; a[4 * i + 2] = v.z; a[4 * i + 3] = v.w;
         }
-        int qs0 = 0, qs1 = 0;
+        d0 = dblk[2 * chunk];
+        d1 = dblk[2 * chunk + 1];
+    }
+    __device__ __forceinline__ void finish()
+    {
+        uint32_t n[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) n[i] = a[i];
+        int q0 = 0, q1 = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            qs0 = sdot4(n[i], 0x01010101u, qs0);
-            qs1 = sdot4(n[8 + i], 0x01010101u, qs1);
+            q0 = sdot4(n[i], 0x01010101u, q0);
+            q1 = sdot4(n[8 + i], 0x01010101u, q1);
         }
-        set(n, dblk[2 * chunk], dblk[2 * chunk + 1], qs0, qs1);
+        set(n, d0, d1, q0, q1);
     }
     __device__ __forceinline__ int part(uint32_t w, int k) const
     {
-        uint32_t t = w ^ 0xAAAAAAAAu;
-        int acc = sdot4(t & 0x03030303u, a[4 * k], 0);
-        acc = sdot4((t >> 2) & 0x03030303u, a[4 * k + 1], acc);
-        acc = sdot4((t >> 4) & 0x03030303u, a[4 * k + 2], acc);
-        return sdot4((t >> 6) & 0x03030303u, a[4 * k + 3], acc);
+        // two chains of two v_dot4 (exact integers)
+        const uint32_t t = w ^ 0xAAAAAAAAu;
+        const int s0 = sdot4((t >> 2) & 0x03030303u, a[4 * k + 1], sdot4(t & 0x03030303u, a[4 * k], 0));
+        const int s1 = sdot4((t >> 6) & 0x03030303u, a[4 * k + 3], sdot4((t >> 4) & 0x03030303u, a[4 * k + 2], 0));
+        return s0 + s1;
     }
     __device__ __forceinline__ void isum2(const uint4 &w, int &i0, int &i1) const
     {
