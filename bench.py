@@ -124,8 +124,9 @@ def _per_dispatch(rows, counter, match=None):
 
 def _copy_kib(d, counter):
     per = _per_dispatch(_counter_rows(d), counter)
-    # the copy is the kernel with the most bytes per dispatch
-    name, vals = max(per.items(), key=lambda kv: sum(kv[1]) / len(kv[1]))
+    # the copy kernel (by name), else the kernel with the most bytes per dispatch
+    named = {k: v for k, v in per.items() if "copy" in k.lower()}
+    name, vals = max((named or per).items(), key=lambda kv: sum(kv[1]) / len(kv[1]))
     return name, sum(vals) / len(vals)
 
 
