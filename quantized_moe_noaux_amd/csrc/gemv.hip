@@ -87,6 +87,30 @@ __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int
         __syncthreads();
         return;
     }
+    if (T == 1) {
+        // one token: slots are its k experts in ascending order, then the
+        // shared expert; the pair of a slot is the slot itself
+        block_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias, s_idx, s_w, *tl);
+        if (tid < k) {
+            const int e = s_idx[tid];
+            int slot = 0;
+            for (int j = 0; j < k; j++) slot += (s_idx[j] < e);
+            slot_e[slot] = e;
+            slot_n[slot] = 1;
+            slot_p0[slot] = slot;
+            pair_t[slot] = 0;
+            pair_w[slot] = s_w[tid];
+        }
+        if (tid == 0) {
+            plan[0] = k + a.n_shared;
+            if (a.n_shared) {
+                slot_e[k] = -1; slot_n[k] = 1; slot_p0[k] = k;
+                pair_t[k] = 0; pair_w[k] = 1.0f;
+            }
+        }
+        __syncthreads();
+        return;
+    }
     for (int i = tid; i < T * 16; i += nt) tokbits[i >> 4][i & 15] = 0u;
     for (int t = 0; t < T; t++)
         block_topk(a.rc, a.logits + (size_t)t * a.E, a.lstride, a.lparts, a.bias, s_idx + t * k, s_w + t * k, *tl);
