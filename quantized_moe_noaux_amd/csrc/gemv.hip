@@ -228,10 +228,10 @@ __device__ __forceinline__ void act_from_lds(Act<WB> &A, const uint32_t *la, con
     if constexpr (WB == 8) {
         A.d = ld[pos >> 1];
     } else if constexpr (WB == 4) {
-        A.d = ld[pos];
+        A.set_scale(ld[pos]);
         A.qs = lq[pos];
     } else {
-        A.d0 = ld[2 * pos]; A.d1 = ld[2 * pos + 1];
+        A.set_scale(ld[2 * pos], ld[2 * pos + 1]);
         A.qs0 = lq[2 * pos]; A.qs1 = lq[2 * pos + 1];
     }
 }

@@ -104,11 +104,8 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t *__restrict__ 
         const uint4 *p = reinterpret_cast<const uint4 *>(qt + 32 * c);
         const uint4 v0 = p[0], v1 = p[1];
         uint32_t nn[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        int qs = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) qs = sdot4(nn[i], 0x01010101u, qs);
         Act<4> A;
-        A.set(nn, 0.f, qs);
+        A.set(nn, 0.f);
         o[c] = A.isum(w);
     } else {
         const uint4 *p = reinterpret_cast<const uint4 *>(qt + 64 * c);

@@ -3,16 +3,18 @@
 // Integer dots.  A weight row is consumed in 16-byte "chunks" (one
 // global_load_dwordx4 per lane).  A chunk holds 128/wbits codes: 16 int8
 // codes (half an activation block), 32 int4 codes (one block) or 64 int2
-// codes (two blocks).  Packed codes are turned into non-negative bytes by an
-// XOR that maps two's complement c to c + 2^(b-1) (0..15 for int4, 0..3 for
-// int2) and multiplied against the int8 activations with v_dot4_i32_i8; the
-// offset is removed with the activation block sum:
-//     sum c*q = sum (c + 2^(b-1))*q - 2^(b-1) * sum q.
+// codes (two blocks).  A packed code is masked in place into the top bits
+// of its byte, where the byte reads as the signed value c * 2^(8-b) (16c for
+// int4, 64c for int2: two's complement codes keep their sign there), and
+// multiplied against the int8 activations with v_dot4_i32_i8:
+//     sum (2^(8-b) c) q = 2^(8-b) * sum c q       (exact in int32).
 // The activation bytes are pre-permuted once (v_perm_b32) so that each
-// masked nibble / 2-bit field lines up with its activation byte.  Every
-// block sum is exact in int32, as the integer-dot formulation requires
-// (GeekNews #31297, implemented features: Q8_0-style int8 activations,
-// integer-dot kernels, packed int4 / int2 weights with per-row scales).
+// masked nibble / 2-bit field lines up with its activation byte, and the
+// power of two is folded into the activation block scale, so d * I comes
+// out with the same rounding as without it.  Every block sum is exact in
+// int32, as the integer-dot formulation requires (GeekNews #31297,
+// implemented features: Q8_0-style int8 activations, integer-dot kernels,
+// packed int4 / int2 weights with per-row scales).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -96,17 +98,26 @@ template <> struct Act<8> {
 // codes meet activation bytes {0,2,4,6} and the odd codes {1,3,5,7}.
 template <> struct Act<4> {
     uint32_t a[8];
-    float d;
-    int qs;
-    __device__ __forceinline__ void set(const uint32_t *n, float d_, int qs_)
+    float d;    // the block's scale
+    float d16;  // d / 16: the dot below is 16 * (block sum)
+    int qs;     // 128 * (sum of the activation codes met by low nibbles)
+    // n: the block's 32 activation codes in natural order
+    __device__ __forceinline__ void set(const uint32_t *n, float d_)
     {
+        int lo = 0;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             a[2 * k] = perm(n[2 * k + 1], n[2 * k], 0x06040200u);
             a[2 * k + 1] = perm(n[2 * k + 1], n[2 * k], 0x07050301u);
+            lo = sdot4(a[2 * k], 0x01010101u, lo);
         }
+        qs = 128 * lo;
+        set_scale(d_);
+    }
+    __device__ __forceinline__ void set_scale(float d_)
+    {
         d = d_;
-        qs = qs_;
+        d16 = d_ * 0.0625f;
     }
     __device__ __forceinline__ void load(const int8_t *q, const float *dblk, int chunk)
     {
@@ -126,25 +137,26 @@ template <> struct Act<4> {
         uint32_t n[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) n[i] = a[i];
-        int q = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) q = sdot4(n[i], 0x01010101u, q);  // block sum of q
-        set(n, d, q);
+        set(n, d);
     }
-    // four independent partial sums of two v_dot4 each (exact integers, so
-    // the grouping does not change the block sum)
-    __device__ __forceinline__ int isum(const uint4 &w) const
+    // 16 * (block sum), in two chains of v_dot4: the high nibbles masked in
+    // place (the byte reads 16c), the low nibbles in offset form c + 8 (one
+    // AND-XOR), whose offset 8 * sum(q) is removed with the precomputed qs:
+    //     16 I = sum 16 c_hi q + 16 * (sum (c_lo + 8) q - 8 sum q_lo)
+    __device__ __forceinline__ int isum16(const uint4 &w) const
     {
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-        int acc[4];
+        int lo = 0, hi = 0;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            const uint32_t t = ww[k] ^ 0x88888888u;
-            acc[k] = sdot4((t >> 4) & 0x0F0F0F0Fu, a[2 * k + 1], sdot4(t & 0x0F0F0F0Fu, a[2 * k], 0));
+            lo = sdot4((ww[k] & 0x0F0F0F0Fu) ^ 0x08080808u, a[2 * k], lo);
+            hi = sdot4(ww[k] & 0xF0F0F0F0u, a[2 * k + 1], hi);
         }
-        return ((acc[0] + acc[1]) + (acc[2] + acc[3])) - 8 * qs;
+        return hi + 16 * lo - qs;
     }
-    __device__ __forceinline__ float dot(const uint4 &w) const { return d * (float)isum(w); }
+    __device__ __forceinline__ int isum(const uint4 &w) const { return isum16(w) >> 4; }  // exact: a multiple of 16
+    // d * I: (d / 16) * (16 I), both factors exact powers-of-two rescalings
+    __device__ __forceinline__ float dot(const uint4 &w) const { return d16 * (float)isum16(w); }
 };
 
 // int2 weights: 64 codes = two blocks.  Weight dword k holds codes
@@ -152,8 +164,14 @@ template <> struct Act<4> {
 // activation bytes {i, 4+i, 8+i, 12+i} (a 4x4 byte transpose).
 template <> struct Act<2> {
     uint32_t a[16];
-    float d0, d1;
-    int qs0, qs1;
+    float d0, d1;      // the two blocks' scales
+    float d0s, d1s;    // d / 64: the masked fields carry a factor 64
+    int qs0, qs1;      // block sums of the activation codes (kept for the staging layout)
+    __device__ __forceinline__ void set_scale(float d0_, float d1_)
+    {
+        d0 = d0_; d1 = d1_;
+        d0s = d0_ * 0.015625f; d1s = d1_ * 0.015625f;
+    }
     __device__ __forceinline__ void set(const uint32_t *n, float d0_, float d1_, int qs0_, int qs1_)
     {
 #pragma unroll
@@ -166,7 +184,8 @@ template <> struct Act<2> {
             a[4 * k + 2] = perm(hi23, hi01, 0x05040100u);
             a[4 * k + 3] = perm(hi23, hi01, 0x07060302u);
         }
-        d0 = d0_; d1 = d1_; qs0 = qs0_; qs1 = qs1_;
+        set_scale(d0_, d1_);
+        qs0 = qs0_; qs1 = qs1_;
     }
     __device__ __forceinline__ void load(const int8_t *q, const float *dblk, int chunk)
     {
@@ -197,24 +216,30 @@ template <> struct Act<2> {
         }
         set(n, d0, d1, q0, q1);
     }
-    __device__ __forceinline__ int part(uint32_t w, int k) const
+    // 64 * (sum over one weight dword's 16 codes): field i of every byte
+    // shifted up into the top two bits; two chains of two v_dot4
+    __device__ __forceinline__ int part64(uint32_t w, int k) const
     {
-        // two chains of two v_dot4 (exact integers)
-        const uint32_t t = w ^ 0xAAAAAAAAu;
-        const int s0 = sdot4((t >> 2) & 0x03030303u, a[4 * k + 1], sdot4(t & 0x03030303u, a[4 * k], 0));
-        const int s1 = sdot4((t >> 6) & 0x03030303u, a[4 * k + 3], sdot4((t >> 4) & 0x03030303u, a[4 * k + 2], 0));
+        const int s0 = sdot4((w << 4) & 0xC0C0C0C0u, a[4 * k + 1], sdot4((w << 6) & 0xC0C0C0C0u, a[4 * k], 0));
+        const int s1 = sdot4(w & 0xC0C0C0C0u, a[4 * k + 3], sdot4((w << 2) & 0xC0C0C0C0u, a[4 * k + 2], 0));
         return s0 + s1;
+    }
+    __device__ __forceinline__ void isum2_64(const uint4 &w, int &i0, int &i1) const
+    {
+        i0 = part64(w.x, 0) + part64(w.y, 1);
+        i1 = part64(w.z, 2) + part64(w.w, 3);
     }
     __device__ __forceinline__ void isum2(const uint4 &w, int &i0, int &i1) const
     {
-        i0 = part(w.x, 0) + part(w.y, 1) - 2 * qs0;
-        i1 = part(w.z, 2) + part(w.w, 3) - 2 * qs1;
+        isum2_64(w, i0, i1);
+        i0 >>= 6;  // exact: multiples of 64
+        i1 >>= 6;
     }
     __device__ __forceinline__ float dot(const uint4 &w) const
     {
         int i0, i1;
-        isum2(w, i0, i1);
-        return d0 * (float)i0 + d1 * (float)i1;
+        isum2_64(w, i0, i1);
+        return d0s * (float)i0 + d1s * (float)i1;
     }
 };
 
