@@ -50,6 +50,12 @@ COPY_BYTES = 1 << 30
 # a rocprofv3 trace
 GEMV_STAGES = [("router+quant", "k_router_logits_small"), ("plan", "k_plan"),
                ("gate_up_swiglu_quant", "k_gate_up"), ("down_combine", "k_down")]
+
+
+def gemv_stages(n_stages):
+    """The GEMV path's stages of one call: a one-token call of the production
+    row widths routes inside its gate/up launch and has no plan launch."""
+    return GEMV_STAGES if n_stages == len(GEMV_STAGES) else [s for s in GEMV_STAGES if s[0] != "plan"]
 GROUPED_STAGES = [("router_logits_fp64", "k_router_logits_mfma"), ("topk", "k_topk"),
                   ("quant_x", "k_gg_quant"), ("permute", "k_perm_"),
                   ("gate_up_swiglu_quant", "k_gg_gate_up"), ("down", "k_gg_down"),
@@ -82,8 +88,13 @@ def stages_of(workload):
     if workload == "prefill_int4":
         return GROUPED_STAGES
     if workload == "stack_int2":
-        return [("rmsnorm", "k_rmsnorm")] + GEMV_STAGES
+        return stack_stages(GEMV_STAGES)
     return GEMV_STAGES
+
+
+def stack_stages(stages):
+    """In the stack the router launch also forms the layer's RMSNorm."""
+    return [("rmsnorm+router+quant", m) if n == "router+quant" else (n, m) for n, m in stages]
 
 
 def traffic_from_profiles(workload, kernel):
@@ -212,8 +223,9 @@ def main():
     steps = args.steps if args.steps is not None else (50 if grouped else 200)
     warmup = args.warmup if args.warmup is not None else (5 if grouped else 20)
     flags = moe.MOE_PATH_GROUPED if grouped else moe.MOE_PATH_GEMV
-    stages = GROUPED_STAGES if grouped else GEMV_STAGES
     sh = moe.shape_of(wl)
+    n_stages = moe.moe_layer_stage_count(sh, T, flags)
+    stages = GROUPED_STAGES if grouped else gemv_stages(n_stages)
     log("bench: %s T=%d H=%d I=%d E=%d k=%d int%d (%s path)" %
         (wl.name, T, wl.hidden, wl.inter, wl.n_experts, wl.top_k, wl.wbits, "grouped" if grouped else "GEMV"))
 
@@ -232,7 +244,6 @@ def main():
     ws = moe.workspace(moe.moe_workspace_bytes(sh, T, flags), dev)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read to flush
     stream = torch.cuda.current_stream()
-    n_stages = moe.moe_layer_stage_count(sh, T, flags)
     assert n_stages == len(stages), (n_stages, len(stages))
     torch.cuda.synchronize()
 
@@ -313,9 +324,10 @@ def main():
                 ("mfma", 2.0 * rows * wl.hidden * wl.inter / 1e12, MFMA_I8_PEAK_TOPS, "TOP/s"),
                 ("hbm", (rows + T) * wl.hidden * 4 / 1e9, HBM_PEAK_GBS, "GB/s")]
     else:
-        work = [("hbm", router_bytes / 1e9, HBM_PEAK_GBS, "GB/s"), None,
-                ("hbm", n_exp * gate_up_bytes / 1e9, HBM_PEAK_GBS, "GB/s"),
-                ("hbm", n_exp * down_bytes / 1e9, HBM_PEAK_GBS, "GB/s")]
+        by_name = {"router+quant": ("hbm", router_bytes / 1e9, HBM_PEAK_GBS, "GB/s"),
+                   "gate_up_swiglu_quant": ("hbm", n_exp * gate_up_bytes / 1e9, HBM_PEAK_GBS, "GB/s"),
+                   "down_combine": ("hbm", n_exp * down_bytes / 1e9, HBM_PEAK_GBS, "GB/s")}
+        work = [by_name.get(n) for n in names]
     dom = int(np.argmax(stage_ms))
     bound, amount, peak, unit = work[dom] if work[dom] else ("hbm", None, HBM_PEAK_GBS, "GB/s")
     achieved = amount / (stage_ms[dom] * 1e-3) if amount else None
@@ -423,35 +435,29 @@ def bench_stack(args, wl):
     step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms = float(step_ms.mean())
 
-    # per kernel: single layers (layer i % L) on a normalised token, flush-
-    # subtracted as in the layer benchmark; the RMSNorm launch included
-    names = ["rmsnorm"] + [s[0] for s in GEMV_STAGES]
+    # per kernel: one layer (layer i % L) of the stack at a time, stage by
+    # stage, flush-subtracted as in the layer benchmark
     n_stages = moe.moe_layer_stage_count(sh, 1)
-    lws = moe.workspace(moe.moe_workspace_bytes(sh, 1), dev)
-    nrm = torch.empty_like(x)
-    y = torch.empty_like(x)
+    names = [s_[0] for s_ in stack_stages(gemv_stages(n_stages))]
+    one = [moe.layers([L]) for L in layers]
+    xt = torch.empty_like(x)
     reps = 4 * wl.layers
     fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     sev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n_stages + 1)] for _ in range(reps)]
+            for _ in range(n_stages)] for _ in range(reps)]
     for i in range(reps):
-        L = layers[i % wl.layers]
         fev[i][0].record(stream)
         flush()
         fev[i][1].record(stream)
-        sev[i][0][0].record(stream)
-        flush()
-        moe.moe_rmsnorm(xs[i % n_inputs], L.norm_g, eps, nrm)
-        sev[i][0][1].record(stream)
+        xt.copy_(xs[i % n_inputs])
         for s_ in range(n_stages):
-            sev[i][s_ + 1][0].record(stream)
+            sev[i][s_][0].record(stream)
             flush()
-            moe.moe_layer_forward(sh, nrm, L.gate_w, L.bias, L.routed, L.shared, y, lws,
-                                  flags=moe.MOE_STAGE(s_))
-            sev[i][s_ + 1][1].record(stream)
+            moe.moe_stack_forward(sh, xt, one[i % wl.layers], eps, ws, flags=moe.MOE_STAGE(s_))
+            sev[i][s_][1].record(stream)
     torch.cuda.synchronize()
     flush_ms = float(np.mean([a.elapsed_time(b) for a, b in fev]))
-    stage_ms = np.array([[sev[i][s_][0].elapsed_time(sev[i][s_][1]) for s_ in range(n_stages + 1)]
+    stage_ms = np.array([[sev[i][s_][0].elapsed_time(sev[i][s_][1]) for s_ in range(n_stages)]
                          for i in range(reps)]).mean(0) - flush_ms
     log("bench: per-kernel pass done (flush %.1f us subtracted)" % (flush_ms * 1e3))
 
@@ -460,8 +466,10 @@ def bench_stack(args, wl):
     down_bytes = wl.down_bytes + 4 * wl.hidden
     token_bytes = wl.layers * n_exp * (gate_up_bytes + down_bytes)
     router_bytes = wl.layers * 4 * wl.n_experts * wl.hidden
-    work = [None, ("hbm", 4 * wl.n_experts * wl.hidden / 1e9), None, ("hbm", n_exp * gate_up_bytes / 1e9),
-            ("hbm", n_exp * down_bytes / 1e9)]
+    by_name = {"rmsnorm+router+quant": ("hbm", 4 * wl.n_experts * wl.hidden / 1e9),
+               "gate_up_swiglu_quant": ("hbm", n_exp * gate_up_bytes / 1e9),
+               "down_combine": ("hbm", n_exp * down_bytes / 1e9)}
+    work = [by_name.get(n) for n in names]
     cand = [j for j in range(len(names)) if work[j]]
     dom = max(cand, key=lambda j: stage_ms[j])
     amount = work[dom][1]

@@ -169,7 +169,9 @@ size_t moe_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags);
 /* number of stages moe_layer_forward runs for these arguments (the n of
  * MOE_STAGE(n) runs from 0 to this minus 1); < 0 on bad arguments.
  * GEMV path: router + quantiser (one launch for T <= 8, else two), then
- * plan, gate/up, down per chunk of tokens.  GROUPED path: 7 stages -- router
+ * plan, gate/up, down per chunk of tokens; a single token (T = 1) of the
+ * production row widths is routed by the gate/up launch itself, so its
+ * stages are router + quantiser, gate/up, down.  GROUPED path: 7 stages -- router
  * logits, top-k, quantiser, permutation (three launches), gate/up, down,
  * combine. */
 int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags);
@@ -187,11 +189,17 @@ int moe_rmsnorm(const float *x, const float *g, double eps, int32_t T, int32_t H
  *   for l in 0 .. n_layers-1:   x = x + MoE_l(RMSNorm_l(x))
  * RMSNorm as moe_rmsnorm with eps and the layer's norm weight; MoE_l as
  * moe_layer_forward with the layer's router, correction bias and experts;
- * the layer result is rounded to fp32 and added to x in fp32.
+ * the layer result is rounded to fp32 and added to x in fp32.  On the GEMV
+ * path (T <= 8) with H <= 8192, H % 4 == 0 and 16-byte aligned x and norm
+ * weights, the router launch forms RMSNorm_l(x) itself (the same fp32 values
+ * as moe_rmsnorm) and no separate RMSNorm launch runs.
  *   x        [T][H] fp32 residual stream, updated in place
  *   layers   HOST array of n_layers descriptors (device pointers inside)
  *   idx_out, w_out  [n_layers][T][k] (nullable): every layer's routing
- *   flags    MOE_PATH_* (MOE_ACCUMULATE is implied; MOE_STAGE not allowed)
+ *   flags    MOE_PATH_* (MOE_ACCUMULATE is implied); MOE_STAGE(n) selects
+ *            stage n of every layer as moe_layer_stage_count counts them,
+ *            with a separate RMSNorm launch (when there is one) run with
+ *            stage 0
  * ws: at least moe_stack_workspace_bytes(shape, T, flags) bytes, 256-byte
  *   aligned.  The launches only read the layers array during the call, so a
  *   stream capture of one call replays with the same device pointers. */

@@ -49,9 +49,13 @@ inline int hip_rc(int e) { return e ? MOE_EHIP : MOE_OK; }
 size_t route_ws(const moe_shape_t &s, int T) { return align256(router_logit_bytes(s, T)); }
 
 // The stage list of the GEMV path for T tokens: the router / quantiser
-// launch(es), then
-// (plan, gate/up, down) for every chunk of Tc tokens.
-int gemv_stage_count(int T, int Tc) { return (T <= kGemvMaxT ? 1 : 2) + 3 * ((T + Tc - 1) / Tc); }
+// launch(es), then (plan, gate/up, down) for every chunk of Tc tokens; a
+// token routed inside the gate/up launch has no plan launch.
+int gemv_stage_count(const moe_shape_t &s, int T, int Tc)
+{
+    if (gemv_inline_route(s, T)) return 3;
+    return (T <= kGemvMaxT ? 1 : 2) + 3 * ((T + Tc - 1) / Tc);
+}
 
 // The grouped path's stages: router logits, top-k, quantiser, permutation
 // (three launches), gate/up, down, combine.
@@ -156,7 +160,8 @@ int moe_route(const moe_shape_t *shape, const float *x, int32_t T, const float *
     double *logits = static_cast<double *>(ws);
     const int ksplit = router_ksplit(T, shape->hidden, shape->n_experts);
     int e = (T <= kGemvMaxT)
-                ? launch_router_logits(x, T, shape->hidden, gate_w, shape->n_experts, logits, nullptr, nullptr, stream)
+                ? launch_router_logits(x, T, shape->hidden, gate_w, shape->n_experts, logits, nullptr, nullptr,
+                                       nullptr, 0.0, stream)
                 : launch_router_logits_mfma(x, T, shape->hidden, gate_w, shape->n_experts, ksplit, logits, stream);
     if (e) return MOE_EHIP;
     return hip_rc(launch_topk(rcfg, logits, ksplit, bias, T, topk_idx, topk_w, stream));
@@ -198,7 +203,7 @@ int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags)
     if (use_grouped(*shape, T, flags)) return gg_shape_ok(*shape) ? kGgStages : -MOE_EUNSUPPORTED;
     const int Tc = gemv_chunk_tokens(*shape, T);
     if (!Tc) return -MOE_EUNSUPPORTED;
-    return gemv_stage_count(T, Tc);
+    return gemv_stage_count(*shape, T, Tc);
 }
 
 int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t expert, const int8_t *q,
@@ -235,6 +240,11 @@ int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t exp
     return MOE_OK;
 }
 
+static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float *gate_w, const float *bias,
+                      const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
+                      float *w_out, uint32_t flags, void *ws, size_t ws_bytes, const float *ng, double eps,
+                      hipStream_t stream);
+
 int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w, const float *bias,
                       const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
                       float *w_out, uint32_t flags, void *ws, size_t ws_bytes, hipStream_t stream)
@@ -257,12 +267,26 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
     if (use_grouped(*shape, T, flags))
         return layer_grouped(*shape, x, T, gate_w, bias, *routed, shared, y, idx_out, w_out, flags, ws, ws_bytes,
                              stream);
+    return layer_gemv(*shape, x, T, gate_w, bias, routed, shared, y, idx_out, w_out, flags, ws, ws_bytes, nullptr,
+                      0.0, stream);
+}
+
+// moe_layer_forward on the GEMV path (arguments already checked).  With
+// ng != nullptr the layer input is RMSNorm(x) with weight ng, formed by the
+// router launch (router_norms_input must hold); y may then be x itself with
+// MOE_ACCUMULATE, since x is read by the router launch only.
+static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float *gate_w, const float *bias,
+                      const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
+                      float *w_out, uint32_t flags, void *ws, size_t ws_bytes, const float *ng, double eps,
+                      hipStream_t stream)
+{
+    const moe_shape_t *shape = &sh;
     if (shape->hidden % kGemvDownRows) return MOE_EUNSUPPORTED;
     const int Tc = gemv_chunk_tokens(*shape, T);
     if (!Tc) return MOE_EUNSUPPORTED;
     const GemvWs L = gemv_ws(*shape, T, Tc, false);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
-    const int nstages = gemv_stage_count(T, Tc);
+    const int nstages = gemv_stage_count(*shape, T, Tc);
     const uint32_t sel = (flags & MOE_STAGE_MASK) >> 8;
     if (sel && nstages > 8) return MOE_EINVAL;
     auto run = [&](int s) { return sel == 0 || ((sel >> s) & 1u); };
@@ -294,18 +318,24 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
     };
     int stage = 0;
     if (T <= kGemvMaxT) {
-        if (run(stage) && launch_router_logits(x, T, H, gate_w, E, logits, xq, xd, stream)) return MOE_EHIP;
+        if (run(stage) && launch_router_logits(x, T, H, gate_w, E, logits, xq, xd, ng, eps, stream))
+            return MOE_EHIP;
         stage++;
     } else {
+        if (ng) return MOE_EINVAL;
         if (run(stage) && launch_router_logits_mfma(x, T, H, gate_w, E, ksplit, logits, stream)) return MOE_EHIP;
         stage++;
         if (run(stage) && launch_quant(x, T, H, xq, xd, stream)) return MOE_EHIP;
         stage++;
     }
+    const bool here = gemv_inline_route(*shape, T);
     for (int c0 = 0; c0 < T; c0 += Tc) {
         GemvArgs a = args(c0, (T - c0 < Tc) ? T - c0 : Tc);
-        if (run(stage) && launch_plan(a, stream)) return MOE_EHIP;
-        stage++;
+        a.inline_route = here ? 1 : 0;
+        if (!here) {
+            if (run(stage) && launch_plan(a, stream)) return MOE_EHIP;
+            stage++;
+        }
         if (run(stage) && launch_gate_up(a, stream)) return MOE_EHIP;
         stage++;
         if (run(stage) && launch_down(a, stream)) return MOE_EHIP;
@@ -336,7 +366,8 @@ int moe_stack_forward(const moe_shape_t *shape, float *x, int32_t T, const moe_l
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || n_layers < 0 || !(eps >= 0.0)) return MOE_EINVAL;
-    if (flags & ~3u) return MOE_EINVAL;
+    if (flags & ~(3u | MOE_STAGE_MASK)) return MOE_EINVAL;
+    if ((flags & 3u) == 3u) return MOE_EINVAL;
     if ((idx_out == nullptr) != (w_out == nullptr)) return MOE_EINVAL;
     if (T == 0 || n_layers == 0) return MOE_OK;
     if (!x || !layers || !ws || !al(ws, 256)) return MOE_EINVAL;
@@ -353,12 +384,23 @@ int moe_stack_forward(const moe_shape_t *shape, float *x, int32_t T, const moe_l
     float *n = static_cast<float *>(ws);
     void *lws = static_cast<char *>(ws) + nb;
     const size_t tk = (size_t)T * shape->top_k;
+    const uint32_t sel = (flags & MOE_STAGE_MASK) >> 8;
     for (int l = 0; l < n_layers; l++) {
         const moe_layer_t &L = layers[l];
-        if (launch_rmsnorm(x, L.norm_g, eps, T, shape->hidden, n, stream)) return MOE_EHIP;
-        rc = moe_layer_forward(shape, n, T, L.gate_w, L.bias, &L.routed, shape->n_shared ? &L.shared : nullptr,
-                               x, idx_out ? idx_out + l * tk : nullptr, w_out ? w_out + l * tk : nullptr,
-                               flags | MOE_ACCUMULATE, lws, ws_bytes - nb, stream);
+        const moe_weights_t *sw = shape->n_shared ? &L.shared : nullptr;
+        int32_t *il = idx_out ? idx_out + l * tk : nullptr;
+        float *wl = w_out ? w_out + l * tk : nullptr;
+        if (!use_grouped(*shape, T, flags) && T <= kGemvMaxT && router_norms_input(x, L.norm_g, shape->hidden)) {
+            // the router launch normalises the residual itself; the layer
+            // adds its output to the residual in place
+            rc = layer_gemv(*shape, x, T, L.gate_w, L.bias, &L.routed, sw, x, il, wl, flags | MOE_ACCUMULATE, lws,
+                            ws_bytes - nb, L.norm_g, eps, stream);
+        } else {
+            if ((sel == 0 || (sel & 1u)) && launch_rmsnorm(x, L.norm_g, eps, T, shape->hidden, n, stream))
+                return MOE_EHIP;
+            rc = moe_layer_forward(shape, n, T, L.gate_w, L.bias, &L.routed, sw, x, il, wl, flags | MOE_ACCUMULATE,
+                                   lws, ws_bytes - nb, stream);
+        }
         if (rc) return rc;
     }
     return MOE_OK;

@@ -21,7 +21,10 @@
 //               order.  The combine is fused; no float atomics, so results
 //               are run-to-run identical.
 // The *_sw ("row-sweep") kernels serve the production shapes; the *_rg
-// ("row-group") kernels take any other shape the ABI accepts.
+// ("row-group") kernels take any other shape the ABI accepts.  A single
+// token on the row-sweep kernels has no plan launch: its gate/up workgroups
+// run the selection themselves while the shared expert's workgroups, which
+// need no routing, already stream their rows.
 #include "moe_dev.h"
 #include "moe_internal.h"
 #include "topk_dev.h"
@@ -163,9 +166,9 @@ __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int
 
 // ---------------------------------------------------------------- plan kernel
 // One workgroup routes the chunk's tokens and publishes the plan (and the
-// routing, when asked): measured on MI355X, one such launch costs far less
-// than every gate/up workgroup re-deriving the plan, or than cross-workgroup
-// signalling through a shared atomic counter.
+// routing, when asked): for several tokens, measured on MI355X, one such
+// launch costs less than every gate/up workgroup re-deriving the union plan,
+// or than cross-workgroup signalling through a shared atomic counter.
 __global__ __launch_bounds__(256) void k_plan(const GemvArgs a, const PlanDims pd)
 {
     __shared__ int plan[1 + 3 * (kGemvMaxT * kMaxTopK + 1) + 2 * kGemvMaxT * (kMaxTopK + 1)];
@@ -640,12 +643,53 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
 // Every slot of a chunk, with the plan the plan kernel published.  The plan
 // is range-checked, so a corrupt plan can only skip work, never steer a load
 // out of the weight tensors.
+// One token, no plan launch: the first n_shared * tiles workgroups take the
+// shared expert, which needs no routing, and start streaming at once; every
+// other workgroup runs the noaux_tc selection itself (the same inputs in the
+// same order, so every workgroup reaches the same result) and takes the u-th
+// selected expert in ascending order.  Workgroup (u = 0, tile 0) publishes the
+// plan for the down kernel, and the routing when asked.
+template <int WB, int CPT, int RPS>
+__device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, int tiles, float (*s_h)[32],
+                                       float (*part)[1][kSwGroups][32])
+{
+    __shared__ int plan[1 + 5 * (kMaxTopK + 1)];
+    __shared__ int s_idx[kMaxTopK];
+    __shared__ float s_w[kMaxTopK];
+    __shared__ TopkLds tl;
+    const int v = blockIdx.x / tiles, tile = blockIdx.x % tiles, row0 = tile * 32;
+    if (v < a.n_shared) {
+        if (threadIdx.x == 0) plan[0] = 0;  // the token list of the shared slot: token 0
+        __syncthreads();
+        gate_up_tile_sw<WB, CPT, RPS, 1>(a, a.shared, 0, row0, 1, plan, a.rc.k, s_h, part);
+        return;
+    }
+    const int u = v - a.n_shared;
+    build_plan(a, pd, plan, s_idx, s_w, nullptr, &tl);
+    if (u == 0 && tile == 0) {
+        for (int i = threadIdx.x; i < pd.words; i += kSwThreads) a.plan[i] = plan[i];
+        if (a.idx_out && threadIdx.x < a.rc.k) {
+            a.idx_out[threadIdx.x] = s_idx[threadIdx.x];
+            a.w_out[threadIdx.x] = s_w[threadIdx.x];
+        }
+    }
+    const int e = plan[pd.o_e + u], p0 = plan[pd.o_p0 + u];
+    if (e < 0 || e >= a.E || p0 < 0 || p0 >= pd.P) return;
+    gate_up_tile_sw<WB, CPT, RPS, 1>(a, a.routed, e, row0, 1, plan + pd.o_t + p0, p0, s_h, part);
+}
+
 template <int WB, int CPT, int RPS, int TT>
 __global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
     __shared__ float s_h[TT][32];
     __shared__ float part[2][TT][kSwGroups][32];
     const int tiles = a.I / 32;
+    if constexpr (TT == 1) {
+        if (a.inline_route) {
+            gate_up_sw_routed_here<WB, CPT, RPS>(a, pd, tiles, s_h, part);
+            return;
+        }
+    }
     const int u = blockIdx.x / tiles, row0 = (blockIdx.x % tiles) * 32;
     // the slot count and the slot's entries in one round trip (u < pd.S, so
     // every entry read lies inside the plan; a stale entry of an unused slot
@@ -840,6 +884,12 @@ static int run_down(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, h
     case 4: return FN<__VA_ARGS__, 4>(a, cc, pd, st);                           \
     default: return FN<__VA_ARGS__, 8>(a, cc, pd, st);                          \
     }
+
+bool gemv_inline_route(const moe_shape_t &s, int T)
+{
+    ChunkCfg cc;
+    return T == 1 && chunk_cfg(s.hidden, s.wbits, cc) && gate_up_sw_kind(cc.cpr) != 0;
+}
 
 int launch_gate_up(const GemvArgs &a, hipStream_t st)
 {

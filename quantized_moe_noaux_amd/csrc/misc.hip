@@ -11,8 +11,6 @@ namespace moe {
 // read once: every float4 of a thread is loaded before any arithmetic (a
 // decode step normalises one 24 KB row, so load latency, not bandwidth, is
 // what costs), kept in registers and reused for the output.
-constexpr int kNormPer = 8;  // float4s per thread held in registers (H <= 8192 in one pass)
-
 __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, const float *__restrict__ g,
                                                  double eps, int H, float *out)
 {
@@ -20,42 +18,21 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, co
     const float *xr = x + (size_t)blockIdx.x * H;
     float *orow = out + (size_t)blockIdx.x * H;
     const int tid = threadIdx.x;
-    double ss = 0.0;
     const bool vec = (((uintptr_t)xr | (uintptr_t)g | (uintptr_t)orow) & 15) == 0;
     if (vec && (H & 3) == 0 && H <= 256 * 4 * kNormPer) {
         const int n4 = H / 4;
         float4 v[kNormPer];
+        load_row_regs(xr, n4, v);
+        const double r = row_rstd(v, H, eps, red);
 #pragma unroll
         for (int j = 0; j < kNormPer; j++) {
             const int i = tid + 256 * j;
-            v[j] = (i < n4) ? reinterpret_cast<const float4 *>(xr)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int j = 0; j < kNormPer; j++) {
-            ss = fma((double)v[j].x, (double)v[j].x, ss);
-            ss = fma((double)v[j].y, (double)v[j].y, ss);
-            ss = fma((double)v[j].z, (double)v[j].z, ss);
-            ss = fma((double)v[j].w, (double)v[j].w, ss);
-        }
-        ss = wave_sum_d(ss);
-        if (lane_id() == 0) red[wave_id()] = ss;
-        __syncthreads();
-        const double r = 1.0 / sqrt(((red[0] + red[1]) + (red[2] + red[3])) / H + eps);
-#pragma unroll
-        for (int j = 0; j < kNormPer; j++) {
-            const int i = tid + 256 * j;
-            if (i < n4) {
-                const float4 gv = reinterpret_cast<const float4 *>(g)[i];
-                float4 o;
-                o.x = (float)((double)v[j].x * r * (double)gv.x);
-                o.y = (float)((double)v[j].y * r * (double)gv.y);
-                o.z = (float)((double)v[j].z * r * (double)gv.z);
-                o.w = (float)((double)v[j].w * r * (double)gv.w);
-                reinterpret_cast<float4 *>(orow)[i] = o;
-            }
+            if (i < n4)
+                reinterpret_cast<float4 *>(orow)[i] = norm4(v[j], r, reinterpret_cast<const float4 *>(g)[i]);
         }
         return;
     }
+    double ss = 0.0;
     for (int j = tid; j < H; j += 256) ss = fma((double)xr[j], (double)xr[j], ss);
     ss = wave_sum_d(ss);
     if (lane_id() == 0) red[wave_id()] = ss;

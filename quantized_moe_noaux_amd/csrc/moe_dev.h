@@ -65,6 +65,45 @@ __device__ __forceinline__ double wave_max_d(double v)
     return v;
 }
 
+// ---------------------------------------------------------------- RMSNorm pieces
+// RMSNorm with the sum of squares and the scaling in fp64 and one fixed
+// reduction order, shared by the RMSNorm kernel and the router launch that
+// normalises its own input, so that both produce the same fp32 values.
+// A row of n4 float4s is held by the 256 threads of a block: thread t,
+// register j = float4 t + 256 j (zero past the row), so H <= 8192 fits.
+constexpr int kNormPer = 8;
+__device__ __forceinline__ void load_row_regs(const float *__restrict__ xr, int n4, float4 (&v)[kNormPer])
+{
+#pragma unroll
+    for (int j = 0; j < kNormPer; j++) {
+        const int i = threadIdx.x + 256 * j;
+        v[j] = (i < n4) ? reinterpret_cast<const float4 *>(xr)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+// 1 / sqrt(mean(x^2) + eps) of the row in v; every thread of the 256-thread
+// block calls it (one barrier), red = 4 doubles of LDS not in use elsewhere.
+__device__ __forceinline__ double row_rstd(const float4 (&v)[kNormPer], int H, double eps, double *red)
+{
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kNormPer; j++) {
+        ss = fma((double)v[j].x, (double)v[j].x, ss);
+        ss = fma((double)v[j].y, (double)v[j].y, ss);
+        ss = fma((double)v[j].z, (double)v[j].z, ss);
+        ss = fma((double)v[j].w, (double)v[j].w, ss);
+    }
+    ss = wave_sum_d(ss);
+    if (lane_id() == 0) red[wave_id()] = ss;
+    __syncthreads();
+    return 1.0 / sqrt(((red[0] + red[1]) + (red[2] + red[3])) / H + eps);
+}
+// x * r * g rounded once to fp32, per component
+__device__ __forceinline__ float4 norm4(const float4 &v, double r, const float4 &g)
+{
+    return make_float4((float)((double)v.x * r * (double)g.x), (float)((double)v.y * r * (double)g.y),
+                       (float)((double)v.z * r * (double)g.z), (float)((double)v.w * r * (double)g.w));
+}
+
 // ---------------------------------------------------------------- activation chunks
 // Activation operand of one weight chunk, held in registers.
 template <int WB> struct Act;

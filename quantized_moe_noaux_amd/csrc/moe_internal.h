@@ -95,8 +95,15 @@ GemvWs gemv_ws(const moe_shape_t &s, int T, int Tc, bool single);
 
 // ---------------------------------------------------------------- launchers
 // (each returns hipGetLastError() as an int after its launch)
+// Router logits (and the quantised x) of T <= kGemvMaxT tokens; with
+// ng != nullptr the input is RMSNorm(x) with weight ng, formed in the launch.
 int launch_router_logits(const float *x, int T, int H, const float *gate_w, int E, double *logits,
-                         int8_t *xq, float *xd, hipStream_t st);
+                         int8_t *xq, float *xd, const float *ng, double eps, hipStream_t st);
+// whether the router launch can normalise its own input for this row width
+inline bool router_norms_input(const float *x, const float *ng, int H)
+{
+    return H % 4 == 0 && H <= 8192 && ((((uintptr_t)x) | ((uintptr_t)ng)) & 15) == 0;
+}
 // Router logits of more than kGemvMaxT tokens: fp64 MFMA over `ksplit`
 // slices of the hidden dimension, partial sums in part[ksplit][T][E]
 // (router_ksplit picks the slice count; 1 for T <= kGemvMaxT).
@@ -136,7 +143,12 @@ struct GemvArgs {
     int32_t *idx_out;
     float *w_out;
     int accumulate;
+    // one token, routed by the gate/up workgroups themselves (no plan launch)
+    int inline_route;
 };
+// Whether a T-token call of this shape routes inside the gate/up launch
+// (one token, row-sweep gate/up kernel) instead of in a plan launch.
+bool gemv_inline_route(const moe_shape_t &s, int T);
 // one workgroup: routing of the chunk and its batch-union plan
 int launch_plan(const GemvArgs &a, hipStream_t st);
 // gate/up + SwiGLU + h quantisation of every slot of the published plan

@@ -28,40 +28,75 @@ bool route_cfg(const moe_shape_t &s, RouteCfg &rc)
 
 // ---------------------------------------------------------------- logits, small T
 // Block b < E computes z[t][b] for all T <= 8 tokens; blocks >= E quantise x.
+// With ng != nullptr the input is RMSNorm(x) with weight ng: every block
+// normalises the rows it reads itself (a block-wide fp64 sum of squares per
+// token, the same arithmetic as the RMSNorm kernel, so the values equal that
+// kernel's output) and the normalised row never goes through memory.  The
+// host only passes ng for H <= 8192, H % 4 == 0 and 16-byte aligned x, ng.
 __global__ __launch_bounds__(256) void k_router_logits_small(
     const float *__restrict__ x, int T, int H, const float *__restrict__ gate_w, int E,
-    double *__restrict__ logits, int8_t *__restrict__ xq, float *__restrict__ xd)
+    double *__restrict__ logits, int8_t *__restrict__ xq, float *__restrict__ xd,
+    const float *__restrict__ ng, double eps)
 {
     __shared__ double red[4][kGemvMaxT];
+    __shared__ double nred[kGemvMaxT][4];
     const int tid = threadIdx.x;
+    const int n4 = H / 4;
     if ((int)blockIdx.x < E) {
         const int e = blockIdx.x;
         double acc[kGemvMaxT];
 #pragma unroll
         for (int t = 0; t < kGemvMaxT; t++) acc[t] = 0.0;
         const float4 *wr = reinterpret_cast<const float4 *>(gate_w + (size_t)e * H);
-        const int n4 = H / 4;
-        constexpr int kPer = 8;  // float4s per thread per pass: all loads issued before use
-        for (int base = 0; base < n4; base += 256 * kPer) {
-            float4 w[kPer];
+        constexpr int kPer = kNormPer;  // float4s per thread per pass: all loads issued before use
+        if (ng) {
+            float4 w[kPer], gv[kPer];
 #pragma unroll
             for (int j = 0; j < kPer; j++) {
-                const int i = base + tid + 256 * j;
+                const int i = tid + 256 * j;
                 w[j] = (i < n4) ? wr[i] : make_float4(0, 0, 0, 0);
+                gv[j] = (i < n4) ? reinterpret_cast<const float4 *>(ng)[i] : make_float4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int t = 0; t < kGemvMaxT; t++) {
                 if (t < T) {
-                    const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H);
+                    float4 v[kNormPer];
+                    load_row_regs(x + (size_t)t * H, n4, v);
+                    const double r = row_rstd(v, H, eps, nred[t]);
 #pragma unroll
                     for (int j = 0; j < kPer; j++) {
-                        const int i = base + tid + 256 * j;
-                        if (i < n4) {
-                            const float4 v = xr[i];
-                            acc[t] = fma((double)w[j].x, (double)v.x, acc[t]);
-                            acc[t] = fma((double)w[j].y, (double)v.y, acc[t]);
-                            acc[t] = fma((double)w[j].z, (double)v.z, acc[t]);
-                            acc[t] = fma((double)w[j].w, (double)v.w, acc[t]);
+                        if (tid + 256 * j < n4) {
+                            const float4 n = norm4(v[j], r, gv[j]);
+                            acc[t] = fma((double)w[j].x, (double)n.x, acc[t]);
+                            acc[t] = fma((double)w[j].y, (double)n.y, acc[t]);
+                            acc[t] = fma((double)w[j].z, (double)n.z, acc[t]);
+                            acc[t] = fma((double)w[j].w, (double)n.w, acc[t]);
+                        }
+                    }
+                }
+            }
+        } else {
+            for (int base = 0; base < n4; base += 256 * kPer) {
+                float4 w[kPer];
+#pragma unroll
+                for (int j = 0; j < kPer; j++) {
+                    const int i = base + tid + 256 * j;
+                    w[j] = (i < n4) ? wr[i] : make_float4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int t = 0; t < kGemvMaxT; t++) {
+                    if (t < T) {
+                        const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H);
+#pragma unroll
+                        for (int j = 0; j < kPer; j++) {
+                            const int i = base + tid + 256 * j;
+                            if (i < n4) {
+                                const float4 v = xr[i];
+                                acc[t] = fma((double)w[j].x, (double)v.x, acc[t]);
+                                acc[t] = fma((double)w[j].y, (double)v.y, acc[t]);
+                                acc[t] = fma((double)w[j].z, (double)v.z, acc[t]);
+                                acc[t] = fma((double)w[j].w, (double)v.w, acc[t]);
+                            }
                         }
                     }
                 }
@@ -84,6 +119,19 @@ __global__ __launch_bounds__(256) void k_router_logits_small(
     const int b = g >> 3, sub = g & 7;
     const bool live = b < T * nb;
     float4 v = live ? reinterpret_cast<const float4 *>(x + (size_t)b * 32)[sub] : make_float4(0, 0, 0, 0);
+    if (ng) {
+        // the tokens this block's 32 blocks of 32 fall in (block-uniform bounds)
+        const int b0 = ((int)blockIdx.x - E) * 32;
+        const int b1 = min(b0 + 31, T * nb - 1);
+        double r = 0.0;
+        for (int t = b0 / nb; t <= b1 / nb; t++) {
+            float4 row[kNormPer];
+            load_row_regs(x + (size_t)t * H, n4, row);
+            const double rt = row_rstd(row, H, eps, nred[t]);
+            if (live && b / nb == t) r = rt;
+        }
+        if (live) v = norm4(v, r, reinterpret_cast<const float4 *>(ng)[(b % nb) * 8 + sub]);
+    }
     float d;
     uint32_t packed = quant_block8(v, d);
     if (live) {
@@ -93,10 +141,11 @@ __global__ __launch_bounds__(256) void k_router_logits_small(
 }
 
 int launch_router_logits(const float *x, int T, int H, const float *gate_w, int E, double *logits,
-                         int8_t *xq, float *xd, hipStream_t st)
+                         int8_t *xq, float *xd, const float *ng, double eps, hipStream_t st)
 {
+    if (ng && !router_norms_input(x, ng, H)) return (int)hipErrorInvalidValue;
     const int qblocks = xq ? (T * (H / 32) * 8 + 255) / 256 : 0;
-    k_router_logits_small<<<E + qblocks, 256, 0, st>>>(x, T, H, gate_w, E, logits, xq, xd);
+    k_router_logits_small<<<E + qblocks, 256, 0, st>>>(x, T, H, gate_w, E, logits, xq, xd, ng, eps);
     return (int)hipGetLastError();
 }
 

@@ -62,7 +62,12 @@ def test_workspace_sizes(m):
 
 def test_stage_count(m):
     sh = big_shape(m)
-    assert m.moe_layer_stage_count(sh, 1) == 4          # router+quant, plan, gate/up, down
+    # one token: router+quant, gate/up (which routes the token itself), down
+    assert m.moe_layer_stage_count(sh, 1) == 3
+    assert m.moe_layer_stage_count(big_shape(m, wbits=2), 1) == 3
+    # a row width without a row-sweep kernel keeps the plan launch
+    assert m.moe_layer_stage_count(big_shape(m, hidden=4096), 1) == 4
+    assert m.moe_layer_stage_count(sh, 2) == 4          # router+quant, plan, gate/up, down
     assert m.moe_layer_stage_count(sh, 0) == 0
     assert m.moe_layer_stage_count(big_shape(m, top_k=40), 1) < 0
     # grouped path: logits, top-k, quant, permute, gate/up, down, combine

@@ -138,3 +138,43 @@ def test_stack_graph_replay(dev, m, stack):
             # eager work between replays
             _ = (t * 2).sum().item()
             assert torch.equal(x_static, ref), "graph replay %d differs from the eager stack" % rep
+
+
+def test_stack_matches_separate_norm_launches(dev, m, stack):
+    """The stack's router launch forms each layer's RMSNorm itself; the result
+    must equal, bit for bit, RMSNorm launches followed by layer calls that add
+    into the residual, through the public entry points."""
+    wl, hosts, layers = stack
+    sh = m.shape_of(wl)
+    n_l = 6
+    x0 = to_dev(hosts[0].x, dev)
+    x_fused, idx_f, w_f = run_stack(m, wl, layers[:n_l], x0, dev)
+    x = x0.clone()
+    n = torch.empty_like(x)
+    ws = m.workspace(m.moe_workspace_bytes(sh, 1), dev)
+    idx = torch.empty((n_l, 1, wl.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((n_l, 1, wl.top_k), dtype=torch.float32, device=dev)
+    for l, L in enumerate(layers[:n_l]):
+        m.moe_rmsnorm(x, L.norm_g, EPS, n)
+        m.moe_layer_forward(sh, n, L.gate_w, L.bias, L.routed, L.shared, x, ws, idx[l], w[l],
+                            flags=m.MOE_ACCUMULATE)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_f[:n_l], idx.cpu().numpy())
+    assert np.array_equal(w_f[:n_l], w.cpu().numpy())
+    assert torch.equal(x_fused, x)
+
+
+def test_stack_stages_one_by_one(dev, m, stack):
+    wl, hosts, layers = stack
+    sh = m.shape_of(wl)
+    arr = m.layers(layers[:1])
+    ws = m.workspace(m.moe_stack_workspace_bytes(sh, 1), dev)
+    x0 = to_dev(hosts[0].x, dev)
+    ref = x0.clone()
+    m.moe_stack_forward(sh, ref, arr, EPS, ws)
+    n = m.moe_layer_stage_count(sh, 1)
+    x = x0.clone()
+    for s in range(n):
+        m.moe_stack_forward(sh, x, arr, EPS, ws, flags=m.MOE_STAGE(s))
+    torch.cuda.synchronize()
+    assert torch.equal(x, ref)
