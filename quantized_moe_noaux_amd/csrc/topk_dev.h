@@ -21,119 +21,175 @@ __device__ __forceinline__ uint64_t order_key(double v)
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// LDS scratch of block_topk
-struct TopkLds {
-    uint64_t key[kMaxExperts];   // order key of c = s + bias
-    double c[kMaxExperts];
-    double s[kMaxExperts];       // sigmoid scores
-    double gs[kMaxGroups];       // group scores
-    int kept[kMaxGroups];        // kept groups, ascending
+// Lane exchanges for the group phase.  DPP moves (quad_perm, row mirrors)
+// stay inside the VALU; a cross-lane permute through the LDS crossbar costs
+// a round trip of ~100 cycles per step on MI355X.
+template <int CTRL> __device__ __forceinline__ double dpp_d(double v)
+{
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int l)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+// (b1, b2) = the two largest of the multiset {b1, b2, o1, o2}, where b1 >= b2
+// and o1 >= o2
+__device__ __forceinline__ void merge_top2(double &b1, double &b2, double o1, double o2)
+{
+    const double n2 = fmax(fmin(b1, o1), fmax(b2, o2));
+    b1 = fmax(b1, o1);
+    b2 = n2;
+}
+template <int CTRL> __device__ __forceinline__ void dpp_top2(double &b1, double &b2)
+{
+    merge_top2(b1, b2, dpp_d<CTRL>(b1), dpp_d<CTRL>(b2));
+}
+
+// LDS scratch of block_topk.  Keys are stored per group at a stride of
+// mpad = m rounded up to 8 (zero keys in the padding), finalists likewise
+// padded to a multiple of 8, so the rank loops read whole 8-key steps with
+// no bounds checks: a zero key never outranks a real one.
+struct __align__(16) TopkLds {
+    double s[kMaxExperts];                       // sigmoid scores
+    double c[kMaxExperts];                       // c = s + bias
+    uint64_t key[kMaxExperts + 7 * kMaxGroups];  // order keys, group-strided
+    uint64_t fkey[kMaxExperts + 8];              // finalists' keys
+    int fe[kMaxExperts];                         // finalists' experts
+    int kept[kMaxGroups];                        // kept groups, ascending
     int nkept;
-    uint64_t ckey[kMaxExperts];  // keys of the kept candidates, in expert order
-    int crank[2][kMaxExperts];   // partial ranks of the kept candidates
     int sel_e[kMaxTopK];
     double sel_s[kMaxTopK];
 };
 
+// Number of keys among the 8 at p that outrank key ke at position pos
+// (position j outranks if its key is larger, or equal with j < pos).
+__device__ __forceinline__ int outrank8(const uint64_t *p, int j0, uint64_t ke, int pos)
+{
+    const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(p);
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const ulonglong2 v = q[u];
+        cnt += (v.x > ke) || (v.x == ke && j0 + 2 * u < pos);
+        cnt += (v.y > ke) || (v.y == ke && j0 + 2 * u + 1 < pos);
+    }
+    return cnt;
+}
+
 // Block-wide noaux_tc routing of one token (every thread of the block calls
-// it; blockDim.x >= 64).  The selection is a parallel rank count:
-//   rank(e) = #{kept candidates e' with c' > c, or c' == c and e' < e}
-// and e is selected at position rank(e) when that is below k (key 0 = a
-// padding entry never outranks a real one: real keys are above 0).  Every phase
-// spreads its work over many lanes with independent loads: on MI355X a
-// dependent LDS or cross-lane round trip costs ~100 cycles, so serial
-// chains, not arithmetic, set the latency of this step.  All scores and
-// comparisons are fp64.
+// it; blockDim.x >= 64).  Every phase spreads its work over many lanes with
+// independent loads: on MI355X a dependent LDS or cross-lane round trip costs
+// ~100 cycles, so serial chains, not arithmetic, set the latency of this step.
+//   1. s, c = s + bias and the order key of c for every expert (all logit
+//      loads issued before any arithmetic);
+//   2. one wave: group score = sum of the two largest c (lane l holds the
+//      experts epl*l ..; a group spans lpg lanes, merged by DPP), and the
+//      topk_group best groups (score desc, index asc) are kept;
+//   3. in-group rank of every candidate of a kept group; only a candidate
+//      with in-group rank < k can be among the top k, so each kept group
+//      has exactly min(m, k) finalists, stored at (kept slot, in-group rank);
+//   4. rank of every finalist among the finalists: for a finalist in the top
+//      k it equals its rank among all candidates (every candidate above it is
+//      a finalist too), and one outside the top k has rank >= k there too.
+//      Equal keys rank by position, which is expert order (kept groups
+//      ascend, and in-group ranks order equal keys by expert index), so a
+//      tie goes to the lower expert index;
+//   5. the selected s normalised to sum one, times routed_scaling_factor.
+// All scores and comparisons are fp64 (order keys compare as the doubles).
 //   zt: the token's logits, as the sum of nparts slices pstride apart
 //   (added in slice order)
 __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, size_t pstride, int nparts,
                            const float *__restrict__ bias, int *sel_e, float *sel_w, TopkLds &L)
 {
     const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id();
-    const int E = rc.E, G = rc.G, m = E / G;
-    for (int e = tid; e < E; e += nt) {
-        double z = zt[e];
-        for (int p = 1; p < nparts; p++) z += zt[p * pstride + e];
-        const double sv = 1.0 / (1.0 + exp(-z));
-        const double cv = sv + (double)bias[e];
-        L.s[e] = sv;
-        L.c[e] = cv;
-        L.key[e] = order_key(cv);
+    const int E = rc.E, G = rc.G, m = E / G, k = rc.k;
+    const int mpad = (m + 7) & ~7;
+    for (int e0 = 0; e0 < E; e0 += 2 * nt) {
+        const int ea = e0 + tid, eb = e0 + nt + tid;
+        double za = 0.0, zb = 0.0;
+        float ba = 0.f, bb = 0.f;
+        if (ea < E) { za = zt[ea]; ba = bias[ea]; }
+        if (eb < E) { zb = zt[eb]; bb = bias[eb]; }
+        for (int p = 1; p < nparts; p++) {
+            if (ea < E) za += zt[p * pstride + ea];
+            if (eb < E) zb += zt[p * pstride + eb];
+        }
+        if (ea < E) {
+            const double sv = 1.0 / (1.0 + exp(-za)), cv = sv + (double)ba;
+            L.s[ea] = sv;
+            L.c[ea] = cv;
+            L.key[(ea / m) * mpad + ea % m] = order_key(cv);
+        }
+        if (eb < E) {
+            const double sv = 1.0 / (1.0 + exp(-zb)), cv = sv + (double)bb;
+            L.s[eb] = sv;
+            L.c[eb] = cv;
+            L.key[(eb / m) * mpad + eb % m] = order_key(cv);
+        }
     }
+    for (int i = tid; i < G * (mpad - m); i += nt) L.key[(i / (mpad - m)) * mpad + m + i % (mpad - m)] = 0ull;
     __syncthreads();
     if (tid < 64) {
-        // group score = sum of the two largest c: lpg lanes per group (a power
-        // of two), each scanning <= 8 experts, then a lane butterfly
-        int lpg = 1;
-        while (lpg * 2 * G <= 64) lpg <<= 1;
-        const int g = lane / lpg, sub = lane % lpg;
+        const int epl = rc.epl, lpg = rc.lpg;
         double b1 = -INFINITY, b2 = -INFINITY;
-        if (g < G) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int r = sub + lpg * j;
-                if (r < m) {
-                    const double cv = L.c[g * m + r];
-                    if (cv > b1) { b2 = b1; b1 = cv; }
-                    else if (cv > b2) b2 = cv;
-                }
+        for (int j = 0; j < 8; j++) {
+            const int e = lane * epl + j;
+            if (j < epl && e < E) {
+                const double cv = L.c[e];
+                if (cv > b1) { b2 = b1; b1 = cv; }
+                else if (cv > b2) b2 = cv;
             }
         }
-        for (int o = 1; o < lpg; o <<= 1) {
-            const double o1 = __shfl_xor(b1, o), o2 = __shfl_xor(b2, o);
-            const double n2 = fmax(fmin(b1, o1), fmax(b2, o2));
-            b1 = fmax(b1, o1);
-            b2 = n2;
-        }
+        if (lpg > 1) dpp_top2<0xB1>(b1, b2);   // quad_perm [1,0,3,2]: lane ^ 1
+        if (lpg > 2) dpp_top2<0x4E>(b1, b2);   // quad_perm [2,3,0,1]: lane ^ 2
+        if (lpg > 4) dpp_top2<0x141>(b1, b2);  // row_half_mirror: the other quad of 8
+        if (lpg > 8) dpp_top2<0x140>(b1, b2);  // row_mirror: the other half of 16
+        for (int o = 16; o < lpg; o <<= 1) merge_top2(b1, b2, __shfl_xor(b1, o), __shfl_xor(b2, o));
         const double gsv = (m >= 2) ? b1 + b2 : b1;
-        // rank of each group among the G (score desc, index asc)
+        const int g = lane / lpg;
         int grank = 0;
         for (int h = 0; h < G; h++) {
-            const double o = __shfl(gsv, h * lpg);
+            const double o = readlane_d(gsv, h * lpg);
             grank += (o > gsv) || (o == gsv && h < g);
         }
-        const bool keep = g < G && sub == 0 && grank < rc.tg;
+        const bool keep = g < G && lane % lpg == 0 && grank < rc.tg;
         const unsigned long long kb = __ballot(keep);
         if (keep) L.kept[__popcll(kb & ((1ull << lane) - 1))] = g;
         if (lane == 0) L.nkept = __popcll(kb);
     }
     __syncthreads();
-    // Candidates = the experts of the kept groups; kept groups ascend, so
-    // candidate order is expert order and a tie goes to the lower position.
-    // rank(ci) = #{j : key_j > key_ci, or key_j == key_ci and j < ci}, counted
-    // by two threads per candidate over halves of j (broadcast LDS reads, no
-    // atomics) and summed in a fixed order.
-    const int nk = L.nkept, ncand = nk * m;
-    for (int ci = tid; ci < ncand; ci += nt) L.ckey[ci] = L.key[L.kept[ci / m] * m + ci % m];
-    __syncthreads();
-    const int split = (2 * ncand <= nt) ? 2 : 1, half = ncand / split;
-    for (int item = tid; item < ncand * split; item += nt) {
-        const int ci = item % ncand, part = item / ncand;
-        const int j0 = part * half, j1 = (part + 1 == split) ? ncand : j0 + half;
-        const uint64_t ke = L.ckey[ci];
+    const int nk = L.nkept, f1 = m < k ? m : k, nf = nk * f1, nfpad = (nf + 7) & ~7;
+    for (int ci = tid; ci < nk * m; ci += nt) {
+        const int slot = ci / m, r = ci - slot * m, g = L.kept[slot];
+        const uint64_t *gk = L.key + g * mpad;
+        const uint64_t ke = gk[r];
         int cnt = 0;
-        for (int j = j0; j < j1; j += 8) {
-            uint64_t kj[8];
-#pragma unroll
-            for (int u = 0; u < 8; u++) kj[u] = (j + u < j1) ? L.ckey[j + u] : 0ull;
-#pragma unroll
-            for (int u = 0; u < 8; u++) cnt += (kj[u] > ke) || (kj[u] == ke && j + u < ci);
-        }
-        L.crank[part][ci] = cnt;
-    }
-    __syncthreads();
-    for (int ci = tid; ci < ncand; ci += nt) {
-        const int r = L.crank[0][ci] + (split == 2 ? L.crank[1][ci] : 0);
-        if (r < rc.k) {
-            const int e = L.kept[ci / m] * m + ci % m;
-            L.sel_e[r] = e;
-            L.sel_s[r] = L.s[e];
+        for (int j = 0; j < mpad; j += 8) cnt += outrank8(gk + j, j, ke, r);
+        if (cnt < f1) {
+            L.fkey[slot * f1 + cnt] = ke;
+            L.fe[slot * f1 + cnt] = g * m + r;
         }
     }
+    for (int i = nf + tid; i < nfpad; i += nt) L.fkey[i] = 0ull;
     __syncthreads();
-    if (tid < rc.k) {
+    for (int fi = tid; fi < nf; fi += nt) {
+        const uint64_t ke = L.fkey[fi];
+        int cnt = 0;
+        for (int j = 0; j < nfpad; j += 8) cnt += outrank8(L.fkey + j, j, ke, fi);
+        if (cnt < k) {
+            const int e = L.fe[fi];
+            L.sel_e[cnt] = e;
+            L.sel_s[cnt] = L.s[e];
+        }
+    }
+    __syncthreads();
+    if (tid < k) {
         double sum = 0.0;
-        for (int i = 0; i < rc.k; i++) sum += L.sel_s[i];
+        for (int i = 0; i < k; i++) sum += L.sel_s[i];
         sel_e[tid] = L.sel_e[tid];
         sel_w[tid] = (float)(L.sel_s[tid] / sum * (double)rc.rsf);
     }
