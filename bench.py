@@ -187,6 +187,8 @@ def main():
     ap.add_argument("--workload", default="decode_int4",
                     choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--graph", action="store_true", help="launch each step as a captured HIP graph")
+    ap.add_argument("--stack-eager", action="store_true", help="stack: launch directly instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -266,18 +268,43 @@ def main():
     torch.cuda.synchronize()
     log("bench: inputs ready, %d warmup steps done" % warmup)
 
+    # With --graph the step is launched as a HIP graph (one captured per
+    # rotating input).  Measured on MI355X with ROCm 7, replaying the
+    # three-launch decode layer as a graph costs ~7 us more per step than
+    # launching its kernels directly, so direct launch is the default.
+    graphs = []
+    if args.graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        for i in range(n_inputs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            flush()
+            graphs[i % n_inputs].replay()
+        torch.cuda.synchronize()
+        log("bench: %d step graphs captured" % n_inputs)
+
+    def timed(run):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            flush()
+            ev[i][0].record(stream)
+            run(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, np.array([a.elapsed_time(b) for a, b in ev])
+
     # ---------------------------------------------------------------- timed steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        flush()
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    if graphs:
+        wall, step_ms = timed(lambda i: graphs[i % n_inputs].replay())
+    else:
+        wall, step_ms = timed(step)
     ms = float(step_ms.mean())
 
     # ---------------------------------------------------------------- per-kernel
@@ -332,8 +359,9 @@ def main():
     bound, amount, peak, unit = work[dom] if work[dom] else ("hbm", None, HBM_PEAK_GBS, "GB/s")
     achieved = amount / (stage_ms[dom] * 1e-3) if amount else None
     traffic = traffic_from_profiles(wl.name, names[dom])
-    log("bench: step %.2f us (p10 %.2f p90 %.2f), %.0f tok/s, weights %.0f GB/s = %.1f%% of HBM peak" %
-        (ms * 1e3, np.percentile(step_ms, 10) * 1e3, np.percentile(step_ms, 90) * 1e3, tok_s,
+    log("bench: step %.2f us (p10 %.2f p90 %.2f%s), %.0f tok/s, weights %.0f GB/s = %.1f%% of HBM peak" %
+        (ms * 1e3, np.percentile(step_ms, 10) * 1e3, np.percentile(step_ms, 90) * 1e3,
+         ", graph" if graphs else "", tok_s,
          layer_bytes / (ms * 1e-3) / 1e9, 100 * layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS))
     log("bench: stages (us): %s" % ", ".join("%s %.2f" % (n, v * 1e3) for n, v in zip(names, stage_ms)))
 
@@ -359,7 +387,7 @@ def main():
         "config": {"workload": wl.name, "T": T, "hidden": wl.hidden, "inter": wl.inter,
                    "n_experts": wl.n_experts, "n_group": wl.n_group, "topk_group": wl.topk_group,
                    "top_k": wl.top_k, "n_shared": wl.n_shared, "wbits": wl.wbits, "rsf": wl.rsf,
-                   "path": "grouped" if grouped else "gemv"},
+                   "path": "grouped" if grouped else "gemv", "graph": bool(graphs)},
         "effective_weight_GBps": layer_bytes / (ms * 1e-3) / 1e9,
         "effective_weight_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": bound, "kernel": names[dom], "achieved": achieved, "peak": peak, "unit": unit,
@@ -406,23 +434,29 @@ def bench_stack(args, wl):
         if not args.no_flush:
             flush_buf.sum()
 
-    # the step: the token's residual stream through every layer, one graph
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
-        moe.moe_stack_forward(sh, x, arr, eps, ws)
-    torch.cuda.synchronize()
+    # the step: the token's residual stream through every layer, as one
+    # captured graph (or, with --stack-eager, launched directly)
+    graph = None
+    if not args.stack_eager:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            moe.moe_stack_forward(sh, x, arr, eps, ws)
+        torch.cuda.synchronize()
 
     def step(i):
         x.copy_(xs[i % n_inputs])
-        graph.replay()
+        if graph is not None:
+            graph.replay()
+        else:
+            moe.moe_stack_forward(sh, x, arr, eps, ws)
 
     for i in range(warmup):
         flush()
         step(i)
     torch.cuda.synchronize()
-    log("bench: graph captured, %d warmup steps done" % warmup)
+    log("bench: %s, %d warmup steps done" % ("graph captured" if graph is not None else "direct launch", warmup))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
@@ -521,7 +555,7 @@ def bench_stack(args, wl):
         "config": {"workload": wl.name, "T": 1, "layers": wl.layers, "hidden": wl.hidden, "inter": wl.inter,
                    "n_experts": wl.n_experts, "n_group": wl.n_group, "topk_group": wl.topk_group,
                    "top_k": wl.top_k, "n_shared": wl.n_shared, "wbits": wl.wbits, "rsf": wl.rsf,
-                   "path": "gemv", "graph": True},
+                   "path": "gemv", "graph": graph is not None},
         "effective_weight_GBps": token_bytes / (ms * 1e-3) / 1e9,
         "effective_weight_frac": token_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -134,15 +134,17 @@ __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, siz
     __syncthreads();
     if (tid < 64) {
         const int epl = rc.epl, lpg = rc.lpg;
+        // all eight reads issued at once (clamped in bounds, masked after),
+        // then a branch-free top-2 insertion
+        double cvs[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) cvs[j] = L.c[min(lane * epl + j, E - 1)];
         double b1 = -INFINITY, b2 = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            const int e = lane * epl + j;
-            if (j < epl && e < E) {
-                const double cv = L.c[e];
-                if (cv > b1) { b2 = b1; b1 = cv; }
-                else if (cv > b2) b2 = cv;
-            }
+            const double cv = (j < epl && lane * epl + j < E) ? cvs[j] : -INFINITY;
+            b2 = fmax(b2, fmin(b1, cv));
+            b1 = fmax(b1, cv);
         }
         if (lpg > 1) dpp_top2<0xB1>(b1, b2);   // quad_perm [1,0,3,2]: lane ^ 1
         if (lpg > 2) dpp_top2<0x4E>(b1, b2);   // quad_perm [2,3,0,1]: lane ^ 2

@@ -154,3 +154,44 @@ def test_expert_ffn(dev, m, name, T):
     m.moe_expert_ffn(shape1, w, 0, to_dev(q, dev), to_dev(d, dev), y, ws)
     torch.cuda.synchronize()
     assert_close(y.cpu().numpy(), oracle.expert_ffn(oracle.shape_of(wl), ex, q, d))
+
+
+# ---------------------------------------------------------------- graph replay
+@pytest.mark.parametrize("name,T,path", [("decode_int4", 1, "gemv"), ("verify_int8", 8, "gemv"),
+                                         ("tiny", 100, "grouped")])
+def test_layer_graph_replay(dev, m, name, T, path):
+    """A captured layer call replays the eager result exactly, on several
+    inputs in turn, with eager work and synchronisations between replays."""
+    wl = synth.workload(name)
+    L = DevLayer(wl, dev, T=T)
+    flags = m.MOE_PATH_GROUPED if path == "grouped" else m.MOE_PATH_GEMV
+    sh = m.shape_of(wl)
+    ws = m.workspace(m.moe_workspace_bytes(sh, T, flags), dev)
+    xs = [L.x] + [torch.from_numpy(synth.host_normals(s, synth.stream_id(0, synth.X), T * wl.hidden, 1.0)
+                                   .reshape(T, wl.hidden)).to(dev) for s in (21, 22)]
+    outs = []
+    for x in xs:
+        y = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
+        idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, wl.top_k), dtype=torch.float32, device=dev)
+        m.moe_layer_forward(sh, x, L.gate_w, L.bias, L.routed, L.shared, y, ws, idx, w, flags=flags)
+        outs.append((y, idx, w))
+    torch.cuda.synchronize()
+    x_s = torch.empty_like(L.x)
+    y_s = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
+    i_s = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+    w_s = torch.empty((T, wl.top_k), dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        m.moe_layer_forward(sh, x_s, L.gate_w, L.bias, L.routed, L.shared, y_s, ws, i_s, w_s, flags=flags)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for x, (y, idx, w) in zip(xs, outs):
+            x_s.copy_(x)
+            g.replay()
+            torch.cuda.synchronize()
+            _ = (x * 2).sum().item()
+            assert torch.equal(y_s, y) and torch.equal(i_s, idx) and torch.equal(w_s, w), \
+                "replay %d differs from the eager call" % rep
