@@ -49,15 +49,16 @@ template <int CTRL> __device__ __forceinline__ void dpp_top2(double &b1, double 
 }
 
 // LDS scratch of block_topk.  Keys are stored per group at a stride of
-// mpad = m rounded up to 8 (zero keys in the padding), finalists likewise
-// padded to a multiple of 8, so the rank loops read whole 8-key steps with
-// no bounds checks: a zero key never outranks a real one.
+// mpad = m rounded up to 8 (zero keys in the padding), so the in-group rank
+// loop reads whole 8-key steps with no bounds checks: a zero key never
+// outranks a real one.
 struct __align__(16) TopkLds {
     double s[kMaxExperts];                       // sigmoid scores
     double c[kMaxExperts];                       // c = s + bias
     uint64_t key[kMaxExperts + 7 * kMaxGroups];  // order keys, group-strided
-    uint64_t fkey[kMaxExperts + 8];              // finalists' keys
+    uint64_t fkey[kMaxExperts];                  // finalists' keys
     int fe[kMaxExperts];                         // finalists' experts
+    int frank[kMaxExperts];                      // finalists' ranks among the finalists
     int kept[kMaxGroups];                        // kept groups, ascending
     int nkept;
     int sel_e[kMaxTopK];
@@ -96,7 +97,10 @@ __device__ __forceinline__ int outrank8(const uint64_t *p, int j0, uint64_t ke, 
 //      a finalist too), and one outside the top k has rank >= k there too.
 //      Equal keys rank by position, which is expert order (kept groups
 //      ascend, and in-group ranks order equal keys by expert index), so a
-//      tie goes to the lower expert index;
+//      tie goes to the lower expert index.  The rank is the in-group rank
+//      plus, per other kept group, the length of that group's run of
+//      finalists that outrank it: a group's finalists sit in outrank order,
+//      so a binary search finds the run;
 //   5. the selected s normalised to sum one, times routed_scaling_factor.
 // All scores and comparisons are fp64 (order keys compare as the doubles).
 //   zt: the token's logits, as the sum of nparts slices pstride apart
@@ -164,7 +168,7 @@ __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, siz
         if (lane == 0) L.nkept = __popcll(kb);
     }
     __syncthreads();
-    const int nk = L.nkept, f1 = m < k ? m : k, nf = nk * f1, nfpad = (nf + 7) & ~7;
+    const int nk = L.nkept, f1 = m < k ? m : k, nf = nk * f1;
     for (int ci = tid; ci < nk * m; ci += nt) {
         const int slot = ci / m, r = ci - slot * m, g = L.kept[slot];
         const uint64_t *gk = L.key + g * mpad;
@@ -174,18 +178,39 @@ __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, siz
         if (cnt < f1) {
             L.fkey[slot * f1 + cnt] = ke;
             L.fe[slot * f1 + cnt] = g * m + r;
+            L.frank[slot * f1 + cnt] = 0;
         }
     }
-    for (int i = nf + tid; i < nfpad; i += nt) L.fkey[i] = 0ull;
+    __syncthreads();
+    int top = 1;  // largest power of two <= f1
+    while (2 * top <= f1) top *= 2;
+    for (int it = tid; it < nf * nk; it += nt) {
+        const int fi = it / nk, b = it - fi * nk, ga = fi / f1;
+        int cnt;
+        if (b == ga) {
+            cnt = fi - ga * f1;
+        } else {
+            // group b's entries at positions before fi's group outrank it on
+            // equal keys too
+            const uint64_t kx = L.fkey[fi], *gb = L.fkey + b * f1;
+            cnt = 0;
+            for (int st = top; st > 0; st >>= 1) {
+                const int j = cnt + st - 1;
+                if (j < f1) {
+                    const uint64_t ky = gb[j];
+                    if (ky > kx || (ky == kx && b < ga)) cnt += st;
+                }
+            }
+        }
+        atomicAdd(&L.frank[fi], cnt);
+    }
     __syncthreads();
     for (int fi = tid; fi < nf; fi += nt) {
-        const uint64_t ke = L.fkey[fi];
-        int cnt = 0;
-        for (int j = 0; j < nfpad; j += 8) cnt += outrank8(L.fkey + j, j, ke, fi);
-        if (cnt < k) {
+        const int r = L.frank[fi];
+        if (r < k) {
             const int e = L.fe[fi];
-            L.sel_e[cnt] = e;
-            L.sel_s[cnt] = L.s[e];
+            L.sel_e[r] = e;
+            L.sel_s[r] = L.s[e];
         }
     }
     __syncthreads();
