@@ -257,9 +257,12 @@ def main():
         moe.moe_layer_forward(sh, xs[i % n_inputs], gate_w, bias, routed, shared, y, ws, idx, wts, flags=flags | f)
 
     # union of the selected experts per input, for the bytes actually read
+    # (through moe_route, so that every launch of the layer's kernels in this
+    # run is a timed one or a warmup, all on flushed caches)
     union_sizes = []
+    rws = moe.workspace(moe.moe_route_workspace_bytes(sh, T), dev)
     for i in range(n_inputs):
-        step(i)
+        moe.moe_route(sh, xs[i], gate_w, bias, idx, wts, rws)
         torch.cuda.synchronize()
         union_sizes.append(len(np.unique(idx.cpu().numpy())))
     for i in range(warmup):
@@ -288,49 +291,58 @@ def main():
         torch.cuda.synchronize()
         log("bench: %d step graphs captured" % n_inputs)
 
-    def timed(run):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            flush()
-            ev[i][0].record(stream)
-            run(i)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, np.array([a.elapsed_time(b) for a, b in ev])
+    run = (lambda i: graphs[i % n_inputs].replay()) if graphs else step
 
     # ---------------------------------------------------------------- timed steps
-    if graphs:
-        wall, step_ms = timed(lambda i: graphs[i % n_inputs].replay())
-    else:
-        wall, step_ms = timed(step)
-    ms = float(step_ms.mean())
+    # Every interval is one pair of events with a cache flush inside, right
+    # before the work: [flush] alone, and [flush, stages 0..s] for every s
+    # (MOE_STAGE masks; the last prefix is the whole step), interleaved on
+    # each rotating input.  A flush-only interval carries the same event
+    # overhead and flush as the others, so the differences are the work's
+    # GPU time (each kernel starts right after its predecessor, as in a
+    # serving loop) and stage s's duration is prefix s minus prefix s-1.
+    def prefix_flags(s):
+        f = 0
+        for j in range(s + 1):
+            f |= moe.MOE_STAGE(j)
+        return f
 
-    # ---------------------------------------------------------------- per-kernel
-    # Each stage of each step runs alone between two events, after a flush
-    # inside the same interval; one flush-only interval per step is
-    # subtracted.  Both intervals carry the same event overhead, so the
-    # difference is the stage's launch duration (plus one dispatch gap), with
-    # the caches as cold as in the timed steps.
     def ev_pair():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    sev = [[ev_pair() for _ in range(n_stages)] for _ in range(steps)]
+
     fev = [ev_pair() for _ in range(steps)]
+    sev = [[ev_pair() for _ in range(n_stages)] for _ in range(steps)]
+    rev = [ev_pair() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for i in range(steps):
         fev[i][0].record(stream)
         flush()
         fev[i][1].record(stream)
-        for s in range(n_stages):
+        rev[i][0].record(stream)
+        flush()
+        run(i)
+        rev[i][1].record(stream)
+        for s in range(n_stages - 1):
             sev[i][s][0].record(stream)
             flush()
-            step(i, moe.MOE_STAGE(s))
+            step(i, prefix_flags(s))
             sev[i][s][1].record(stream)
     torch.cuda.synchronize()
-    flush_ms = float(np.mean([a.elapsed_time(b) for a, b in fev]))
-    stage_ms = np.array([[sev[i][s][0].elapsed_time(sev[i][s][1]) for s in range(n_stages)]
-                         for i in range(steps)]).mean(0) - flush_ms
-    log("bench: per-stage pass done (flush %.1f us subtracted)" % (flush_ms * 1e3))
+    wall = time.perf_counter() - t0
+    f_ms = np.array([a.elapsed_time(b) for a, b in fev])
+    flush_ms = float(f_ms.mean())
+    step_ms = np.array([a.elapsed_time(b) for a, b in rev]) - f_ms
+    ms = float(step_ms.mean())
+    per = np.array([[sev[i][s][0].elapsed_time(sev[i][s][1]) for s in range(n_stages - 1)]
+                    + [step_ms[i] + f_ms[i]] for i in range(steps)]) - f_ms[:, None]
+    prefix_ms = per.mean(0)
+    stage_ms = np.diff(np.concatenate([[0.0], prefix_ms]))
+    # standard error of each stage's mean (per-step differences of prefixes):
+    # a stage much shorter than the step's own spread is not resolved
+    stage_se = np.diff(np.concatenate([np.zeros((steps, 1)), per], 1), axis=1).std(0) / np.sqrt(steps)
+    log("bench: step and per-stage timing done (%d steps, %.1f us of flush subtracted per interval)" %
+        (steps, flush_ms * 1e3))
 
     # algorithmic work.  Weight bytes: each unique routed expert of the batch
     # and the shared expert once (codes + fp32 row scales); router weights
@@ -394,9 +406,11 @@ def main():
                      "frac": achieved / peak if achieved else None, "traffic": traffic,
                      "algorithmic_per_launch": amount, "avg_launch_us": float(stage_ms[dom] * 1e3)},
         "detail": {"stage_us": {n: float(v * 1e3) for n, v in zip(names, stage_ms)},
+                   "stage_us_stderr": {n: float(v * 1e3) for n, v in zip(names, stage_se)},
                    "stage_roofline_frac": {n: (w[1] / (v * 1e-3) / w[2] if w else None)
                                            for n, v, w in zip(names, stage_ms, work)},
                    "step_us_p10_p50_p90": [float(np.percentile(step_ms, p) * 1e3) for p in (10, 50, 90)],
+                   "flush_us": flush_ms * 1e3,
                    "mean_experts_read": n_exp, "layer_weight_bytes": layer_bytes,
                    "router_weight_bytes": router_bytes, "wall_s_timed_loop_incl_flush": wall},
         "cpu_baseline": cpu,
@@ -457,43 +471,59 @@ def bench_stack(args, wl):
         step(i)
     torch.cuda.synchronize()
     log("bench: %s, %d warmup steps done" % ("graph captured" if graph is not None else "direct launch", warmup))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # timed as the layer benchmark does: one pair of events per interval,
+    # each with a flush right before the work, minus an interleaved
+    # flush-only interval
+    def ev_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def prefix_flags(s):
+        f = 0
+        for j in range(s + 1):
+            f |= moe.MOE_STAGE(j)
+        return f
+
+    fev = [ev_pair() for _ in range(steps)]
+    rev = [ev_pair() for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        fev[i][0].record(stream)
         flush()
-        ev[i][0].record(stream)
+        fev[i][1].record(stream)
+        rev[i][0].record(stream)
+        flush()
         step(i)
-        ev[i][1].record(stream)
+        rev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    step_ms = np.array([a.elapsed_time(b) for a, b in rev]) - np.array([a.elapsed_time(b) for a, b in fev])
     ms = float(step_ms.mean())
 
-    # per kernel: one layer (layer i % L) of the stack at a time, stage by
-    # stage, flush-subtracted as in the layer benchmark
+    # per kernel: one layer (layer i % L) of the stack at a time; stage s's
+    # duration is the time of stages 0..s minus that of stages 0..s-1
     n_stages = moe.moe_layer_stage_count(sh, 1)
     names = [s_[0] for s_ in stack_stages(gemv_stages(n_stages))]
     one = [moe.layers([L]) for L in layers]
-    xt = torch.empty_like(x)
+    xt = xs[0].clone()
     reps = 4 * wl.layers
-    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    sev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n_stages)] for _ in range(reps)]
+    fev = [ev_pair() for _ in range(reps)]
+    sev = [[ev_pair() for _ in range(n_stages)] for _ in range(reps)]
     for i in range(reps):
         fev[i][0].record(stream)
         flush()
         fev[i][1].record(stream)
-        xt.copy_(xs[i % n_inputs])
         for s_ in range(n_stages):
             sev[i][s_][0].record(stream)
             flush()
-            moe.moe_stack_forward(sh, xt, one[i % wl.layers], eps, ws, flags=moe.MOE_STAGE(s_))
+            moe.moe_stack_forward(sh, xt, one[i % wl.layers], eps, ws, flags=prefix_flags(s_))
             sev[i][s_][1].record(stream)
     torch.cuda.synchronize()
     flush_ms = float(np.mean([a.elapsed_time(b) for a, b in fev]))
-    stage_ms = np.array([[sev[i][s_][0].elapsed_time(sev[i][s_][1]) for s_ in range(n_stages)]
-                         for i in range(reps)]).mean(0) - flush_ms
-    log("bench: per-kernel pass done (flush %.1f us subtracted)" % (flush_ms * 1e3))
+    prefix_ms = np.array([np.mean([sev[i][s_][0].elapsed_time(sev[i][s_][1]) for i in range(reps)])
+                          for s_ in range(n_stages)]) - flush_ms
+    stage_ms = np.diff(np.concatenate([[0.0], prefix_ms]))
+    log("bench: per-kernel pass done (%d layers per stage prefix, flush %.1f us subtracted)" % (reps, flush_ms * 1e3))
 
     n_exp = wl.top_k + wl.n_shared
     gate_up_bytes = 2 * (wl.gate_bytes + 4 * wl.inter)
@@ -562,7 +592,8 @@ def bench_stack(args, wl):
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(wl.name, names[dom]),
                      "algorithmic_per_launch": amount, "avg_launch_us": float(stage_ms[dom] * 1e3)},
         "detail": {"per_layer_us": {n: float(v * 1e3) for n, v in zip(names, stage_ms)},
-                   "step_us_p10_p50_p90": [float(np.percentile(step_ms, p) * 1e3) for p in (10, 50, 90)],
+                   "step_us_p10_p50_p90": [float(np.percentile(step_ms, p) * 1e3)
+                                                           for p in (10, 50, 90)],
                    "token_weight_bytes": token_bytes, "router_weight_bytes": router_bytes,
                    "wall_s_timed_loop_incl_flush": wall},
         "cpu_baseline": cpu,
