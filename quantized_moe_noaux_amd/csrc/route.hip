@@ -201,7 +201,6 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const float *__restr
         vb[j] = e < E;
         pb[j] = gate_w + (size_t)(vb[j] ? e : 0) * H + kbeg + 4 * g;
     }
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     v4d acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; i++)
@@ -210,14 +209,17 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const float *__restr
     // three register sets: the K block being multiplied and the next two in
     // flight (one wave per SIMD pair: the loads' latency is not hidden by
     // other waves)
+    // Loads are unconditional, so they issue as plain dwordx4 loads with
+    // partial waits: a row past T or E reads row 0 (its results are never
+    // stored, and rows do not mix in the product), and a block past the
+    // slice end re-reads the last block (it is never multiplied).
     float4 a[3][2], b[3][4];
     auto fetch = [&](int set, int kk) {
+        const int kc = kk < kq ? kk : kq - 16;
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-            a[set][i] = (kk < kq && va[i]) ? *reinterpret_cast<const float4 *>(pa[i] + kk) : z4;
+        for (int i = 0; i < 2; i++) a[set][i] = *reinterpret_cast<const float4 *>(pa[i] + kc);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            b[set][j] = (kk < kq && vb[j]) ? *reinterpret_cast<const float4 *>(pb[j] + kk) : z4;
+        for (int j = 0; j < 4; j++) b[set][j] = *reinterpret_cast<const float4 *>(pb[j] + kc);
     };
     auto mul = [&](int set) {
 #pragma unroll
