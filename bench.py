@@ -188,6 +188,7 @@ def main():
                     choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--graph", action="store_true", help="launch each step as a captured HIP graph")
+    ap.add_argument("--top-p", type=float, default=0.0, help="adaptive expert top-p (decode / verify)")
     ap.add_argument("--stack-eager", action="store_true", help="stack: launch directly instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -217,6 +218,10 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     wl = synth.workload(args.workload)
+    if args.top_p:
+        if wl.layers > 1 or args.workload == "prefill_int4":
+            raise SystemExit("--top-p applies to the one-layer GEMV workloads (decode_int4, verify_int8)")
+        wl = synth.workload(args.workload, top_p=args.top_p)
     if wl.layers > 1:
         return bench_stack(args, wl)
     T = wl.T
@@ -264,7 +269,8 @@ def main():
     for i in range(n_inputs):
         moe.moe_route(sh, xs[i], gate_w, bias, idx, wts, rws)
         torch.cuda.synchronize()
-        union_sizes.append(len(np.unique(idx.cpu().numpy())))
+        sel = idx.cpu().numpy()
+        union_sizes.append(len(np.unique(sel[sel >= 0])))        # top-p drops slots (-1)
     for i in range(warmup):
         flush()
         step(i)
@@ -370,7 +376,8 @@ def main():
     dom = int(np.argmax(stage_ms))
     bound, amount, peak, unit = work[dom] if work[dom] else ("hbm", None, HBM_PEAK_GBS, "GB/s")
     achieved = amount / (stage_ms[dom] * 1e-3) if amount else None
-    traffic = traffic_from_profiles(wl.name, names[dom])
+    # counters are taken on the plain selection; a top-p run reads fewer bytes
+    traffic = None if wl.top_p else traffic_from_profiles(wl.name, names[dom])
     log("bench: step %.2f us (p10 %.2f p90 %.2f%s), %.0f tok/s, weights %.0f GB/s = %.1f%% of HBM peak" %
         (ms * 1e3, np.percentile(step_ms, 10) * 1e3, np.percentile(step_ms, 90) * 1e3,
          ", graph" if graphs else "", tok_s,
@@ -396,7 +403,8 @@ def main():
         "dtype": "i8",
         "data": "synthetic (seeded SplitMix64 weights and N(0,1) tokens, %d rotating inputs%s)" %
                 (n_inputs, "" if args.no_flush else ", caches flushed between steps"),
-        "config": {"workload": wl.name, "T": T, "hidden": wl.hidden, "inter": wl.inter,
+        "config": {"workload": wl.name + ("_topp%g" % wl.top_p if wl.top_p else ""), "T": T,
+                   "top_p": wl.top_p, "hidden": wl.hidden, "inter": wl.inter,
                    "n_experts": wl.n_experts, "n_group": wl.n_group, "topk_group": wl.topk_group,
                    "top_k": wl.top_k, "n_shared": wl.n_shared, "wbits": wl.wbits, "rsf": wl.rsf,
                    "path": "grouped" if grouped else "gemv", "graph": bool(graphs)},

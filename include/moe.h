@@ -60,6 +60,16 @@ typedef struct {
     int32_t n_shared;     /* 0 or 1 shared expert (weight 1, not scaled) */
     int32_t wbits;        /* 2, 4 or 8 */
     float   routed_scaling_factor;
+    /* Adaptive expert top-p (GeekNews #31297, useful options: the --topp
+     * knob).  In (0, 1): each token keeps the shortest prefix of its
+     * selection (selection order, at least one expert) whose share of the
+     * selection's summed sigmoid scores reaches routed_top_p (shares added in
+     * slot order in fp64), and renormalises the kept weights to sum to
+     * routed_scaling_factor; a dropped slot reports expert -1 and weight 0
+     * and its expert is not read.  0 or >= 1: off (every selected expert is
+     * kept).  The grouped path does not take it: with top-p on, MOE_PATH_AUTO
+     * stays on the GEMV path and MOE_PATH_GROUPED is MOE_EUNSUPPORTED. */
+    float   routed_top_p;
 } moe_shape_t;
 
 typedef struct {

@@ -31,7 +31,7 @@ class Shape(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
-                ("rsf", ctypes.c_double)]
+                ("rsf", ctypes.c_double), ("top_p", ctypes.c_double)]
 
 
 class Expert(ctypes.Structure):
@@ -81,9 +81,11 @@ def _c(a, dt):
     return np.ascontiguousarray(a, dtype=dt)
 
 
-def shape_of(wl, rsf=None):
+def shape_of(wl, rsf=None, top_p=None):
+    # top_p as the fp32 value the GPU library receives
+    p = getattr(wl, "top_p", 0.0) if top_p is None else top_p
     return Shape(wl.hidden, wl.inter, wl.n_experts, wl.n_group, wl.topk_group, wl.top_k,
-                 wl.n_shared, wl.wbits, wl.rsf if rsf is None else rsf)
+                 wl.n_shared, wl.wbits, wl.rsf if rsf is None else rsf, float(np.float32(p)))
 
 
 def _expert_struct(ex):
@@ -227,4 +229,4 @@ def permute(idx, E):
 
 def layer_experts(layer, idx):
     """HostExpert objects for the routed experts that idx selects."""
-    return {int(e): layer.expert(int(e)) for e in np.unique(idx)}
+    return {int(e): layer.expert(int(e)) for e in np.unique(idx) if e >= 0}

@@ -127,13 +127,33 @@ int oracle_route(const oracle_shape *sh, const float *x, int T, const float *gat
         for (int e = 0; e < E; e++)
             if (gkeep[e / m] && !taken[e] && c[e] > best_left) best_left = c[e];
 
+        /* adaptive expert top-p (GeekNews #31297, useful options; yodev.dev
+           colibrì page, useful knobs: the --topp option, 30-40% fewer expert
+           reads).  The pages name the knob only; the reading: keep the
+           shortest prefix of the selection (selection order, at least one
+           expert) whose share of the selection's summed s reaches p, the
+           shares s_i / sum added in slot order in fp64, then renormalise
+           over the kept prefix.  Dropped slots report expert -1 and weight 0. */
+        int kept = k;
+        if (sh->top_p > 0.0 && sh->top_p < 1.0) {
+            double cum = 0.0;
+            kept = 0;
+            while (kept < k) {
+                cum += s[idx[(size_t)t * k + kept]] / sum;
+                kept++;
+                if (cum >= sh->top_p) break;
+            }
+            sum = 0.0;
+            for (int i = 0; i < kept; i++) sum += s[idx[(size_t)t * k + i]];
+        }
         for (int i = 0; i < k; i++)
-            w[(size_t)t * k + i] = (float)(s[idx[(size_t)t * k + i]] / sum * sh->rsf);
+            w[(size_t)t * k + i] = (i < kept) ? (float)(s[idx[(size_t)t * k + i]] / sum * sh->rsf) : 0.0f;
 
         if (margins) {
             margins[2 * t + 0] = c[idx[(size_t)t * k + k - 1]] - best_left;  /* +inf if none left */
             margins[2 * t + 1] = last_kept_g - best_dropped_g;              /* +inf if tg == G  */
         }
+        for (int i = kept; i < k; i++) idx[(size_t)t * k + i] = -1;
     next:
         free(s); free(c); free(gscore); free(gkeep); free(taken);
     }
@@ -314,7 +334,7 @@ int oracle_layer_forward(const oracle_shape *sh, const float *x, int T, const fl
     int rc = oracle_route(sh, x, T, gate_w, bias, idx, w, NULL);
     if (rc) return rc;
     for (int i = 0; i < T * k; i++)
-        if (!routed[idx[i]]) return -3;
+        if (idx[i] >= 0 && !routed[idx[i]]) return -3;
     if (sh->n_shared && !shared) return -3;
 
     int8_t *q = malloc((size_t)H);
@@ -323,9 +343,14 @@ int oracle_layer_forward(const oracle_shape *sh, const float *x, int T, const fl
     if (!q || !d || !ys || !ysh) { rc = -2; goto out; }
     for (int t = 0; t < T; t++) {
         oracle_quant_act(x + (size_t)t * H, 1, H, q, d);
-        for (int i = 0; i < k; i++)
+        for (int i = 0; i < k; i++) {
+            if (idx[(size_t)t * k + i] < 0) {  /* dropped by top-p: weight 0, nothing read */
+                memset(ys + (size_t)i * H, 0, sizeof(float) * H);
+                continue;
+            }
             if ((rc = oracle_expert_ffn(sh, routed[idx[(size_t)t * k + i]], q, d, 1,
                                         ys + (size_t)i * H, NULL, NULL))) goto out;
+        }
         if (sh->n_shared && (rc = oracle_expert_ffn(sh, shared, q, d, 1, ysh, NULL, NULL))) goto out;
         oracle_combine(sh, 1, w + (size_t)t * k, ys, sh->n_shared ? ysh : NULL, y + (size_t)t * H);
     }

@@ -37,6 +37,7 @@ typedef struct {
     int32_t n_shared;     /* 0 or 1 shared expert */
     int32_t wbits;        /* 2, 4 or 8 */
     double  rsf;          /* routed_scaling_factor */
+    double  top_p;        /* adaptive expert top-p threshold in (0, 1); 0 or >= 1: off */
 } oracle_shape;
 
 /* One expert: packed codes, row-major [rows][rows_bytes], plus fp32 per-row

@@ -69,6 +69,28 @@ __device__ bool plan_ok(const int *plan, const PlanDims &pd, int T, int E)
     return true;
 }
 
+// The pairs a plan uses: the routed slots' pairs are 0 .. R-1 (pairs are
+// numbered by (expert, token) order), the shared slot's (the last slot,
+// expert -1) start at its own first pair, T * k, which top-p can leave
+// apart from R.  Staged pair i of the (R + ns) is pair i for i < R, else
+// p0s + (i - R).
+struct PlanPairs {
+    int R, p0s, ns;
+    __device__ int operator()(int i) const { return i < R ? i : p0s + (i - R); }
+    __device__ int count() const { return R + ns; }
+};
+__device__ PlanPairs plan_pairs(const int *plan, const PlanDims &pd)
+{
+    const int S = plan[0];
+    const bool sh = S > 0 && plan[pd.o_e + S - 1] == -1;
+    PlanPairs q;
+    q.R = 0;
+    for (int u = 0; u < S - (sh ? 1 : 0); u++) q.R += plan[pd.o_n + u];
+    q.p0s = sh ? plan[pd.o_p0 + S - 1] : 0;
+    q.ns = sh ? plan[pd.o_n + S - 1] : 0;
+    return q;
+}
+
 // Builds the batch-union plan in LDS (all threads of the block take part).
 // Slots hold the union of the routed experts in ascending expert order, then
 // the shared expert; pairs of a slot list its tokens in ascending order.
@@ -91,23 +113,28 @@ __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int
         return;
     }
     if (T == 1) {
-        // one token: slots are its k experts in ascending order, then the
-        // shared expert; the pair of a slot is the slot itself
+        // one token: slots are its kept experts in ascending order, then the
+        // shared expert; the pair of a routed slot is the slot itself, the
+        // shared expert's pair is k (also when top-p keeps fewer experts)
         block_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias, s_idx, s_w, *tl);
         if (tid < k) {
             const int e = s_idx[tid];
-            int slot = 0;
-            for (int j = 0; j < k; j++) slot += (s_idx[j] < e);
-            slot_e[slot] = e;
-            slot_n[slot] = 1;
-            slot_p0[slot] = slot;
-            pair_t[slot] = 0;
-            pair_w[slot] = s_w[tid];
+            if (e >= 0) {
+                int slot = 0;
+                for (int j = 0; j < k; j++) slot += (s_idx[j] >= 0 && s_idx[j] < e);
+                slot_e[slot] = e;
+                slot_n[slot] = 1;
+                slot_p0[slot] = slot;
+                pair_t[slot] = 0;
+                pair_w[slot] = s_w[tid];
+            }
         }
         if (tid == 0) {
-            plan[0] = k + a.n_shared;
+            int kept = 0;
+            for (int j = 0; j < k; j++) kept += (s_idx[j] >= 0);
+            plan[0] = kept + a.n_shared;
             if (a.n_shared) {
-                slot_e[k] = -1; slot_n[k] = 1; slot_p0[k] = k;
+                slot_e[kept] = -1; slot_n[kept] = 1; slot_p0[kept] = k;
                 pair_t[k] = 0; pair_w[k] = 1.0f;
             }
         }
@@ -119,11 +146,12 @@ __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int
         block_topk(a.rc, a.logits + (size_t)t * a.E, a.lstride, a.lparts, a.bias, s_idx + t * k, s_w + t * k, *tl);
     for (int i = tid; i < T * k; i += nt) {
         const int e = s_idx[i];
-        atomicOr(&tokbits[i / k][e >> 5], 1u << (e & 31));
+        if (e >= 0) atomicOr(&tokbits[i / k][e >> 5], 1u << (e & 31));  // e < 0: dropped by top-p
     }
     __syncthreads();
     const int nw = (a.E + 31) >> 5;
     for (int i = tid; i < T * k; i += nt) {
+        if (s_idx[i] < 0) continue;
         const int t = i / k, e = s_idx[i], wi = e >> 5;
         const uint32_t bit = 1u << (e & 31), below = bit - 1u;
         int slot = 0, p0 = 0, n = 0, rank = 0;
@@ -384,10 +412,9 @@ __global__ __launch_bounds__(256) void k_down_rg(const GemvArgs a, const ChunkCf
     __syncthreads();
     if (!plan_ok(plan, pd, a.T, a.E)) return;
     const int S = plan[0];
-    int npairs = 0;
-    for (int u = 0; u < S; u++) npairs += plan[pd.o_n + u];
-    for (int c = tid; c < npairs * cpr; c += 256) {
-        const int p = c / cpr, pos = c - p * cpr;
+    const PlanPairs pp = plan_pairs(plan, pd);
+    for (int c = tid; c < pp.count() * cpr; c += 256) {
+        const int i = c / cpr, pos = c - i * cpr, p = pp(i);
         stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pos, la_of(p), ld_of(p), lq_of(p));
     }
     __syncthreads();
@@ -666,6 +693,7 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
     }
     const int u = v - a.n_shared;
     build_plan(a, pd, plan, s_idx, s_w, nullptr, &tl);
+    if (u >= plan[0] - a.n_shared) return;  // a slot top-p dropped (uniform in the workgroup)
     if (u == 0 && tile == 0) {
         for (int i = threadIdx.x; i < pd.words; i += kSwThreads) a.plan[i] = plan[i];
         if (a.idx_out && threadIdx.x < a.rc.k) {
@@ -783,10 +811,9 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     MOE_DS_LOAD(0, w0, s0)
     if (1 < S) MOE_DS_LOAD(1, w1, s1)
     {
-        int npairs = 0;
-        for (int u = 0; u < S; u++) npairs += plan[pd.o_n + u];
-        for (int c = tid; c < npairs * cpr; c += kDsThreads) {
-            const int p = c / cpr, pp = c - p * cpr;
+        const PlanPairs pq = plan_pairs(plan, pd);
+        for (int c = tid; c < pq.count() * cpr; c += kDsThreads) {
+            const int i = c / cpr, pp = c - i * cpr, p = pq(i);
             stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pp, la_of(p), ld_of(p), lq_of(p));
         }
         __syncthreads();

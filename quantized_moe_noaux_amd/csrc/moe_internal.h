@@ -20,7 +20,9 @@ constexpr int kGemvMaxLdsAct = 64 * 1024;
 struct RouteCfg {
     int E, G, tg, k, epl, lpg;
     float rsf;
+    float top_p;  // adaptive expert top-p; active in (0, 1)
 };
+inline bool top_p_on(const moe_shape_t &s) { return s.routed_top_p > 0.f && s.routed_top_p < 1.f; }
 
 bool route_cfg(const moe_shape_t &s, RouteCfg &rc);
 

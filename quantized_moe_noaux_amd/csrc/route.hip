@@ -21,6 +21,7 @@ bool route_cfg(const moe_shape_t &s, RouteCfg &rc)
         if (lpg & (lpg - 1)) continue;
         rc.E = E; rc.G = G; rc.tg = s.topk_group; rc.k = s.top_k;
         rc.epl = epl; rc.lpg = lpg; rc.rsf = s.routed_scaling_factor;
+        rc.top_p = top_p_on(s) ? s.routed_top_p : 0.f;
         return true;
     }
     return false;

@@ -101,7 +101,10 @@ __device__ __forceinline__ int outrank8(const uint64_t *p, int j0, uint64_t ke, 
 //      plus, per other kept group, the length of that group's run of
 //      finalists that outrank it: a group's finalists sit in outrank order,
 //      so a binary search finds the run;
-//   5. the selected s normalised to sum one, times routed_scaling_factor.
+//   5. the selected s normalised to sum one, times routed_scaling_factor;
+//      with adaptive top-p (rc.top_p in (0, 1)) only the shortest prefix of
+//      the selection whose share of the summed s reaches p is kept and
+//      renormalised, and the dropped slots read expert -1, weight 0.
 // All scores and comparisons are fp64 (order keys compare as the doubles).
 //   zt: the token's logits, as the sum of nparts slices pstride apart
 //   (added in slice order)
@@ -217,8 +220,23 @@ __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, siz
     if (tid < k) {
         double sum = 0.0;
         for (int i = 0; i < k; i++) sum += L.sel_s[i];
-        sel_e[tid] = L.sel_e[tid];
-        sel_w[tid] = (float)(L.sel_s[tid] / sum * (double)rc.rsf);
+        int kept = k;
+        if (rc.top_p > 0.f) {
+            // adaptive top-p: the shortest prefix whose share of the summed s
+            // reaches p (shares added in slot order), renormalised
+            const double p = (double)rc.top_p;
+            double cum = 0.0;
+            kept = 0;
+            while (kept < k) {
+                cum += L.sel_s[kept] / sum;
+                kept++;
+                if (cum >= p) break;
+            }
+            sum = 0.0;
+            for (int i = 0; i < kept; i++) sum += L.sel_s[i];
+        }
+        sel_e[tid] = (tid < kept) ? L.sel_e[tid] : -1;
+        sel_w[tid] = (tid < kept) ? (float)(L.sel_s[tid] / sum * (double)rc.rsf) : 0.f;
     }
     __syncthreads();
 }

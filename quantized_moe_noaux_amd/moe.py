@@ -37,7 +37,7 @@ class moe_shape_t(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
-                ("routed_scaling_factor", ctypes.c_float)]
+                ("routed_scaling_factor", ctypes.c_float), ("routed_top_p", ctypes.c_float)]
 
 
 class moe_weights_t(ctypes.Structure):
@@ -108,14 +108,15 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def shape(hidden, inter, n_experts, n_group, topk_group, top_k, n_shared, wbits, rsf):
-    return moe_shape_t(hidden, inter, n_experts, n_group, topk_group, top_k, n_shared, wbits, rsf)
+def shape(hidden, inter, n_experts, n_group, topk_group, top_k, n_shared, wbits, rsf, top_p=0.0):
+    return moe_shape_t(hidden, inter, n_experts, n_group, topk_group, top_k, n_shared, wbits, rsf, top_p)
 
 
-def shape_of(wl, rsf=None):
+def shape_of(wl, rsf=None, top_p=None):
     """moe_shape_t from an object with the workload fields (hidden, inter, ...)."""
     return shape(wl.hidden, wl.inter, wl.n_experts, wl.n_group, wl.topk_group, wl.top_k,
-                 wl.n_shared, wl.wbits, wl.rsf if rsf is None else rsf)
+                 wl.n_shared, wl.wbits, wl.rsf if rsf is None else rsf,
+                 getattr(wl, "top_p", 0.0) if top_p is None else top_p)
 
 
 def weights(w):

@@ -49,6 +49,7 @@ class Workload:
     bias_sigma: float
     layers: int = 1
     seed: int = 0
+    top_p: float = 0.0      # adaptive expert top-p (0: off)
 
     def rowbytes(self, in_dim):
         return in_dim * self.wbits // 8

@@ -77,6 +77,26 @@ def test_stage_count(m):
     assert m.moe_layer_stage_count(sh, 1, 3) < 0
 
 
+def test_top_p_shape_and_path(m):
+    # the shape struct carries routed_top_p at the end, as include/moe.h lays it out
+    assert ctypes.sizeof(m.moe_shape_t) == 9 * 4 + 4
+    sh = big_shape(m)
+    sh.routed_top_p = 0.7
+    # top-p keeps the GEMV path: AUTO does not switch to the grouped kernels
+    assert m.moe_layer_stage_count(sh, 2048) > 2 + 3 * 256
+    assert m.moe_layer_stage_count(sh, 2048, m.MOE_PATH_GROUPED) < 0
+    assert m.moe_workspace_bytes(sh, 2048, m.MOE_PATH_GROUPED) == 0
+    assert m.moe_workspace_bytes(sh, 2048) == m.moe_workspace_bytes(sh, 2048, m.MOE_PATH_GEMV)
+    assert m.moe_layer_stage_count(sh, 1) == 3
+    assert call_layer(m, sh, T=4, flags=m.MOE_PATH_GROUPED) == m.MOE_EUNSUPPORTED
+    for bad in (-0.1, float("nan")):
+        sh.routed_top_p = bad
+        assert m.moe_layer_stage_count(sh, 1) < 0
+    for off in (0.0, 1.0, 2.0):                         # off: the plain selection and paths
+        sh.routed_top_p = off
+        assert m.moe_layer_stage_count(sh, 2048) == 7
+
+
 def test_grouped_workspace(m):
     sh = big_shape(m)
     G = m.MOE_PATH_GROUPED

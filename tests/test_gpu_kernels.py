@@ -143,6 +143,23 @@ def test_route_ties_lower_index(dev, m):
     assert list(idx[0]) == [5, 6, 13, 4]
 
 
+@pytest.mark.parametrize("name,T", [("tiny", 8), ("decode_int4", 64), ("prefill_int4", 2048)])
+@pytest.mark.parametrize("p", [0.3, 0.7, 0.9])
+def test_route_top_p_bit_exact(dev, m, name, T, p):
+    wl = synth.workload(name, top_p=p)
+    L = synth.HostLayer(wl, T=T)
+    idx, w = run_route(m, dev, wl, L.x, L.gate_w, L.bias)
+    idx_ref, w_ref = oracle.route(oracle.shape_of(wl), L.x, L.gate_w, L.bias)
+    kept = (idx_ref >= 0).sum(1)
+    print("%s T=%d p=%.1f: experts kept per token %.2f (min %d, max %d)" % (name, T, p, kept.mean(), kept.min(),
+                                                                           kept.max()))
+    assert 1 <= kept.min() and kept.max() <= wl.top_k
+    if p <= 0.7:
+        assert kept.min() < wl.top_k                     # the cut drops experts here
+    assert np.array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=1e-6, atol=0)
+
+
 # ---------------------------------------------------------------- permutation
 @pytest.mark.parametrize("T,k,E,skew", [(2048, 8, 256, True), (2048, 8, 256, False), (3, 8, 256, False),
                                         (1, 1, 16, False), (0, 8, 256, False), (777, 4, 16, True)])

@@ -195,3 +195,19 @@ def test_layer_graph_replay(dev, m, name, T, path):
             _ = (x * 2).sum().item()
             assert torch.equal(y_s, y) and torch.equal(i_s, idx) and torch.equal(w_s, w), \
                 "replay %d differs from the eager call" % rep
+
+
+# ---------------------------------------------------------------- adaptive expert top-p
+@pytest.mark.parametrize("name,T,p", [("tiny", 8, 0.5), ("tiny", 5, 0.8), ("decode_int4", 1, 0.7),
+                                      ("decode_int4", 1, 0.3), ("verify_int8", 3, 0.7), ("tiny", 20, 0.6)])
+def test_layer_top_p(dev, m, name, T, p):
+    """Top-p keeps a per-token prefix of each selection: indices and weights
+    match the oracle's (dropped slots -1 / 0), the output within tolerance.
+    T = 20 runs on the GEMV path in chunks (AUTO does not take the grouped
+    kernels with top-p on)."""
+    wl = synth.workload(name, top_p=p)
+    L = DevLayer(wl, dev, T=T)
+    rel = check(m, L, T)
+    idx, _ = oracle.route(oracle.shape_of(wl), L.host.x[:T], L.host.gate_w, L.host.bias)
+    print("%s T=%d p=%.1f: experts kept per token %.2f, max rel err %.3g" %
+          (name, T, p, (idx >= 0).sum(1).mean(), rel))

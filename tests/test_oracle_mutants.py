@@ -26,7 +26,10 @@ DOTS = [pins.test_code_layout_by_hand] + \
 LAYER = [pins.test_single_expert_layer_is_dense_swiglu, pins.test_layer_linear_in_rsf_and_shared_alone,
          pins.test_layer_equals_sum_of_experts]
 MISC = [pins.test_rmsnorm_closed_forms, pins.test_permute_is_stable_sort]
-ALL = ROUTE + QUANT + DOTS + LAYER + MISC
+TOPP = [lambda: pins.test_top_p_keeps_the_shortest_prefix_reaching_p(0.7), pins.test_top_p_off_and_single_expert,
+        pins.test_top_p_boundary_is_inclusive, pins.test_top_p_follows_selection_order_not_weight,
+        pins.test_top_p_layer_with_one_expert_per_token]
+ALL = ROUTE + QUANT + DOTS + LAYER + MISC + TOPP
 
 MUTANTS = {
     "group score = max only": ("gscore[g] = (m >= 2) ? b1 + b2 : b1;", "gscore[g] = b1;"),
@@ -54,6 +57,11 @@ MUTANTS = {
     "shared scaled by rsf": ("if (y_shared) acc += (double)y_shared[(size_t)t * H + r];",
                              "if (y_shared) acc += sh->rsf * (double)y_shared[(size_t)t * H + r];"),
     "rmsnorm eps outside sqrt": ("sqrt(ss / H + eps)", "(sqrt(ss / H) + eps)"),
+    "top-p boundary exclusive": ("if (cum >= sh->top_p) break;", "if (cum > sh->top_p) break;"),
+    "top-p not renormalised": ("            sum = 0.0;\n            for (int i = 0; i < kept; i++)",
+                               "            for (int i = 0; i < kept; i++) if (0)"),
+    "top-p counts one short": ("                kept++;\n                if (cum >= sh->top_p) break;",
+                               "                if (cum >= sh->top_p) break;\n                kept++;"),
     "permute not stable": ("int row = fill[idx[a]]++;",
                            "int row = off[idx[a]] + off[idx[a] + 1] - 1 - fill[idx[a]]++;"),
 }

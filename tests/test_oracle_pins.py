@@ -160,6 +160,96 @@ def test_route_weights_use_unbiased_scores():
         np.testing.assert_allclose(w[t], ss / ss.sum() * 2.5, rtol=2e-7)
 
 
+# ---------------------------------------------------------------- adaptive expert top-p
+def _with_p(sh, p):
+    sh.top_p = float(np.float32(p))
+    return sh
+
+
+@pytest.mark.parametrize("p", [0.25, 0.5, 0.7, 0.9])
+def test_top_p_keeps_the_shortest_prefix_reaching_p(p):
+    rng = np.random.default_rng(int(p * 100))
+    E, G, tg, k, H, T = 32, 8, 3, 6, 64, 60
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((E, H)) / math.sqrt(H)).astype(np.float32)
+    b = (0.3 * rng.standard_normal(E)).astype(np.float32)
+    i0, w0 = oracle.route(mkshape(E, G, tg, k, H=H), x, W, b)
+    i1, w1 = oracle.route(_with_p(mkshape(E, G, tg, k, H=H), p), x, W, b)
+    counts = []
+    for t in range(T):
+        n = int((i1[t] >= 0).sum())
+        counts.append(n)
+        assert 1 <= n <= k
+        assert list(i1[t][:n]) == list(i0[t][:n])          # a prefix of the selection, in order
+        assert np.all(i1[t][n:] == -1) and np.all(w1[t][n:] == 0)
+        assert abs(float(w1[t].astype(np.float64).sum()) - 2.5) <= 2.5e-6   # renormalised
+        np.testing.assert_allclose(w1[t][:n] / w1[t][0], w0[t][:n] / w0[t][0], rtol=1e-6)
+        share = np.cumsum(w0[t].astype(np.float64)) / float(w0[t].astype(np.float64).sum())
+        if n > 1:
+            assert share[n - 2] < p + 1e-6                   # one fewer does not reach p
+        assert share[n - 1] >= p - 1e-6                      # n does
+    assert len(set(counts)) > 1                              # the cut adapts per token
+
+
+def test_top_p_off_and_single_expert():
+    rng = np.random.default_rng(5)
+    E, H, T = 16, 64, 20
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((E, H)) / 8).astype(np.float32)
+    b = (0.2 * rng.standard_normal(E)).astype(np.float32)
+    i0, w0 = oracle.route(mkshape(E, 4, 2, 4, H=H), x, W, b)
+    for p in (0.0, 1.0, 1.5):                                # off: the plain selection
+        i1, w1 = oracle.route(_with_p(mkshape(E, 4, 2, 4, H=H), p), x, W, b)
+        assert np.array_equal(i1, i0) and np.array_equal(w1, w0)
+    i1, w1 = oracle.route(_with_p(mkshape(E, 4, 2, 4, H=H), 1e-7), x, W, b)
+    assert np.array_equal(i1[:, 0], i0[:, 0]) and np.all(i1[:, 1:] == -1)
+    assert np.all(w1[:, 0] == np.float32(2.5)) and np.all(w1[:, 1:] == 0)
+
+
+def test_top_p_boundary_is_inclusive():
+    # four equal scores in the kept group: every share is exactly 1/4, so
+    # p = 1/2 is reached with two experts and p = 3/4 with three
+    c = [0.8] * 4 + [0.1] * 4
+    for p, n in ((0.5, 2), (0.75, 3), (0.5000001, 3)):
+        E = len(c)
+        sh = _with_p(mkshape(E, 2, 1, 4, H=32, rsf=1.0), p)
+        x = np.ones((1, 32), np.float32)
+        W = np.zeros((E, 32), np.float32)
+        idx, w = oracle.route(sh, x, W, np.asarray(c, np.float32) - np.float32(0.5))
+        assert list(idx[0]) == [0, 1, 2, 3][:n] + [-1] * (4 - n)
+        np.testing.assert_allclose(w[0][:n], [1.0 / n] * n, rtol=1e-7)
+
+
+def test_top_p_follows_selection_order_not_weight():
+    # the bias ranks the experts by c as 2, 1, 0 while their weights (from the
+    # unbiased s) rank 0, 1, 2; the prefix is taken in selection order
+    z = np.array([2.0, 0.0, -2.0, -5.0])
+    E, H = 4, 32
+    x = np.ones((1, H), np.float32)
+    W = np.repeat((z / H)[:, None], H, 1).astype(np.float32)
+    b = np.array([0.0, 0.5, 1.0, 0.0], np.float32)
+    idx, w = oracle.route(_with_p(mkshape(E, 1, 1, 3, H=H, rsf=1.0), 0.3), x, W, b)
+    s = 1 / (1 + np.exp(-z))
+    assert list(idx[0]) == [2, 1, -1]                        # shares 0.08, then 0.41 >= 0.3
+    np.testing.assert_allclose(w[0][:2], s[[2, 1]] / s[[2, 1]].sum(), rtol=1e-6)
+
+
+def test_top_p_layer_with_one_expert_per_token():
+    # p tiny: each token keeps its first expert at weight rsf, so the layer is
+    # rsf * FFN_first(x) + FFN_shared(x)
+    wl = synth.workload("tiny")
+    L, sh = _tiny_layer(wl)
+    sh = _with_p(sh, 1e-7)
+    idx, w = oracle.route(sh, L.x, L.gate_w, L.bias)
+    assert np.all(idx[:, 1:] == -1)
+    y, _, _ = oracle.layer_forward(sh, L.x, L.gate_w, L.bias, oracle.layer_experts(L, idx), L.shared)
+    q, d = oracle.quant_act(L.x)
+    for t in range(wl.T):
+        ref = oracle.expert_ffn(sh, L.shared, q[t:t + 1], d[t:t + 1]).astype(np.float64)[0] + \
+            wl.rsf * oracle.expert_ffn(sh, L.expert(idx[t, 0]), q[t:t + 1], d[t:t + 1]).astype(np.float64)[0]
+        np.testing.assert_allclose(y[t], ref, rtol=0, atol=1e-5 * np.abs(ref).max())
+
+
 def test_route_rejects_bad_shapes():
     x = np.zeros((1, 32), np.float32)
     with pytest.raises(ValueError):
