@@ -67,8 +67,8 @@ typedef struct {
      * slot order in fp64), and renormalises the kept weights to sum to
      * routed_scaling_factor; a dropped slot reports expert -1 and weight 0
      * and its expert is not read.  0 or >= 1: off (every selected expert is
-     * kept).  The grouped path does not take it: with top-p on, MOE_PATH_AUTO
-     * stays on the GEMV path and MOE_PATH_GROUPED is MOE_EUNSUPPORTED. */
+     * kept).  Both paths take it: the grouped path's permutation gives a
+     * dropped assignment no row. */
     float   routed_top_p;
 } moe_shape_t;
 
@@ -233,7 +233,9 @@ size_t moe_stack_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t f
  *   perm [T*k]  out: perm[row] = a, ascending a within each expert
  *   inv  [T*k]  out: inv[a] = row
  * ws: at least moe_permute_workspace_bytes(T, k, E) bytes, 256-byte aligned.
- * idx entries must lie in [0, E). */
+ * idx entries lie in [0, E), or are -1 for an assignment adaptive top-p
+ * dropped: it gets no row and inv = -1, and rows 0 .. off[E]-1 hold the
+ * kept assignments (any other value is treated as -1). */
 int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *perm,
                 int32_t *off, int32_t *inv, void *ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E);

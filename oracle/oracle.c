@@ -382,6 +382,8 @@ void oracle_rmsnorm(const float *x, const float *g, double eps, int T, int H, fl
  * Assignment a = t*k + i routes token t to expert idx[a].  Rows are grouped
  * by expert: off[e] .. off[e+1]-1 hold the assignments of expert e in
  * ascending a (a counting sort, stable); perm[row] = a, inv[a] = row.
+ * reading: an assignment adaptive top-p dropped (expert -1) gets no row and
+ *   inv = -1; rows 0 .. off[E]-1 hold the kept ones.
  */
 int oracle_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32_t *off,
                    int32_t *inv)
@@ -389,6 +391,7 @@ int oracle_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32
     const int n = T * k;
     for (int e = 0; e <= E; e++) off[e] = 0;
     for (int a = 0; a < n; a++) {
+        if (idx[a] == -1) continue;                 /* dropped by top-p: no row */
         if (idx[a] < 0 || idx[a] >= E) return -1;
         off[idx[a] + 1]++;
     }
@@ -397,6 +400,7 @@ int oracle_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32
     if (!fill) return -2;
     for (int e = 0; e < E; e++) fill[e] = off[e];
     for (int a = 0; a < n; a++) {
+        if (idx[a] < 0) { inv[a] = -1; continue; }
         int row = fill[idx[a]]++;
         perm[row] = a;
         inv[a] = row;

@@ -69,7 +69,7 @@ bool use_grouped(const moe_shape_t &s, int T, uint32_t flags)
     const uint32_t path = flags & 3u;
     if (path == MOE_PATH_GROUPED) return true;
     if (path == MOE_PATH_GEMV) return false;
-    return T > kGemvMaxT && gg_shape_ok(s) && !top_p_on(s);
+    return T > kGemvMaxT && gg_shape_ok(s);
 }
 
 // moe_layer_forward on the expert-grouped path (arguments already checked)
@@ -190,8 +190,7 @@ int moe_block_dots(int32_t wbits, const uint8_t *codes, int32_t rows, int32_t D,
 size_t moe_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags)
 {
     if (check_shape(shape) || T < 0 || (flags & 3u) == 3u) return 0;
-    if (use_grouped(*shape, T, flags))
-        return (gg_shape_ok(*shape) && !top_p_on(*shape)) ? gg_ws(*shape, T > 0 ? T : 1).total : 0;
+    if (use_grouped(*shape, T, flags)) return gg_shape_ok(*shape) ? gg_ws(*shape, T > 0 ? T : 1).total : 0;
     const int Tc = gemv_chunk_tokens(*shape, T > 0 ? T : 1);
     if (!Tc) return 0;
     return gemv_ws(*shape, T, Tc, false).total;
@@ -202,8 +201,7 @@ int moe_layer_stage_count(const moe_shape_t *shape, int32_t T, uint32_t flags)
     if (check_shape(shape) || T < 0) return -MOE_EINVAL;
     if (T == 0) return 0;
     if ((flags & 3u) == 3u) return -MOE_EINVAL;
-    if (use_grouped(*shape, T, flags))
-        return (gg_shape_ok(*shape) && !top_p_on(*shape)) ? kGgStages : -MOE_EUNSUPPORTED;
+    if (use_grouped(*shape, T, flags)) return gg_shape_ok(*shape) ? kGgStages : -MOE_EUNSUPPORTED;
     const int Tc = gemv_chunk_tokens(*shape, T);
     if (!Tc) return -MOE_EUNSUPPORTED;
     return gemv_stage_count(*shape, T, Tc);
@@ -261,7 +259,7 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
     if (flags & ~(3u | MOE_ACCUMULATE | MOE_STAGE_MASK)) return MOE_EINVAL;
     const uint32_t path = flags & 3u;
     if (path == 3u) return MOE_EINVAL;
-    if (path == MOE_PATH_GROUPED && (!gg_shape_ok(*shape) || top_p_on(*shape))) return MOE_EUNSUPPORTED;
+    if (path == MOE_PATH_GROUPED && !gg_shape_ok(*shape)) return MOE_EUNSUPPORTED;
     if (T == 0) return MOE_OK;
     if (!x || !gate_w || !bias || !y || !ws) return MOE_EINVAL;
     if ((idx_out == nullptr) != (w_out == nullptr)) return MOE_EINVAL;

@@ -429,11 +429,20 @@ __global__ __launch_bounds__(kGgThreads) void k_gg_down(const GgArgs a)
 __global__ __launch_bounds__(256) void k_gg_combine(const GgArgs a)
 {
     __shared__ int rows[kMaxTopK + 1];
+    __shared__ int nr;
     const int t = blockIdx.x, k = a.k, H = a.H;
-    if ((int)threadIdx.x < k) rows[threadIdx.x] = a.inv[(size_t)t * k + threadIdx.x];
-    if (threadIdx.x == 0) rows[k] = a.n_shared ? a.Tk + t : -1;
+    if (threadIdx.x == 0) {
+        // the token's kept slots in slot order (adaptive top-p leaves a
+        // prefix; a dropped slot has no row), then its shared row
+        int c = 0;
+        for (int i = 0; i < k; i++) {
+            const int r = a.inv[(size_t)t * k + i];
+            if (r >= 0) rows[c++] = r;
+        }
+        if (a.n_shared) rows[c++] = a.Tk + t;
+        nr = c;
+    }
     __syncthreads();
-    const int nr = a.n_shared ? k + 1 : k;
     float *out = a.y + (size_t)t * H;
     if (((uintptr_t)out & 15) == 0) {
         for (int c = threadIdx.x; c < H / 4; c += 256) {

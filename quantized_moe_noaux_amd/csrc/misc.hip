@@ -128,6 +128,8 @@ int launch_block_dots(int wbits, const uint8_t *codes, int rows, int D, const in
 //                tile list
 //  k_perm_place  each assignment's row = off[e] + its tile's start + the
 //                number of earlier assignments of the same expert in its tile
+// An assignment of expert -1 (dropped by adaptive top-p) gets no row and
+// inv = -1; the kept ones fill rows 0 .. off[E]-1.
 __global__ __launch_bounds__(256) void k_perm_count(const int32_t *__restrict__ idx, int n, int E,
                                                     int32_t *__restrict__ cnt /*[tiles][E]*/)
 {
@@ -135,7 +137,10 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t *__restrict__ 
     for (int e = threadIdx.x; e < E; e += 256) c[e] = 0;
     __syncthreads();
     const int a = blockIdx.x * 256 + threadIdx.x;
-    if (a < n) atomicAdd(&c[idx[a]], 1);
+    if (a < n) {
+        const int e = idx[a];
+        if (e >= 0 && e < E) atomicAdd(&c[e], 1);  // e = -1: dropped by top-p, no row
+    }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256) cnt[(size_t)blockIdx.x * E + e] = c[e];
 }
@@ -211,6 +216,10 @@ __global__ __launch_bounds__(256) void k_perm_place(const int32_t *__restrict__ 
     __syncthreads();
     if (a >= n) return;
     const int e = s_e[threadIdx.x];
+    if (e < 0 || e >= E) {  // dropped by top-p: no row
+        inv[a] = -1;
+        return;
+    }
     int r = 0;
     for (int j = 0; j < (int)threadIdx.x; j++) r += (s_e[j] == e);
     const int row = off[e] + base[(size_t)blockIdx.x * E + e] + r;

@@ -150,3 +150,21 @@ def test_prefill_sampled_tokens(dev, m, prefill):
     assert np.array_equal(idx[rows], idx_ref)
     rel = assert_close(y.cpu().numpy()[rows], y_ref)
     print("prefill sampled rows: max rel err %.3g" % rel)
+
+
+# ---------------------------------------------------------------- adaptive expert top-p
+@pytest.mark.parametrize("wbits,T,p", [(4, 100, 0.6), (8, 40, 0.8), (2, 70, 0.5)])
+def test_grouped_top_p(dev, m, wbits, T, p):
+    """Top-p on the grouped path: the permutation gives dropped slots no row
+    and the combine skips them; indices, weights and outputs match the
+    oracle, and the GEMV path's routing bit for bit."""
+    wl = synth.workload("tiny", wbits=wbits, top_p=p)
+    L = DevLayer(wl, dev, T=T)
+    y, idx, w = forward(m, L, m.MOE_PATH_GROUPED, T)
+    y_ref, idx_ref, w_ref = reference(L, np.arange(T))
+    assert (idx_ref < 0).any()
+    assert np.array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=1e-6)
+    assert_close(y.cpu().numpy(), y_ref)
+    yg, idxg, _ = forward(m, L, m.MOE_PATH_GEMV, T)
+    assert np.array_equal(idxg, idx)

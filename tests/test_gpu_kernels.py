@@ -179,6 +179,28 @@ def test_permute_bit_exact(dev, m, T, k, E, skew):
     assert np.array_equal(inv.cpu().numpy(), inv_ref.reshape(-1))
 
 
+@pytest.mark.parametrize("T,k,E", [(2048, 8, 256), (37, 4, 16)])
+def test_permute_with_dropped_slots(dev, m, T, k, E):
+    # adaptive top-p leaves a per-token prefix; the dropped slots (-1) get no row
+    rng = np.random.default_rng(T + E)
+    idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)], np.int32).reshape(T, k)
+    kept = rng.integers(1, k + 1, T)
+    for t in range(T):
+        idx[t, kept[t]:] = -1
+    perm = torch.full((T * k,), -7, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ws = m.workspace(m.moe_permute_workspace_bytes(T, k, E), dev)
+    m.moe_permute(to_dev(idx, dev), E, perm, off, inv, ws)
+    torch.cuda.synchronize()
+    perm_ref, off_ref, inv_ref = oracle.permute(idx, E)
+    R = int(off_ref[E])
+    assert R == int(kept.sum())
+    assert np.array_equal(off.cpu().numpy(), off_ref)
+    assert np.array_equal(perm.cpu().numpy()[:R], perm_ref[:R])
+    assert np.array_equal(inv.cpu().numpy(), inv_ref.reshape(-1))
+
+
 # ---------------------------------------------------------------- rmsnorm
 @pytest.mark.parametrize("T,H", [(1, 6144), (5, 256), (3, 100)])
 def test_rmsnorm(dev, m, T, H):

@@ -25,7 +25,7 @@ DOTS = [pins.test_code_layout_by_hand] + \
        [lambda b=b: pins.test_matvec_equals_dequantised_matmul(b) for b in (2, 4, 8)]
 LAYER = [pins.test_single_expert_layer_is_dense_swiglu, pins.test_layer_linear_in_rsf_and_shared_alone,
          pins.test_layer_equals_sum_of_experts]
-MISC = [pins.test_rmsnorm_closed_forms, pins.test_permute_is_stable_sort]
+MISC = [pins.test_rmsnorm_closed_forms, pins.test_permute_is_stable_sort, pins.test_permute_skips_dropped_assignments]
 TOPP = [lambda: pins.test_top_p_keeps_the_shortest_prefix_reaching_p(0.7), pins.test_top_p_off_and_single_expert,
         pins.test_top_p_boundary_is_inclusive, pins.test_top_p_follows_selection_order_not_weight,
         pins.test_top_p_layer_with_one_expert_per_token]
@@ -62,6 +62,8 @@ MUTANTS = {
                                "            for (int i = 0; i < kept; i++) if (0)"),
     "top-p counts one short": ("                kept++;\n                if (cum >= sh->top_p) break;",
                                "                if (cum >= sh->top_p) break;\n                kept++;"),
+    "permute keeps dropped": ("        if (idx[a] == -1) continue;                 /* dropped by top-p: no row */\n",
+                              "        if (idx[a] == -1) { off[1]++; continue; }\n"),
     "permute not stable": ("int row = fill[idx[a]]++;",
                            "int row = off[idx[a]] + off[idx[a] + 1] - 1 - fill[idx[a]]++;"),
 }

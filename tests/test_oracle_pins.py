@@ -437,6 +437,24 @@ def test_rmsnorm_closed_forms():
     np.testing.assert_allclose(o, v / np.sqrt(ms + 1e-6), rtol=1e-7)
 
 
+def test_permute_skips_dropped_assignments():
+    # top-p leaves a per-token prefix; the dropped slots (-1) get no row
+    rng = np.random.default_rng(9)
+    T, k, E = 40, 6, 16
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    kept = rng.integers(1, k + 1, T)
+    for t in range(T):
+        idx[t, kept[t]:] = -1
+    perm, off, inv = oracle.permute(idx, E)
+    flat = idx.reshape(-1)
+    live = [a for a in range(T * k) if flat[a] >= 0]
+    R = len(live)
+    assert off[E] == R == kept.sum()
+    assert list(perm[:R]) == sorted(live, key=lambda a: flat[a])
+    assert np.all(inv.reshape(-1)[flat < 0] == -1)
+    assert np.array_equal(perm[inv.reshape(-1)[flat >= 0]], np.array(live))
+
+
 def test_permute_is_stable_sort():
     rng = np.random.default_rng(5)
     T, k, E = 50, 4, 12
