@@ -99,8 +99,10 @@ __device__ PlanPairs plan_pairs(const int *plan, const PlanDims &pd)
 //   first pair(e) = number of (token, expert) selections with expert below e
 //   pair of (t,e) = first pair(e) + number of tokens before t selecting e
 // tokbits: LDS scratch of kGemvMaxT x 16 words.
+// tl: ntl selection scratch sets; with ntl > 1 (and 256 * ntl threads)
+// groups of 256 threads route ntl tokens at once.
 __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int *s_idx, float *s_w,
-                           uint32_t (*tokbits)[16], TopkLds *tl)
+                           uint32_t (*tokbits)[16], TopkLds *tl, int ntl = 1)
 {
     const int tid = threadIdx.x, nt = blockDim.x, T = a.T, k = a.rc.k;
     int *slot_e = plan + pd.o_e, *slot_n = plan + pd.o_n, *slot_p0 = plan + pd.o_p0;
@@ -142,8 +144,21 @@ __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int
         return;
     }
     for (int i = tid; i < T * 16; i += nt) tokbits[i >> 4][i & 15] = 0u;
-    for (int t = 0; t < T; t++)
-        block_topk(a.rc, a.logits + (size_t)t * a.E, a.lstride, a.lparts, a.bias, s_idx + t * k, s_w + t * k, *tl);
+    {
+        // ng groups of 256 threads route ng tokens per round; a group
+        // without a token in the last round routes that round's first token
+        // again into its own spare outputs (the rounds stay uniform)
+        const int ng = (ntl > 1 && nt >= 256 * ntl) ? ntl : 1;
+        const int gs = nt / ng, g = tid / gs;
+        __shared__ int spare_e[4][kMaxTopK];
+        __shared__ float spare_w[4][kMaxTopK];
+        for (int t0 = 0; t0 < T; t0 += ng) {
+            const int t = t0 + g, tr = (t < T) ? t : t0;
+            block_topk(a.rc, a.logits + (size_t)tr * a.E, a.lstride, a.lparts, a.bias,
+                       (t < T) ? s_idx + t * k : spare_e[g & 3], (t < T) ? s_w + t * k : spare_w[g & 3], tl[g],
+                       tid - g * gs, gs);
+        }
+    }
     for (int i = tid; i < T * k; i += nt) {
         const int e = s_idx[i];
         if (e >= 0) atomicOr(&tokbits[i / k][e >> 5], 1u << (e & 31));  // e < 0: dropped by top-p
@@ -197,24 +212,27 @@ __device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int
 // routing, when asked): for several tokens, measured on MI355X, one such
 // launch costs less than every gate/up workgroup re-deriving the union plan,
 // or than cross-workgroup signalling through a shared atomic counter.
-__global__ __launch_bounds__(256) void k_plan(const GemvArgs a, const PlanDims pd)
+// Four groups of 256 threads route four tokens at a time (each selection is
+// a chain of dependent steps; ~4 us per token on MI355X).
+constexpr int kPlanGroups = 4;
+__global__ __launch_bounds__(256 * kPlanGroups) void k_plan(const GemvArgs a, const PlanDims pd)
 {
     __shared__ int plan[1 + 3 * (kGemvMaxT * kMaxTopK + 1) + 2 * kGemvMaxT * (kMaxTopK + 1)];
     __shared__ int s_idx[kGemvMaxT * kMaxTopK];
     __shared__ float s_w[kGemvMaxT * kMaxTopK];
     __shared__ uint32_t tokbits[kGemvMaxT][16];
-    __shared__ TopkLds tl;
-    build_plan(a, pd, plan, s_idx, s_w, tokbits, &tl);
-    const int tid = threadIdx.x;
-    for (int i = tid; i < pd.words; i += 256) a.plan[i] = plan[i];
+    __shared__ TopkLds tl[kPlanGroups];
+    build_plan(a, pd, plan, s_idx, s_w, tokbits, tl, kPlanGroups);
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int i = tid; i < pd.words; i += nt) a.plan[i] = plan[i];
     if (a.logits && a.idx_out)
-        for (int i = tid; i < a.T * a.rc.k; i += 256) { a.idx_out[i] = s_idx[i]; a.w_out[i] = s_w[i]; }
+        for (int i = tid; i < a.T * a.rc.k; i += nt) { a.idx_out[i] = s_idx[i]; a.w_out[i] = s_w[i]; }
 }
 
 int launch_plan(const GemvArgs &a, hipStream_t st)
 {
     const PlanDims pd = plan_dims(a.T, a.rc.k, a.n_shared, a.logits == nullptr);
-    k_plan<<<1, 256, 0, st>>>(a, pd);
+    k_plan<<<1, 256 * kPlanGroups, 0, st>>>(a, pd);
     return (int)hipGetLastError();
 }
 

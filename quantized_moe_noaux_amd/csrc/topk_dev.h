@@ -81,7 +81,7 @@ __device__ __forceinline__ int outrank8(const uint64_t *p, int j0, uint64_t ke, 
 }
 
 // Block-wide noaux_tc routing of one token (every thread of the block calls
-// it; blockDim.x >= 64).  Every phase spreads its work over many lanes with
+// it; nt >= 64 threads take part).  Every phase spreads its work over many lanes with
 // independent loads: on MI355X a dependent LDS or cross-lane round trip costs
 // ~100 cycles, so serial chains, not arithmetic, set the latency of this step.
 //   1. s, c = s + bias and the order key of c for every expert (all logit
@@ -108,10 +108,15 @@ __device__ __forceinline__ int outrank8(const uint64_t *p, int j0, uint64_t ke, 
 // All scores and comparisons are fp64 (order keys compare as the doubles).
 //   zt: the token's logits, as the sum of nparts slices pstride apart
 //   (added in slice order)
+//   tid, nt: this thread's index among the nt threads (a multiple of 64)
+//   that route this token; several groups of a workgroup may route
+//   different tokens at once, each with its own L, since the barriers are
+//   workgroup-wide and every group passes the same ones.
 __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, size_t pstride, int nparts,
-                           const float *__restrict__ bias, int *sel_e, float *sel_w, TopkLds &L)
+                           const float *__restrict__ bias, int *sel_e, float *sel_w, TopkLds &L, int tid,
+                           int nt)
 {
-    const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id();
+    const int lane = lane_id();
     const int E = rc.E, G = rc.G, m = E / G, k = rc.k;
     const int mpad = (m + 7) & ~7;
     for (int e0 = 0; e0 < E; e0 += 2 * nt) {
@@ -239,6 +244,14 @@ __device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, siz
         sel_w[tid] = (tid < kept) ? (float)(L.sel_s[tid] / sum * (double)rc.rsf) : 0.f;
     }
     __syncthreads();
+}
+
+// the whole workgroup routes one token
+__device__ __forceinline__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, size_t pstride,
+                                           int nparts, const float *__restrict__ bias, int *sel_e, float *sel_w,
+                                           TopkLds &L)
+{
+    block_topk(rc, zt, pstride, nparts, bias, sel_e, sel_w, L, threadIdx.x, blockDim.x);
 }
 
 } // namespace moe
