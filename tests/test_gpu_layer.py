@@ -211,3 +211,17 @@ def test_layer_top_p(dev, m, name, T, p):
     idx, _ = oracle.route(oracle.shape_of(wl), L.host.x[:T], L.host.gate_w, L.host.bias)
     print("%s T=%d p=%.1f: experts kept per token %.2f, max rel err %.3g" %
           (name, T, p, (idx >= 0).sum(1).mean(), rel))
+
+
+# ---------------------------------------------------------------- largest shapes the ABI takes
+@pytest.mark.parametrize("E,G,tg,k,T,path", [(512, 8, 4, 32, 1, "gemv"), (512, 8, 4, 32, 8, "gemv"),
+                                             (512, 64, 8, 32, 5, "gemv"), (512, 64, 8, 32, 40, "grouped"),
+                                             (512, 8, 4, 32, 100, "grouped")])
+def test_largest_routing_shapes(dev, m, E, G, tg, k, T, path):
+    """E = 512 experts, up to G = 64 groups, top_k = 32: the plan holds up to
+    8 * 32 + 1 slots; both paths match the oracle."""
+    wl = synth.workload("tiny", n_experts=E, n_group=G, topk_group=tg, top_k=k)
+    L = DevLayer(wl, dev, T=T)
+    flags = m.MOE_PATH_GROUPED if path == "grouped" else m.MOE_PATH_GEMV
+    rel = check(m, L, T, flags)
+    print("E=%d G=%d tg=%d k=%d T=%d %s: max rel err %.3g" % (E, G, tg, k, T, path, rel))
