@@ -58,7 +58,7 @@ GemvWs gemv_ws(const moe_shape_t &s, int T, int Tc, bool single)
 
 // Range check of a plan read back from the workspace: every slot names a
 // valid expert (or -1 = shared) and its pairs stay inside the buffers.
-__device__ bool plan_ok(const int *plan, const PlanDims &pd, int T, int E)
+__device__ __forceinline__ bool plan_ok(const int *plan, const PlanDims &pd, int T, int E)
 {
     const int S = plan[0];
     if (S < 0 || S > pd.S) return false;
@@ -79,7 +79,7 @@ struct PlanPairs {
     __device__ int operator()(int i) const { return i < R ? i : p0s + (i - R); }
     __device__ int count() const { return R + ns; }
 };
-__device__ PlanPairs plan_pairs(const int *plan, const PlanDims &pd)
+__device__ __forceinline__ PlanPairs plan_pairs(const int *plan, const PlanDims &pd)
 {
     const int S = plan[0];
     const bool sh = S > 0 && plan[pd.o_e + S - 1] == -1;
@@ -101,7 +101,7 @@ __device__ PlanPairs plan_pairs(const int *plan, const PlanDims &pd)
 // tokbits: LDS scratch of kGemvMaxT x 16 words.
 // tl: ntl selection scratch sets; with ntl > 1 (and 256 * ntl threads)
 // groups of 256 threads route ntl tokens at once.
-__device__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int *s_idx, float *s_w,
+__device__ __forceinline__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int *s_idx, float *s_w,
                            uint32_t (*tokbits)[16], TopkLds *tl, int ntl = 1)
 {
     const int tid = threadIdx.x, nt = blockDim.x, T = a.T, k = a.rc.k;
@@ -245,17 +245,19 @@ template <> struct ActShape<8> { static constexpr int NA = 4; };
 template <> struct ActShape<4> { static constexpr int NA = 8; };
 template <> struct ActShape<2> { static constexpr int NA = 16; };
 
+// chunks per thread staged in one batch of loads by the down kernel (one
+// token's pairs fit one batch at the production shapes)
+constexpr int stage_batch(int wb) { return wb == 8 ? 5 : wb == 4 ? 3 : 2; }
+
 template <int WB>
-__device__ __forceinline__ void stage_act(const int8_t *q, const float *d, int pos, uint32_t *la, float *ld, int *lq)
+__device__ __forceinline__ void store_act(const Act<WB> &A, int pos, uint32_t *la, float *ld, int *lq)
 {
-    Act<WB> A;
-    A.load(q, d, pos);
     uint4 *dst = reinterpret_cast<uint4 *>(la + pos * ActShape<WB>::NA);
 #pragma unroll
     for (int i = 0; i < ActShape<WB>::NA / 4; i++)
         dst[i] = make_uint4(A.a[4 * i], A.a[4 * i + 1], A.a[4 * i + 2], A.a[4 * i + 3]);
     if constexpr (WB == 8) {
-        if ((pos & 1) == 0) ld[pos >> 1] = A.d;
+        ld[pos >> 1] = A.d;  // both chunks of a block store the block's scale
     } else if constexpr (WB == 4) {
         ld[pos] = A.d;
         lq[pos] = A.qs;
@@ -263,6 +265,14 @@ __device__ __forceinline__ void stage_act(const int8_t *q, const float *d, int p
         ld[2 * pos] = A.d0; ld[2 * pos + 1] = A.d1;
         lq[2 * pos] = A.qs0; lq[2 * pos + 1] = A.qs1;
     }
+}
+
+template <int WB>
+__device__ __forceinline__ void stage_act(const int8_t *q, const float *d, int pos, uint32_t *la, float *ld, int *lq)
+{
+    Act<WB> A;
+    A.load(q, d, pos);
+    store_act<WB>(A, pos, la, ld, lq);
 }
 
 template <int WB>
@@ -752,9 +762,13 @@ constexpr int kDsThreads = 256;  // down row-sweep block
 constexpr int kDsGroups = kDsThreads / 32;
 constexpr int kDsRows = 16;      // output rows per workgroup
 
+// slots of down rows in flight ahead of use, plus the one in use
+constexpr int down_ring(int wb, int tt) { return 3; }
+constexpr bool kStageFirst = true;
+
 // down/combine: a step reads RPS consecutive down rows of one slot (4 KB);
 // kDsRows rows per workgroup, every slot in turn, prefetching the next slot.
-template <int WB, int RPS, int TT>
+template <int WB, int RPS, int TT, int NB>
 __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -772,15 +786,18 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
 
     for (int i = tid; i < pd.words; i += kDsThreads) plan[i] = a.plan[i];
     __syncthreads();
-    if (!plan_ok(plan, pd, a.T, a.E)) return;
+    if (!plan_ok(plan, pd, a.T, a.E) || plan[0] < 1) return;
     const int S = plan[0];
 
     const int rowoff = tid / cpr, pos = tid % cpr, grp = tid >> 5;
     const int row_base = blockIdx.x * kDsRows;
     const size_t rowbytes = (size_t)cpr * 16;
     const size_t step_bytes = (size_t)kDsThreads * 16;
+    // the slot's base addresses are workgroup-uniform (scalar registers): the
+    // loads then take a fixed per-lane offset, and no vector register of a
+    // load still in flight is reused for the next slot's addresses
     auto slot_src = [&](int u, const float *&ds) {
-        const int e = plan[pd.o_e + u];
+        const int e = __builtin_amdgcn_readfirstlane(plan[pd.o_e + u]);
         const moe_weights_t &W = (e >= 0) ? a.routed : a.shared;
         const int ee = (e >= 0) ? e : 0;
         ds = W.down_s + (size_t)ee * a.H + row_base + rowoff;
@@ -792,64 +809,88 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
 #pragma unroll
         for (int j = 0; j < NSTEP; j++) acc[tt][j] = 0.f;
 
-    // statically named slot buffers (no pointers to register arrays, so
-    // nothing is demoted to scratch)
-    uint4 w0[NSTEP], w1[NSTEP], w2[NSTEP];
-    float s0[NSTEP], s1[NSTEP], s2[NSTEP];
-#define MOE_DS_LOAD(U, WB_, SB_)                                                  \
-    {                                                                             \
-        const float *ds_;                                                         \
-        const uint8_t *src_ = slot_src((U), ds_);                                 \
-        _Pragma("unroll") for (int j = 0; j < NSTEP; j++) {                       \
-            WB_[j] = ld16(src_ + j * step_bytes);                                 \
-            SB_[j] = ds_[j * RPS];                                                \
-        }                                                                         \
-    }
-/* a slot's pairs list its tokens in ascending order: walk the tokens in  \
-   compile-time order so every accumulator index is static */                   \
-#define MOE_DS_USE(U, WB_, SB_)                                                   \
-    {                                                                             \
-        const int n_ = plan[pd.o_n + (U)], p0_ = plan[pd.o_p0 + (U)];             \
-        int q_ = 0;                                                               \
-        _Pragma("unroll") for (int tt = 0; tt < TT; tt++) {                       \
-            if (q_ < n_ && plan[pd.o_t + p0_ + q_] == tt) {                       \
-                const int p = p0_ + q_;                                           \
-                const float pw = __int_as_float(plan[pd.o_w + p]);                \
-                Act<WB> A;                                                        \
-                act_from_lds<WB>(A, la_of(p), ld_of(p), lq_of(p), pos);           \
-                _Pragma("unroll") for (int j = 0; j < NSTEP; j++)                 \
-                    acc[tt][j] += A.dot(WB_[j]) * (pw * SB_[j]);                  \
-                q_++;                                                             \
-            }                                                                     \
-        }                                                                         \
-    }
-    // three buffers in rotation: two slots of rows in flight ahead of use.
-    // The first two slots' rows are requested before the activations are
-    // staged, so the weight stream starts one plan round trip into the kernel.
-    MOE_DS_LOAD(0, w0, s0)
-    if (1 < S) MOE_DS_LOAD(1, w1, s1)
-    {
-        const PlanPairs pq = plan_pairs(plan, pd);
-        for (int c = tid; c < pq.count() * cpr; c += kDsThreads) {
-            const int i = c / cpr, pp = c - i * cpr, p = pq(i);
-            stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pp, la_of(p), ld_of(p), lq_of(p));
+    // a ring of NB slot buffers, NB - 1 slots of rows in flight ahead of use
+    // (every index into the ring is static once the loops are unrolled, so
+    // the buffers stay in registers)
+    uint4 wr[NB][NSTEP];
+    float sr[NB][NSTEP];
+    auto load_slot = [&](int u, uint4 (&wb)[NSTEP], float (&sb)[NSTEP]) {
+        const float *ds;
+        const uint8_t *src = slot_src(u, ds);
+#pragma unroll
+        for (int j = 0; j < NSTEP; j++) {
+            wb[j] = ld16(src + j * step_bytes);
+            sb[j] = ds[j * RPS];
         }
-        __syncthreads();
-    }
-    for (int u = 0; u < S; u += 3) {
-        if (u + 2 < S) MOE_DS_LOAD(u + 2, w2, s2)
-        MOE_DS_USE(u, w0, s0)
-        if (u + 1 < S) {
-            if (u + 3 < S) MOE_DS_LOAD(u + 3, w0, s0)
-            MOE_DS_USE(u + 1, w1, s1)
+    };
+    // a slot's pairs list its tokens in ascending order: walk the tokens in
+    // compile-time order so every accumulator index is static
+    auto use_slot = [&](int u, const uint4 (&wb)[NSTEP], const float (&sb)[NSTEP]) {
+        const int n = plan[pd.o_n + u], p0 = plan[pd.o_p0 + u];
+        int q = 0;
+#pragma unroll
+        for (int tt = 0; tt < TT; tt++) {
+            if (q < n && plan[pd.o_t + p0 + q] == tt) {
+                const int p = p0 + q;
+                const float pw = __int_as_float(plan[pd.o_w + p]);
+                Act<WB> A;
+                act_from_lds<WB>(A, la_of(p), ld_of(p), lq_of(p), pos);
+#pragma unroll
+                for (int j = 0; j < NSTEP; j++) acc[tt][j] += A.dot(wb[j]) * (pw * sb[j]);
+                q++;
+            }
         }
-        if (u + 2 < S) {
-            if (u + 4 < S) MOE_DS_LOAD(u + 4, w1, s1)
-            MOE_DS_USE(u + 2, w2, s2)
+    };
+    // Staging of every pair's int8 h: SB chunks per thread per batch of
+    // loads; the last batch's spare lanes take the last chunk again (same
+    // value, same place), so no load or store sits under a per-lane branch.
+    constexpr int SB = stage_batch(WB);
+    const PlanPairs pq = plan_pairs(plan, pd);
+    const int nst = pq.count() * cpr;
+    Act<WB> sa[SB];
+    int scs[SB];
+    auto stage_issue = [&](int c0) {
+#pragma unroll
+        for (int b = 0; b < SB; b++) {
+            scs[b] = min(c0 + b * kDsThreads + tid, nst - 1);
+            const int i = scs[b] / cpr, pp = scs[b] - i * cpr, p = pq(i);
+            sa[b].load_raw(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pp);
+        }
+    };
+    auto stage_store = [&]() {
+#pragma unroll
+        for (int b = 0; b < SB; b++) {
+            const int i = scs[b] / cpr, pp = scs[b] - i * cpr, p = pq(i);
+            sa[b].finish();
+            store_act<WB>(sa[b], pp, la_of(p), ld_of(p), lq_of(p));
+        }
+    };
+    // The first batch of the staging and then the first NB - 1 slots' rows
+    // are requested together, one plan round trip into the kernel; the
+    // staging stores wait for the staging loads only (the vector memory
+    // counter retires loads in issue order).
+    // (a plan with fewer slots requests its last slot again: straight-line
+    // code, so the wait for the staging counts exactly the loads after it)
+    if (kStageFirst) stage_issue(0);
+#pragma unroll
+    for (int b = 0; b < NB - 1; b++) load_slot(min(b, S - 1), wr[b], sr[b]);
+    if (!kStageFirst) stage_issue(0);
+    // keep every load above issued before the first use of any of them
+    __builtin_amdgcn_sched_barrier(0);
+    stage_store();
+    for (int c0 = SB * kDsThreads; c0 < nst; c0 += SB * kDsThreads) {
+        stage_issue(c0);
+        stage_store();
+    }
+    __syncthreads();
+    for (int u0 = 0; u0 < S; u0 += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const int u = u0 + b;
+            if (u + NB - 1 < S) load_slot(u + NB - 1, wr[(b + NB - 1) % NB], sr[(b + NB - 1) % NB]);
+            if (u < S) use_slot(u, wr[b], sr[b]);
         }
     }
-#undef MOE_DS_LOAD
-#undef MOE_DS_USE
     const int l32 = lane & 31;
     const int jj = l32 / (32 / NSTEP);
     const bool writer = (l32 % (32 / NSTEP)) == 0;
@@ -881,7 +922,8 @@ static int run_gate_up_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims 
 template <int WB, int RPS, int TT>
 static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
-    k_down_sw<WB, RPS, TT><<<a.H / kDsRows, kDsThreads, down_lds_bytes(WB, a.I, pd), st>>>(a, cc, pd);
+    constexpr int NB = down_ring(WB, TT);
+    k_down_sw<WB, RPS, TT, NB><<<a.H / kDsRows, kDsThreads, down_lds_bytes(WB, a.I, pd), st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
 

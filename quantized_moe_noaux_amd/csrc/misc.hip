@@ -92,14 +92,8 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t *__restrict__ 
             const uint4 v = p[i];
             nn[4 * i] = v.x; nn[4 * i + 1] = v.y; nn[4 * i + 2] = v.z; nn[4 * i + 3] = v.w;
         }
-        int qs0 = 0, qs1 = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            qs0 = sdot4(nn[i], 0x01010101u, qs0);
-            qs1 = sdot4(nn[8 + i], 0x01010101u, qs1);
-        }
         Act<2> A;
-        A.set(nn, 0.f, 0.f, qs0, qs1);
+        A.set(nn, 0.f, 0.f);
         int i0, i1;
         A.isum2(w, i0, i1);
         o[2 * c] = i0;

@@ -72,13 +72,23 @@ __device__ __forceinline__ double wave_max_d(double v)
 // A row of n4 float4s is held by the 256 threads of a block: thread t,
 // register j = float4 t + 256 j (zero past the row), so H <= 8192 fits.
 constexpr int kNormPer = 8;
+// v[j] = (i < n) ? p[i] : 0, without a branch around the load: the load reads
+// the clamped index and the value is masked by a multiply.  A load under a
+// per-lane condition compiles to an exec-masked load that is waited for at
+// once (the other path writes the same registers), so a run of guarded loads
+// would cost one memory round trip each; these all stay in flight together.
+// (x * 1 is exact; x * 0 = +-0.  Finite inputs.)
+__device__ __forceinline__ float4 load4_masked(const float4 *__restrict__ p, int i, int n)
+{
+    const float4 t = p[i < n ? i : n - 1];
+    const float m = (i < n) ? 1.f : 0.f;
+    return make_float4(t.x * m, t.y * m, t.z * m, t.w * m);
+}
 __device__ __forceinline__ void load_row_regs(const float *__restrict__ xr, int n4, float4 (&v)[kNormPer])
 {
 #pragma unroll
-    for (int j = 0; j < kNormPer; j++) {
-        const int i = threadIdx.x + 256 * j;
-        v[j] = (i < n4) ? reinterpret_cast<const float4 *>(xr)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int j = 0; j < kNormPer; j++)
+        v[j] = load4_masked(reinterpret_cast<const float4 *>(xr), (int)threadIdx.x + 256 * j, n4);
 }
 // 1 / sqrt(mean(x^2) + eps) of the row in v; every thread of the 256-thread
 // block calls it (one barrier), red = 4 doubles of LDS not in use elsewhere.
@@ -204,15 +214,17 @@ template <> struct Act<4> {
 template <> struct Act<2> {
     uint32_t a[16];
     float d0, d1;      // the two blocks' scales
-    float d0s, d1s;    // d / 64: the masked fields carry a factor 64
-    int qs0, qs1;      // block sums of the activation codes (kept for the staging layout)
+    float d0s, d1s;    // d / 64: the block sums below carry a factor 64
+    int qs0, qs1;      // per block, 128 * (sum of the activation codes met by fields 0-2)
     __device__ __forceinline__ void set_scale(float d0_, float d1_)
     {
         d0 = d0_; d1 = d1_;
         d0s = d0_ * 0.015625f; d1s = d1_ * 0.015625f;
     }
-    __device__ __forceinline__ void set(const uint32_t *n, float d0_, float d1_, int qs0_, int qs1_)
+    // n: the 64 activation codes in natural order
+    __device__ __forceinline__ void set(const uint32_t *n, float d0_, float d1_)
     {
+        int c0 = 0, c1 = 0;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             uint32_t q0 = n[4 * k], q1 = n[4 * k + 1], q2 = n[4 * k + 2], q3 = n[4 * k + 3];
@@ -223,8 +235,14 @@ template <> struct Act<2> {
             a[4 * k + 2] = perm(hi23, hi01, 0x05040100u);
             a[4 * k + 3] = perm(hi23, hi01, 0x07060302u);
         }
+        // fields 0-2 meet bytes 0-2 of every natural-order activation dword
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            c0 = sdot4(n[i], 0x00010101u, c0);
+            c1 = sdot4(n[8 + i], 0x00010101u, c1);
+        }
+        qs0 = 128 * c0; qs1 = 128 * c1;
         set_scale(d0_, d1_);
-        qs0 = qs0_; qs1 = qs1_;
     }
     __device__ __forceinline__ void load(const int8_t *q, const float *dblk, int chunk)
     {
@@ -247,26 +265,27 @@ template <> struct Act<2> {
         uint32_t n[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) n[i] = a[i];
-        int q0 = 0, q1 = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            q0 = sdot4(n[i], 0x01010101u, q0);
-            q1 = sdot4(n[8 + i], 0x01010101u, q1);
-        }
-        set(n, d0, d1, q0, q1);
+        set(n, d0, d1);
     }
-    // 64 * (sum over one weight dword's 16 codes): field i of every byte
-    // shifted up into the top two bits; two chains of two v_dot4
-    __device__ __forceinline__ int part64(uint32_t w, int k) const
+    // 64 * (sum over one block = weight dwords k, k+1).  Fields 0-2 are
+    // XORed into offset form c + 2 in [0, 3] and masked in place, so their
+    // bytes read c + 2, 4(c + 2), 16(c + 2); field 3 stays two's complement
+    // in the top bits (64c).  One v_dot4 chain per field, combined as
+    //     64 S = 64 S0 + 16 S1 + 4 S2 + S3 - 128 * (activations of fields 0-2)
+    // with the offset term (qs) entering at the head of the field-3 chain.
+    __device__ __forceinline__ int block64(uint32_t w0, uint32_t w1, int k, int qs) const
     {
-        const int s0 = sdot4((w << 4) & 0xC0C0C0C0u, a[4 * k + 1], sdot4((w << 6) & 0xC0C0C0C0u, a[4 * k], 0));
-        const int s1 = sdot4(w & 0xC0C0C0C0u, a[4 * k + 3], sdot4((w << 2) & 0xC0C0C0C0u, a[4 * k + 2], 0));
-        return s0 + s1;
+        const uint32_t x0 = w0 ^ 0x2A2A2A2Au, x1 = w1 ^ 0x2A2A2A2Au;
+        const int s0 = sdot4(x1 & 0x03030303u, a[4 * k + 4], sdot4(x0 & 0x03030303u, a[4 * k], 0));
+        const int s1 = sdot4(x1 & 0x0C0C0C0Cu, a[4 * k + 5], sdot4(x0 & 0x0C0C0C0Cu, a[4 * k + 1], 0));
+        const int s2 = sdot4(x1 & 0x30303030u, a[4 * k + 6], sdot4(x0 & 0x30303030u, a[4 * k + 2], 0));
+        const int s3 = sdot4(w1 & 0xC0C0C0C0u, a[4 * k + 7], sdot4(w0 & 0xC0C0C0C0u, a[4 * k + 3], -qs));
+        return ((s0 * 4 + s1) * 4 + s2) * 4 + s3;
     }
     __device__ __forceinline__ void isum2_64(const uint4 &w, int &i0, int &i1) const
     {
-        i0 = part64(w.x, 0) + part64(w.y, 1);
-        i1 = part64(w.z, 2) + part64(w.w, 3);
+        i0 = block64(w.x, w.y, 0, qs0);
+        i1 = block64(w.z, w.w, 2, qs1);
     }
     __device__ __forceinline__ void isum2(const uint4 &w, int &i0, int &i1) const
     {

@@ -54,9 +54,8 @@ __global__ __launch_bounds__(256) void k_router_logits_small(
             float4 w[kPer], gv[kPer];
 #pragma unroll
             for (int j = 0; j < kPer; j++) {
-                const int i = tid + 256 * j;
-                w[j] = (i < n4) ? wr[i] : make_float4(0, 0, 0, 0);
-                gv[j] = (i < n4) ? reinterpret_cast<const float4 *>(ng)[i] : make_float4(0, 0, 0, 0);
+                w[j] = load4_masked(wr, tid + 256 * j, n4);
+                gv[j] = load4_masked(reinterpret_cast<const float4 *>(ng), tid + 256 * j, n4);
             }
 #pragma unroll
             for (int t = 0; t < kGemvMaxT; t++) {
@@ -66,13 +65,12 @@ __global__ __launch_bounds__(256) void k_router_logits_small(
                     const double r = row_rstd(v, H, eps, nred[t]);
 #pragma unroll
                     for (int j = 0; j < kPer; j++) {
-                        if (tid + 256 * j < n4) {
-                            const float4 n = norm4(v[j], r, gv[j]);
-                            acc[t] = fma((double)w[j].x, (double)n.x, acc[t]);
-                            acc[t] = fma((double)w[j].y, (double)n.y, acc[t]);
-                            acc[t] = fma((double)w[j].z, (double)n.z, acc[t]);
-                            acc[t] = fma((double)w[j].w, (double)n.w, acc[t]);
-                        }
+                        // masked-off lanes hold zeros in w, v and gv
+                        const float4 n = norm4(v[j], r, gv[j]);
+                        acc[t] = fma((double)w[j].x, (double)n.x, acc[t]);
+                        acc[t] = fma((double)w[j].y, (double)n.y, acc[t]);
+                        acc[t] = fma((double)w[j].z, (double)n.z, acc[t]);
+                        acc[t] = fma((double)w[j].w, (double)n.w, acc[t]);
                     }
                 }
             }
@@ -80,24 +78,20 @@ __global__ __launch_bounds__(256) void k_router_logits_small(
             for (int base = 0; base < n4; base += 256 * kPer) {
                 float4 w[kPer];
 #pragma unroll
-                for (int j = 0; j < kPer; j++) {
-                    const int i = base + tid + 256 * j;
-                    w[j] = (i < n4) ? wr[i] : make_float4(0, 0, 0, 0);
-                }
+                for (int j = 0; j < kPer; j++) w[j] = load4_masked(wr, base + tid + 256 * j, n4);
 #pragma unroll
                 for (int t = 0; t < kGemvMaxT; t++) {
                     if (t < T) {
                         const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H);
+                        float4 v[kPer];
+#pragma unroll
+                        for (int j = 0; j < kPer; j++) v[j] = load4_masked(xr, base + tid + 256 * j, n4);
 #pragma unroll
                         for (int j = 0; j < kPer; j++) {
-                            const int i = base + tid + 256 * j;
-                            if (i < n4) {
-                                const float4 v = xr[i];
-                                acc[t] = fma((double)w[j].x, (double)v.x, acc[t]);
-                                acc[t] = fma((double)w[j].y, (double)v.y, acc[t]);
-                                acc[t] = fma((double)w[j].z, (double)v.z, acc[t]);
-                                acc[t] = fma((double)w[j].w, (double)v.w, acc[t]);
-                            }
+                            acc[t] = fma((double)w[j].x, (double)v[j].x, acc[t]);
+                            acc[t] = fma((double)w[j].y, (double)v[j].y, acc[t]);
+                            acc[t] = fma((double)w[j].z, (double)v[j].z, acc[t]);
+                            acc[t] = fma((double)w[j].w, (double)v[j].w, acc[t]);
                         }
                     }
                 }

@@ -53,9 +53,11 @@ template <int CTRL> __device__ __forceinline__ void dpp_top2(double &b1, double 
 // loop reads whole 8-key steps with no bounds checks: a zero key never
 // outranks a real one.
 struct __align__(16) TopkLds {
-    double s[kMaxExperts];                       // sigmoid scores
-    double c[kMaxExperts];                       // c = s + bias
-    uint64_t key[kMaxExperts + 7 * kMaxGroups];  // order keys, group-strided
+    // the last entry of s, c and key is a dump slot: a lane without an
+    // expert stores there, so its loads and stores need no branch
+    double s[kMaxExperts + 1];                       // sigmoid scores
+    double c[kMaxExperts + 1];                       // c = s + bias
+    uint64_t key[kMaxExperts + 7 * kMaxGroups + 1];  // order keys, group-strided
     uint64_t fkey[kMaxExperts];                  // finalists' keys
     int fe[kMaxExperts];                         // finalists' experts
     int frank[kMaxExperts];                      // finalists' ranks among the finalists
@@ -112,35 +114,35 @@ __device__ __forceinline__ int outrank8(const uint64_t *p, int j0, uint64_t ke, 
 //   that route this token; several groups of a workgroup may route
 //   different tokens at once, each with its own L, since the barriers are
 //   workgroup-wide and every group passes the same ones.
-__device__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, size_t pstride, int nparts,
+__device__ __forceinline__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, size_t pstride, int nparts,
                            const float *__restrict__ bias, int *sel_e, float *sel_w, TopkLds &L, int tid,
                            int nt)
 {
     const int lane = lane_id();
     const int E = rc.E, G = rc.G, m = E / G, k = rc.k;
     const int mpad = (m + 7) & ~7;
+    const int kdump = kMaxExperts + 7 * kMaxGroups;
     for (int e0 = 0; e0 < E; e0 += 2 * nt) {
+        // both experts' loads at clamped indices, unconditionally (one round
+        // trip); a lane past E computes on a duplicate and stores it in the
+        // dump slots
         const int ea = e0 + tid, eb = e0 + nt + tid;
-        double za = 0.0, zb = 0.0;
-        float ba = 0.f, bb = 0.f;
-        if (ea < E) { za = zt[ea]; ba = bias[ea]; }
-        if (eb < E) { zb = zt[eb]; bb = bias[eb]; }
+        const int ca = min(ea, E - 1), cb = min(eb, E - 1);
+        double za = zt[ca], zb = zt[cb];
+        const float ba = bias[ca], bb = bias[cb];
         for (int p = 1; p < nparts; p++) {
-            if (ea < E) za += zt[p * pstride + ea];
-            if (eb < E) zb += zt[p * pstride + eb];
+            za += zt[p * pstride + ca];
+            zb += zt[p * pstride + cb];
         }
-        if (ea < E) {
-            const double sv = 1.0 / (1.0 + exp(-za)), cv = sv + (double)ba;
-            L.s[ea] = sv;
-            L.c[ea] = cv;
-            L.key[(ea / m) * mpad + ea % m] = order_key(cv);
-        }
-        if (eb < E) {
-            const double sv = 1.0 / (1.0 + exp(-zb)), cv = sv + (double)bb;
-            L.s[eb] = sv;
-            L.c[eb] = cv;
-            L.key[(eb / m) * mpad + eb % m] = order_key(cv);
-        }
+        const double sa = 1.0 / (1.0 + exp(-za)), cva = sa + (double)ba;
+        const double sb = 1.0 / (1.0 + exp(-zb)), cvb = sb + (double)bb;
+        const int da = ea < E ? ea : kMaxExperts, db = eb < E ? eb : kMaxExperts;
+        L.s[da] = sa;
+        L.c[da] = cva;
+        L.key[ea < E ? (ea / m) * mpad + ea % m : kdump] = order_key(cva);
+        L.s[db] = sb;
+        L.c[db] = cvb;
+        L.key[eb < E ? (eb / m) * mpad + eb % m : kdump] = order_key(cvb);
     }
     for (int i = tid; i < G * (mpad - m); i += nt) L.key[(i / (mpad - m)) * mpad + m + i % (mpad - m)] = 0ull;
     __syncthreads();
