@@ -91,6 +91,46 @@ __device__ __forceinline__ PlanPairs plan_pairs(const int *plan, const PlanDims 
     return q;
 }
 
+// The plan of one token (slots = its kept experts in ascending order, then
+// the shared expert).  Kept apart from the batch plan so that a caller that
+// only ever routes one token compiles no access through generic pointers: a
+// pending flat access anywhere in a kernel makes the compiler wait for all
+// outstanding loads wherever it waits for one.
+__device__ __forceinline__ void build_plan_one(const GemvArgs &a, const PlanDims &pd, int *plan, int *s_idx,
+                                               float *s_w, TopkLds &tl)
+{
+    const int tid = threadIdx.x, k = a.rc.k;
+    int *slot_e = plan + pd.o_e, *slot_n = plan + pd.o_n, *slot_p0 = plan + pd.o_p0;
+    int *pair_t = plan + pd.o_t;
+    float *pair_w = reinterpret_cast<float *>(plan + pd.o_w);
+    // one token: slots are its kept experts in ascending order, then the
+    // shared expert; the pair of a routed slot is the slot itself, the
+    // shared expert's pair is k (also when top-p keeps fewer experts)
+    block_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias, s_idx, s_w, tl);
+    if (tid < k) {
+        const int e = s_idx[tid];
+        if (e >= 0) {
+            int slot = 0;
+            for (int j = 0; j < k; j++) slot += (s_idx[j] >= 0 && s_idx[j] < e);
+            slot_e[slot] = e;
+            slot_n[slot] = 1;
+            slot_p0[slot] = slot;
+            pair_t[slot] = 0;
+            pair_w[slot] = s_w[tid];
+        }
+    }
+    if (tid == 0) {
+        int kept = 0;
+        for (int j = 0; j < k; j++) kept += (s_idx[j] >= 0);
+        plan[0] = kept + a.n_shared;
+        if (a.n_shared) {
+            slot_e[kept] = -1; slot_n[kept] = 1; slot_p0[kept] = k;
+            pair_t[k] = 0; pair_w[k] = 1.0f;
+        }
+    }
+    __syncthreads();
+}
+
 // Builds the batch-union plan in LDS (all threads of the block take part).
 // Slots hold the union of the routed experts in ascending expert order, then
 // the shared expert; pairs of a slot list its tokens in ascending order.
@@ -115,32 +155,7 @@ __device__ __forceinline__ void build_plan(const GemvArgs &a, const PlanDims &pd
         return;
     }
     if (T == 1) {
-        // one token: slots are its kept experts in ascending order, then the
-        // shared expert; the pair of a routed slot is the slot itself, the
-        // shared expert's pair is k (also when top-p keeps fewer experts)
-        block_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias, s_idx, s_w, *tl);
-        if (tid < k) {
-            const int e = s_idx[tid];
-            if (e >= 0) {
-                int slot = 0;
-                for (int j = 0; j < k; j++) slot += (s_idx[j] >= 0 && s_idx[j] < e);
-                slot_e[slot] = e;
-                slot_n[slot] = 1;
-                slot_p0[slot] = slot;
-                pair_t[slot] = 0;
-                pair_w[slot] = s_w[tid];
-            }
-        }
-        if (tid == 0) {
-            int kept = 0;
-            for (int j = 0; j < k; j++) kept += (s_idx[j] >= 0);
-            plan[0] = kept + a.n_shared;
-            if (a.n_shared) {
-                slot_e[kept] = -1; slot_n[kept] = 1; slot_p0[kept] = k;
-                pair_t[k] = 0; pair_w[k] = 1.0f;
-            }
-        }
-        __syncthreads();
+        build_plan_one(a, pd, plan, s_idx, s_w, *tl);
         return;
     }
     for (int i = tid; i < T * 16; i += nt) tokbits[i >> 4][i & 15] = 0u;
@@ -567,6 +582,7 @@ __device__ __forceinline__ float group32_reduce_scatter(float (&v)[N])
 }
 
 constexpr int kSwThreads = 192;  // gate/up row-sweep block
+static_assert(kSwThreads % 32 == 0, "row r of a tile is handled by threads r mod 32");
 constexpr int kSwGroups = kSwThreads / 32;
 constexpr int kSwDepth = 11;     // steps of prefetch in flight (<= 168 VGPRs: 3 waves per SIMD)
 
@@ -591,6 +607,10 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
 
     const uint8_t *gb = W.gate + ((size_t)ee * a.I + row0) * rowbytes + (size_t)tid * 16;
     const uint8_t *ub = W.up + ((size_t)ee * a.I + row0) * rowbytes + (size_t)tid * 16;
+    // the row scales this thread applies at the end (row tid % 32; kSwThreads
+    // is a multiple of 32), requested now so the epilogue does not wait on them
+    const float sg_r = W.gate_s[(size_t)ee * a.I + row0 + (tid & 31)];
+    const float su_r = W.up_s[(size_t)ee * a.I + row0 + (tid & 31)];
     const size_t step_bytes = (size_t)kSwThreads * CPT * 16;
     // Activation loads first, then PF steps of weight rows: the vector memory
     // counter retires loads in issue order, so the first dot then waits for
@@ -676,8 +696,7 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
         const int tt = i >> 5, r = i & 31, g0 = (r % RPS) * groups_per_row;
         float g = 0.f, v = 0.f;
         for (int q = 0; q < groups_per_row; q++) { g += part[0][tt][g0 + q][r]; v += part[1][tt][g0 + q][r]; }
-        const size_t row = (size_t)ee * a.I + row0 + r;
-        s_h[tt][r] = silu_mul(g * W.gate_s[row], v * W.up_s[row]);
+        s_h[tt][r] = silu_mul(g * sg_r, v * su_r);  // r == tid % 32
     }
     __syncthreads();
     // quantise h per token: one block of 32 rows, lanes 0..31 of a wave
@@ -720,7 +739,7 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
         return;
     }
     const int u = v - a.n_shared;
-    build_plan(a, pd, plan, s_idx, s_w, nullptr, &tl);
+    build_plan_one(a, pd, plan, s_idx, s_w, tl);
     if (u >= plan[0] - a.n_shared) return;  // a slot top-p dropped (uniform in the workgroup)
     if (u == 0 && tile == 0) {
         for (int i = threadIdx.x; i < pd.words; i += kSwThreads) a.plan[i] = plan[i];
@@ -761,6 +780,7 @@ __global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, con
 constexpr int kDsThreads = 256;  // down row-sweep block
 constexpr int kDsGroups = kDsThreads / 32;
 constexpr int kDsRows = 16;      // output rows per workgroup
+static_assert(kDsRows == kGemvDownRows, "rows per down workgroup (LDS sizing)");
 
 // slots of down rows in flight ahead of use, plus the one in use
 constexpr int down_ring(int wb, int tt) { return 3; }
@@ -783,25 +803,32 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     auto la_of = [&](int p) { return reinterpret_cast<uint32_t *>(act + p * pair_bytes); };
     auto ld_of = [&](int p) { return reinterpret_cast<float *>(act + p * pair_bytes + I); };
     auto lq_of = [&](int p) { return reinterpret_cast<int *>(act + p * pair_bytes + I + 4 * nbh); };
+    // every slot's kDsRows row scales, [slot][row]
+    float *lsc = reinterpret_cast<float *>(act + (size_t)pd.P * pair_bytes);
 
     for (int i = tid; i < pd.words; i += kDsThreads) plan[i] = a.plan[i];
     __syncthreads();
     if (!plan_ok(plan, pd, a.T, a.E) || plan[0] < 1) return;
     const int S = plan[0];
+    // thread i < T * kDsRows writes output (token i / kDsRows, row i % kDsRows);
+    // with MOE_ACCUMULATE it adds to the value read here, at the start
+    static_assert(kGemvMaxT * kDsRows <= kDsThreads, "one output per thread");
+    const float y_old = [&] {
+        const int i = min(tid, a.T * kDsRows - 1);
+        return a.y[(size_t)(i / kDsRows) * a.H + blockIdx.x * kDsRows + i % kDsRows];
+    }();
 
     const int rowoff = tid / cpr, pos = tid % cpr, grp = tid >> 5;
     const int row_base = blockIdx.x * kDsRows;
     const size_t rowbytes = (size_t)cpr * 16;
     const size_t step_bytes = (size_t)kDsThreads * 16;
-    // the slot's base addresses are workgroup-uniform (scalar registers): the
-    // loads then take a fixed per-lane offset, and no vector register of a
-    // load still in flight is reused for the next slot's addresses
-    auto slot_src = [&](int u, const float *&ds) {
-        const int e = __builtin_amdgcn_readfirstlane(plan[pd.o_e + u]);
-        const moe_weights_t &W = (e >= 0) ? a.routed : a.shared;
-        const int ee = (e >= 0) ? e : 0;
-        ds = W.down_s + (size_t)ee * a.H + row_base + rowoff;
-        return W.down + ((size_t)ee * a.H + row_base) * rowbytes + (size_t)tid * 16;
+    auto slot_w = [&](int u) -> const moe_weights_t & { return plan[pd.o_e + u] >= 0 ? a.routed : a.shared; };
+    auto slot_ee = [&](int u) { return max(plan[pd.o_e + u], 0); };
+    // the slot's base address is workgroup-uniform (scalar registers): the
+    // loads then take a fixed per-lane offset
+    auto slot_src = [&](int u) {
+        const int uu = __builtin_amdgcn_readfirstlane(u);
+        return slot_w(uu).down + ((size_t)slot_ee(uu) * a.H + row_base) * rowbytes + (size_t)tid * 16;
     };
     float acc[TT][NSTEP];
 #pragma unroll
@@ -813,20 +840,18 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     // (every index into the ring is static once the loops are unrolled, so
     // the buffers stay in registers)
     uint4 wr[NB][NSTEP];
-    float sr[NB][NSTEP];
-    auto load_slot = [&](int u, uint4 (&wb)[NSTEP], float (&sb)[NSTEP]) {
-        const float *ds;
-        const uint8_t *src = slot_src(u, ds);
+    auto load_slot = [&](int u, uint4 (&wb)[NSTEP]) {
+        const uint8_t *src = slot_src(u);
 #pragma unroll
-        for (int j = 0; j < NSTEP; j++) {
-            wb[j] = ld16(src + j * step_bytes);
-            sb[j] = ds[j * RPS];
-        }
+        for (int j = 0; j < NSTEP; j++) wb[j] = ld16(src + j * step_bytes);
     };
     // a slot's pairs list its tokens in ascending order: walk the tokens in
     // compile-time order so every accumulator index is static
-    auto use_slot = [&](int u, const uint4 (&wb)[NSTEP], const float (&sb)[NSTEP]) {
+    auto use_slot = [&](int u, const uint4 (&wb)[NSTEP]) {
         const int n = plan[pd.o_n + u], p0 = plan[pd.o_p0 + u];
+        float sb[NSTEP];
+#pragma unroll
+        for (int j = 0; j < NSTEP; j++) sb[j] = lsc[u * kDsRows + j * RPS + rowoff];
         int q = 0;
 #pragma unroll
         for (int tt = 0; tt < TT; tt++) {
@@ -841,21 +866,27 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
             }
         }
     };
-    // Staging of every pair's int8 h: SB chunks per thread per batch of
-    // loads; the last batch's spare lanes take the last chunk again (same
-    // value, same place), so no load or store sits under a per-lane branch.
+    // Staging of every pair's int8 h and every slot's row scales: SB chunks
+    // (and one scale) per thread per batch of loads; spare lanes of the last
+    // batch take the last chunk or scale again (same value, same place), so
+    // no load or store sits under a per-lane branch.
     constexpr int SB = stage_batch(WB);
     const PlanPairs pq = plan_pairs(plan, pd);
-    const int nst = pq.count() * cpr;
+    const int nst = pq.count() * cpr, nsc = S * kDsRows;
     Act<WB> sa[SB];
     int scs[SB];
-    auto stage_issue = [&](int c0) {
+    float scv;
+    int sci;
+    auto stage_issue = [&](int c0, int i0) {
 #pragma unroll
         for (int b = 0; b < SB; b++) {
             scs[b] = min(c0 + b * kDsThreads + tid, nst - 1);
             const int i = scs[b] / cpr, pp = scs[b] - i * cpr, p = pq(i);
             sa[b].load_raw(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pp);
         }
+        sci = min(i0 + tid, nsc - 1);
+        const int u = sci / kDsRows;
+        scv = slot_w(u).down_s[(size_t)slot_ee(u) * a.H + row_base + sci % kDsRows];
     };
     auto stage_store = [&]() {
 #pragma unroll
@@ -864,22 +895,22 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
             sa[b].finish();
             store_act<WB>(sa[b], pp, la_of(p), ld_of(p), lq_of(p));
         }
+        lsc[sci] = scv;
     };
-    // The first batch of the staging and then the first NB - 1 slots' rows
-    // are requested together, one plan round trip into the kernel; the
-    // staging stores wait for the staging loads only (the vector memory
-    // counter retires loads in issue order).
-    // (a plan with fewer slots requests its last slot again: straight-line
-    // code, so the wait for the staging counts exactly the loads after it)
-    if (kStageFirst) stage_issue(0);
+    // The first staging batch and then the first NB - 1 slots' rows are
+    // requested together, one plan round trip into the kernel; the staging
+    // stores wait for the staging loads only (the vector memory counter
+    // retires loads in issue order).  A plan with fewer slots requests its
+    // last slot again: straight-line code, so that wait counts exactly the
+    // loads issued after the staging.
+    stage_issue(0, 0);
 #pragma unroll
-    for (int b = 0; b < NB - 1; b++) load_slot(min(b, S - 1), wr[b], sr[b]);
-    if (!kStageFirst) stage_issue(0);
+    for (int b = 0; b < NB - 1; b++) load_slot(min(b, S - 1), wr[b]);
     // keep every load above issued before the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
     stage_store();
-    for (int c0 = SB * kDsThreads; c0 < nst; c0 += SB * kDsThreads) {
-        stage_issue(c0);
+    for (int c0 = SB * kDsThreads, i0 = kDsThreads; c0 < nst || i0 < nsc; c0 += SB * kDsThreads, i0 += kDsThreads) {
+        stage_issue(min(c0, nst - 1), min(i0, nsc - 1));
         stage_store();
     }
     __syncthreads();
@@ -887,8 +918,8 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             const int u = u0 + b;
-            if (u + NB - 1 < S) load_slot(u + NB - 1, wr[(b + NB - 1) % NB], sr[(b + NB - 1) % NB]);
-            if (u < S) use_slot(u, wr[b], sr[b]);
+            if (u + NB - 1 < S) load_slot(u + NB - 1, wr[(b + NB - 1) % NB]);
+            if (u < S) use_slot(u, wr[b]);
         }
     }
     const int l32 = lane & 31;
@@ -903,12 +934,11 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     }
     __syncthreads();
     const int groups_per_row = cpr / 32;
-    for (int i = tid; i < a.T * kDsRows; i += kDsThreads) {
-        const int tt = i / kDsRows, r = i % kDsRows, g0 = (r % RPS) * groups_per_row;
+    if (tid < a.T * kDsRows) {
+        const int tt = tid / kDsRows, r = tid % kDsRows, g0 = (r % RPS) * groups_per_row;
         float v = 0.f;
         for (int q = 0; q < groups_per_row; q++) v += part[tt][g0 + q][r];
-        float *dst = a.y + (size_t)tt * a.H + row_base + r;
-        *dst = a.accumulate ? *dst + v : v;
+        a.y[(size_t)tt * a.H + row_base + r] = a.accumulate ? y_old + v : v;
     }
 }
 

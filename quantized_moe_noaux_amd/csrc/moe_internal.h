@@ -67,14 +67,16 @@ __host__ __device__ inline size_t act_lds_bytes(int wbits, int in)
 {
     return ((size_t)in + (size_t)(in / 32) * (wbits == 8 ? 4 : 8) + 15) & ~(size_t)15;
 }
-// LDS of the down/combine kernel: the plan, then every pair's activations.
+constexpr int kGemvDownRows = 16;  // rows per down/combine workgroup
+// LDS of the down/combine kernel: the plan, every pair's activations, then
+// every slot's row scales of the workgroup's rows.
 inline size_t down_lds_bytes(int wbits, int I, const PlanDims &pd)
 {
-    return sizeof(int) * (size_t)((pd.words + 3) & ~3) + (size_t)pd.P * act_lds_bytes(wbits, I);
+    return sizeof(int) * (size_t)((pd.words + 3) & ~3) + (size_t)pd.P * act_lds_bytes(wbits, I) +
+           sizeof(float) * (size_t)pd.S * kGemvDownRows;
 }
 // LDS of the gate/up kernel: static plan / routing scratch plus Tc tokens of
 // staged activations over H.
-constexpr int kGemvDownRows = 16;  // rows per down/combine workgroup
 constexpr size_t kGateUpStaticLds = 12 * 1024;
 inline size_t gate_up_lds_bytes(int wbits, int H, int Tc) { return kGateUpStaticLds + Tc * act_lds_bytes(wbits, H); }
 // tokens per batch-union chunk: the largest count <= kGemvMaxT whose LDS fits
