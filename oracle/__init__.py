@@ -69,6 +69,8 @@ def lib():
         L.oracle_rmsnorm.argtypes = [vp, vp, dbl, i32, i32, vp]
         L.oracle_permute.restype = i32
         L.oracle_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.oracle_mtp_accept.restype = i32
+        L.oracle_mtp_accept.argtypes = [i32, i32, i32, vp, vp, vp, dbl, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -230,3 +232,23 @@ def permute(idx, E):
 def layer_experts(layer, idx):
     """HostExpert objects for the routed experts that idx selects."""
     return {int(e): layer.expert(int(e)) for e in np.unique(idx) if e >= 0}
+
+
+def mtp_accept(draft, p_logits, q_logits, tau, u):
+    """Draft verification: draft [B][D] int32, p_logits [B][D+1][V],
+    q_logits [B][D][V] float32, uniforms u [B][D+1] float64.  Returns
+    (n_acc [B], next [B], margins [B])."""
+    p_logits = _c(p_logits, np.float32)
+    B, D1, V = p_logits.shape
+    D = D1 - 1
+    draft = _c(np.asarray(draft).reshape(B, D), np.int32)
+    q_logits = _c(np.asarray(q_logits).reshape(B, D, V), np.float32)
+    u = _c(np.asarray(u).reshape(B, D + 1), np.float64)
+    n_acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    mg = np.empty(B, np.float64)
+    rc = lib().oracle_mtp_accept(B, D, V, _p(draft), _p(p_logits), _p(q_logits), float(tau), _p(u),
+                                 _p(n_acc), _p(nxt), _p(mg))
+    if rc:
+        raise ValueError("oracle_mtp_accept failed: %d" % rc)
+    return n_acc, nxt, mg

@@ -408,3 +408,123 @@ int oracle_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32
     free(fill);
     return 0;
 }
+
+/* ---------------------------------------------------------------- MTP draft verification
+ * GeekNews #31297, implemented features: the multi-token-prediction head
+ * drafts tokens, the main model verifies them in one batched forward, and
+ * rejection sampling keeps sampled output lossless; useful options: --temp T
+ * (0 = greedy).  The yodev.dev page: greedy output is identical to plain
+ * greedy decoding.
+ * reading: the pages name rejection sampling but not its rule; the rule
+ * taken is speculative sampling (Leviathan, Kalman & Matias, ICML 2023;
+ * Chen et al. 2023): draft x_i, drawn from q_i, is kept when
+ * u_i * q_i(x_i) < p_i(x_i); at the first refusal the emitted token is drawn
+ * from max(0, p_i - q_i) renormalised (from p_i itself if that has no mass);
+ * when every draft is kept it is drawn from p_D.  p and q are the softmax
+ * of the logits divided by the temperature; nucleus filtering is not
+ * applied.  Draws use inverse CDFs in ascending token order with the given
+ * uniforms; greedy (tau = 0) keeps drafts while they equal the target's
+ * argmax (lowest index on ties) and emits the argmax at the first mismatch. */
+
+/* softmax(z / tau) of one row into out[V], fp64, max subtracted */
+static void softmax_row(const float *z, int V, double tau, double *out)
+{
+    float m = z[0];
+    for (int x = 1; x < V; x++) if (z[x] > m) m = z[x];
+    double s = 0.0;
+    for (int x = 0; x < V; x++) {
+        out[x] = exp(((double)z[x] - (double)m) / tau);
+        s += out[x];
+    }
+    for (int x = 0; x < V; x++) out[x] /= s;
+}
+
+static int argmax_row(const float *z, int V)
+{
+    int a = 0;
+    for (int x = 1; x < V; x++) if (z[x] > z[a]) a = x;
+    return a;
+}
+
+/* smallest x whose cumulative weight exceeds u * (total weight); margin =
+ * distance of the target from the nearest cumulative boundary, relative to
+ * the total */
+static int inverse_cdf(const double *w, int V, double u, double *margin)
+{
+    double W = 0.0;
+    for (int x = 0; x < V; x++) W += w[x];
+    const double t = u * W;
+    double c = 0.0;
+    int last = -1;
+    for (int x = 0; x < V; x++) {
+        if (w[x] <= 0.0) continue;
+        const double c0 = c;
+        c += w[x];
+        last = x;
+        if (c > t) {
+            double m = (t - c0 < c - t) ? t - c0 : c - t;
+            if (margin) *margin = m / W;
+            return x;
+        }
+    }
+    if (margin) *margin = 0.0;  /* rounding left t at or above the total */
+    return last;
+}
+
+int oracle_mtp_accept(int B, int D, int V, const int32_t *draft, const float *p_logits,
+                      const float *q_logits, double tau, const double *u, int32_t *n_acc,
+                      int32_t *next, double *margins)
+{
+    if (B < 0 || D < 0 || V < 1 || tau < 0.0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (int b = 0; b < B; b++) {
+        const int32_t *dr = draft + (size_t)b * D;
+        const float *pb = p_logits + (size_t)b * (D + 1) * V;
+        const float *qb = q_logits + (size_t)b * D * V;
+        const double *ub = u + (size_t)b * (D + 1);
+        double mg = 1.0;
+        int n = D, nx = -1;
+        if (tau == 0.0) {
+            for (int i = 0; i < D; i++) {
+                const int a = argmax_row(pb + (size_t)i * V, V);
+                if (a != dr[i]) { n = i; nx = a; break; }
+            }
+            if (nx < 0) nx = argmax_row(pb + (size_t)D * V, V);
+        } else {
+            double *P = malloc(sizeof(double) * V), *Q = malloc(sizeof(double) * V);
+            if (!P || !Q) { bad = 1; free(P); free(Q); continue; }
+            for (int i = 0; i < D && nx < 0; i++) {
+                const int x = dr[i];
+                if (x < 0 || x >= V) { bad = 1; break; }
+                softmax_row(pb + (size_t)i * V, V, tau, P);
+                softmax_row(qb + (size_t)i * V, V, tau, Q);
+                const double lhs = ub[i] * Q[x], rhs = P[x];
+                const double m = fabs(rhs - lhs) / (rhs > lhs ? rhs : lhs > 0.0 ? lhs : 1.0);
+                if (m < mg) mg = m;
+                if (lhs < rhs) continue;  /* kept */
+                n = i;
+                double R = 0.0;
+                for (int y = 0; y < V; y++) {
+                    Q[y] = P[y] > Q[y] ? P[y] - Q[y] : 0.0;  /* the residual, in place */
+                    R += Q[y];
+                }
+                double m2;
+                nx = inverse_cdf(R > 0.0 ? Q : P, V, ub[D], &m2);
+                if (m2 < mg) mg = m2;
+            }
+            if (nx < 0 && !bad) {
+                double m2;
+                softmax_row(pb + (size_t)D * V, V, tau, P);
+                nx = inverse_cdf(P, V, ub[D], &m2);
+                if (m2 < mg) mg = m2;
+            }
+            free(P);
+            free(Q);
+        }
+        n_acc[b] = n;
+        next[b] = nx;
+        if (margins) margins[b] = mg;
+    }
+    return bad ? -2 : 0;
+}

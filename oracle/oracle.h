@@ -73,5 +73,13 @@ int oracle_combine(const oracle_shape *sh, int T, const float *w, const float *y
 void oracle_rmsnorm(const float *x, const float *g, double eps, int T, int H, float *out);
 int oracle_permute(const int32_t *idx, int T, int k, int E, int32_t *perm, int32_t *off,
                    int32_t *inv);
+/* MTP draft verification of B sequences of D drafts over a vocabulary of V:
+ * draft [B][D], p_logits [B][D+1][V] (target), q_logits [B][D][V] (draft
+ * model), uniforms u [B][D+1] in [0, 1); n_acc [B] drafts kept, next [B] the
+ * token emitted after them; margins [B] (nullable) the smallest relative
+ * distance of any sampled decision from its boundary. */
+int oracle_mtp_accept(int B, int D, int V, const int32_t *draft, const float *p_logits,
+                      const float *q_logits, double tau, const double *u, int32_t *n_acc,
+                      int32_t *next, double *margins);
 
 #endif

@@ -24,6 +24,8 @@ from . import _build
 
 # tensor kinds (bits 32..39 of the stream id)
 X, GATE_W, BIAS, W_GATE, W_UP, W_DOWN, S_GATE, S_UP, S_DOWN = range(9)
+# draft verification: target logits, draft-logit noise, draft draws, uniforms
+MTP_P, MTP_Q, MTP_G, MTP_U = range(9, 13)
 
 
 def stream_id(layer, kind, expert=0):
@@ -111,6 +113,7 @@ def _host_lib():
         lib.synth_int8_codes.argtypes = [u64, u64, u64, ctypes.c_void_p]
         lib.synth_scales.argtypes = [u64, u64, u64, ctypes.c_double, ctypes.c_void_p]
         lib.synth_normals.argtypes = [u64, u64, u64, ctypes.c_double, ctypes.c_void_p]
+        lib.synth_uniforms.argtypes = [u64, u64, u64, ctypes.c_void_p]
         _host = lib
     return _host
 
@@ -145,6 +148,40 @@ def host_normals(seed, stream, n, sigma):
     out = np.empty(n, np.float32)
     _host_lib().synth_normals(key(seed, stream), 0, n, float(sigma), out.ctypes.data)
     return out
+
+
+def host_uniforms(seed, stream, n):
+    out = np.empty(n, np.float64)
+    _host_lib().synth_uniforms(key(seed, stream), 0, n, out.ctypes.data)
+    return out
+
+
+def mtp_inputs(seed, B, D, V, tau, sigma_p=3.0, sigma_n=1.0):
+    """Synthetic inputs of one draft-verification step for B sequences.
+
+    Target logits N(0, sigma_p^2) per token; the draft model's logits are the
+    target's plus N(0, sigma_n^2) noise (a draft head that mostly agrees with
+    the model); draft i of sequence b is drawn from the draft distribution at
+    temperature tau by the Gumbel-max trick (its argmax when tau = 0), with
+    uniforms of its own stream; u [B][D+1] are the uniforms the acceptance
+    step consumes.  Returns (draft [B][D] int32, p_logits [B][D+1][V] f32,
+    q_logits [B][D][V] f32, u [B][D+1] f64)."""
+    p = np.empty((B, D + 1, V), np.float32)
+    q = np.empty((B, D, V), np.float32)
+    draft = np.empty((B, D), np.int32)
+    u = np.empty((B, D + 1), np.float64)
+    for b in range(B):
+        p[b] = host_normals(seed, stream_id(0, MTP_P, b), (D + 1) * V, sigma_p).reshape(D + 1, V)
+        if D:
+            q[b] = p[b, :D] + host_normals(seed, stream_id(0, MTP_Q, b), D * V, sigma_n).reshape(D, V)
+            if tau > 0:
+                g = host_uniforms(seed, stream_id(0, MTP_G, b), D * V).reshape(D, V)
+                g = -np.log(-np.log(g + 2.0 ** -54))  # Gumbel(0, 1); the offset keeps log(0) out
+                draft[b] = np.argmax(q[b].astype(np.float64) / tau + g, axis=1)
+            else:
+                draft[b] = np.argmax(q[b], axis=1)
+        u[b] = host_uniforms(seed, stream_id(0, MTP_U, b), D + 1)
+    return draft, p, q, u
 
 
 def _codes(wl, seed, stream, rows, in_dim):

@@ -29,6 +29,7 @@
  *   normal i        : Box-Muller on u1 = ((word(2i) >> 11) + 1) * 2^-53 and
  *                     u2 = (word(2i+1) >> 11) * 2^-53:
  *                     (float)(sigma * sqrt(-2 ln u1) * cos(2 pi u2)).
+ *   uniform i       : (word(i) >> 11) * 2^-53, a double in [0, 1).
  */
 #include <math.h>
 #include <stdint.h>
@@ -81,6 +82,14 @@ void synth_scales(uint64_t key, uint64_t i0, uint64_t n, double c, float *out)
         uint64_t u24 = synth_word(key, i0 + j) >> 40;
         out[j] = (float)((0.5 + (double)u24 * 0x1p-24) * c);
     }
+}
+
+/* out[j] = uniform (i0 + j), j < n */
+void synth_uniforms(uint64_t key, uint64_t i0, uint64_t n, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < (int64_t)n; j++)
+        out[j] = (double)(synth_word(key, i0 + (uint64_t)j) >> 11) * 0x1p-53;
 }
 
 /* out[j] = normal (i0 + j) * sigma, j < n */

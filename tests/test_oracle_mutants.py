@@ -10,6 +10,7 @@ import subprocess
 import pytest
 
 import oracle
+import test_oracle_accept as acc
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -29,7 +30,11 @@ MISC = [pins.test_rmsnorm_closed_forms, pins.test_permute_is_stable_sort, pins.t
 TOPP = [lambda: pins.test_top_p_keeps_the_shortest_prefix_reaching_p(0.7), pins.test_top_p_off_and_single_expert,
         pins.test_top_p_boundary_is_inclusive, pins.test_top_p_follows_selection_order_not_weight,
         pins.test_top_p_layer_with_one_expert_per_token]
-ALL = ROUTE + QUANT + DOTS + LAYER + MISC + TOPP
+ACCEPT = [acc.test_sampled_first_token_is_lossless, acc.test_acceptance_rate_is_one_minus_total_variation,
+          acc.test_second_and_bonus_tokens_follow_their_rows, acc.test_no_drafts_is_inverse_cdf_sampling_of_p,
+          acc.test_identical_draft_and_target_keep_every_draft, acc.test_greedy_equals_plain_greedy_decoding,
+          acc.test_temperature_enters_both_distributions]
+ALL = ROUTE + QUANT + DOTS + LAYER + MISC + TOPP + ACCEPT
 
 MUTANTS = {
     "group score = max only": ("gscore[g] = (m >= 2) ? b1 + b2 : b1;", "gscore[g] = b1;"),
@@ -66,6 +71,20 @@ MUTANTS = {
                               "        if (idx[a] == -1) { off[1]++; continue; }\n"),
     "permute not stable": ("int row = fill[idx[a]]++;",
                            "int row = off[idx[a]] + off[idx[a] + 1] - 1 - fill[idx[a]]++;"),
+    "draft test ratio inverted": ("const double lhs = ub[i] * Q[x], rhs = P[x];",
+                                  "const double lhs = ub[i] * P[x], rhs = Q[x];"),
+    "residual q - p": ("Q[y] = P[y] > Q[y] ? P[y] - Q[y] : 0.0;", "Q[y] = Q[y] > P[y] ? Q[y] - P[y] : 0.0;"),
+    "residual not clipped": ("Q[y] = P[y] > Q[y] ? P[y] - Q[y] : 0.0;", "Q[y] = P[y] - Q[y];"),
+    "residual from p": ("nx = inverse_cdf(R > 0.0 ? Q : P, V, ub[D], &m2);", "nx = inverse_cdf(P, V, ub[D], &m2);"),
+    "draft rows off by one": ("softmax_row(pb + (size_t)i * V, V, tau, P);",
+                              "softmax_row(pb + (size_t)(i + 1) * V, V, tau, P);"),
+    "inverse cdf unscaled": ("const double t = u * W;", "const double t = u;"),
+    "inverse cdf reuses a draw": ("nx = inverse_cdf(P, V, ub[D], &m2);", "nx = inverse_cdf(P, V, ub[0], &m2);"),
+    "argmax ties to higher index": ("if (z[x] > z[a]) a = x;", "if (z[x] >= z[a]) a = x;"),
+    "greedy against draft logits": ("const int a = argmax_row(pb + (size_t)i * V, V);",
+                                    "const int a = argmax_row(qb + (size_t)i * V, V);"),
+    "temperature ignored": ("out[x] = exp(((double)z[x] - (double)m) / tau);",
+                            "out[x] = exp((double)z[x] - (double)m);"),
 }
 
 
