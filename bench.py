@@ -185,11 +185,15 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_int4",
-                    choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2"])
+                    choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2", "mtp_int4"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--graph", action="store_true", help="launch each step as a captured HIP graph")
     ap.add_argument("--top-p", type=float, default=0.0, help="adaptive expert top-p (decode / verify)")
     ap.add_argument("--stack-eager", action="store_true", help="stack: launch directly instead of a graph")
+    ap.add_argument("--draft", type=int, default=4, help="mtp_int4: drafts per verify step")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="decode_int4 / verify_int8: tokens per step (the verify batch 1 + drafts)")
+    ap.add_argument("--temp", type=float, default=0.7, help="mtp_int4: sampling temperature (0 = greedy)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -217,11 +221,18 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.workload == "mtp_int4":
+        return bench_mtp(args)
     wl = synth.workload(args.workload)
     if args.top_p:
         if wl.layers > 1 or args.workload == "prefill_int4":
             raise SystemExit("--top-p applies to the one-layer GEMV workloads (decode_int4, verify_int8)")
         wl = synth.workload(args.workload, top_p=args.top_p)
+    if args.tokens is not None:
+        if wl.layers > 1 or args.workload == "prefill_int4" or not 1 <= args.tokens <= 8:
+            raise SystemExit("--tokens takes 1..8 on the one-layer GEMV workloads (decode_int4, verify_int8)")
+        from dataclasses import replace
+        wl = replace(wl, T=args.tokens)
     if wl.layers > 1:
         return bench_stack(args, wl)
     T = wl.T
@@ -403,7 +414,8 @@ def main():
         "dtype": "i8",
         "data": "synthetic (seeded SplitMix64 weights and N(0,1) tokens, %d rotating inputs%s)" %
                 (n_inputs, "" if args.no_flush else ", caches flushed between steps"),
-        "config": {"workload": wl.name + ("_topp%g" % wl.top_p if wl.top_p else ""), "T": T,
+        "config": {"workload": wl.name + ("_topp%g" % wl.top_p if wl.top_p else "") +
+                               ("_T%d" % T if args.tokens is not None else ""), "T": T,
                    "top_p": wl.top_p, "hidden": wl.hidden, "inter": wl.inter,
                    "n_experts": wl.n_experts, "n_group": wl.n_group, "topk_group": wl.topk_group,
                    "top_k": wl.top_k, "n_shared": wl.n_shared, "wbits": wl.wbits, "rsf": wl.rsf,
@@ -604,6 +616,132 @@ def bench_stack(args, wl):
                                                            for p in (10, 50, 90)],
                    "token_weight_bytes": token_bytes, "router_weight_bytes": router_bytes,
                    "wall_s_timed_loop_incl_flush": wall},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+MTP_VOCAB = 320000   # the order of the pages' 320k-merge BPE vocabulary
+
+
+def bench_mtp(args):
+    """One MTP verify step per timed step: the int4 decode layer at T = 1 + D
+    (batch-union GEMV path) and the acceptance step over D+1 target and D
+    draft logit rows of the vocabulary (moe_mtp_accept), beside the same layer
+    at T = 1 for plain decode.  Tokens per step are the kernel's own kept
+    drafts + 1 on the synthetic verify inputs (draft logits = target + noise,
+    tuned into the pages' 39-59% per-draft acceptance)."""
+    import numpy as np
+    import torch
+    import synth
+    from quantized_moe_noaux_amd import moe
+
+    dev = "cuda:0"
+    D, V, tau = args.draft, MTP_VOCAB, args.temp
+    T = 1 + D
+    wl = synth.workload("decode_int4", T=T)
+    wl1 = synth.workload("decode_int4")
+    n_inputs = 16
+    steps = args.steps if args.steps is not None else 100
+    warmup = args.warmup if args.warmup is not None else 10
+    sh, sh1 = moe.shape_of(wl), moe.shape_of(wl1)
+    flags = moe.MOE_PATH_GEMV
+    log("bench: mtp_int4 verify T=%d (D=%d drafts) + acceptance over V=%d, tau=%g" % (T, D, V, tau))
+    host = synth.HostLayer(wl)
+    gate_w = torch.from_numpy(host.gate_w).to(dev)
+    bias = torch.from_numpy(host.bias).to(dev)
+    routed = synth.device_weights(wl, 0, 0, wl.n_experts, dev)
+    shared = synth.device_weights(wl, 0, wl.n_experts, 1, dev)
+    xs = torch.stack([torch.from_numpy(
+        synth.host_normals(wl.seed + i, synth.stream_id(0, synth.X), T * wl.hidden, 1.0).reshape(T, wl.hidden))
+        for i in range(n_inputs)]).to(dev)
+    mi = [synth.mtp_inputs(1000 + i, 1, D, V, tau) for i in range(n_inputs)]
+    to = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+    drafts = [to(a[0], np.int32) for a in mi]
+    pls = [to(a[1], np.float32) for a in mi]
+    qls = [to(a[2], np.float32) for a in mi]
+    us = [to(a[3], np.float64) for a in mi]
+    y = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
+    ws = moe.workspace(moe.moe_workspace_bytes(sh, T, flags), dev)
+    ws1 = moe.workspace(moe.moe_workspace_bytes(sh1, 1, flags), dev)
+    aws = moe.workspace(moe.moe_mtp_accept_workspace_bytes(1, D, V), dev)
+    n_acc = torch.empty((n_inputs,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((n_inputs,), dtype=torch.int32, device=dev)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def flush():
+        flush_buf.sum()
+
+    def layer(i):
+        moe.moe_layer_forward(sh, xs[i % n_inputs], gate_w, bias, routed, shared, y, ws, flags=flags)
+
+    def accept(i):
+        k = i % n_inputs
+        moe.moe_mtp_accept(drafts[k], pls[k], qls[k], tau, us[k], n_acc[k:k + 1], nxt[k:k + 1], aws)
+
+    def decode(i):
+        moe.moe_layer_forward(sh1, xs[i % n_inputs][:1], gate_w, bias, routed, shared, y[:1], ws1, flags=flags)
+
+    for i in range(warmup):
+        flush(); layer(i); accept(i); flush(); decode(i)
+    torch.cuda.synchronize()
+    ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    E = [[ev() for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        for k, work in enumerate((lambda: None, lambda: decode(i), lambda: layer(i),
+                                  lambda: (layer(i), accept(i)))):
+            E[i][k][0].record(stream)
+            flush()
+            work()
+            E[i][k][1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([[a.elapsed_time(b) for a, b in row] for row in E])  # ms
+    t = t[:, 1:] - t[:, :1]
+    dec_ms, lay_ms, ver_ms = (float(v) for v in t.mean(0))
+    acc_ms = ver_ms - lay_ms
+    na = n_acc.cpu().numpy()
+    tok_step = float(np.mean(na + 1))
+    per_draft = float(sum((na > j).sum() for j in range(D)) / max(1, sum((na >= j).sum() for j in range(D))))
+    value = tok_step / (ver_ms * 1e-3)
+    dec_tok_s = 1.0 / (dec_ms * 1e-3)
+    log("bench: decode layer %.2f us; verify layer (T=%d) %.2f us + acceptance %.2f us = %.2f us" %
+        (dec_ms * 1e3, T, lay_ms * 1e3, acc_ms * 1e3, ver_ms * 1e3))
+    log("bench: %.2f tokens per verify step (%.0f%% of drafts kept): %.0f tok/s vs %.0f tok/s plain decode" %
+        (tok_step, 100 * per_draft, value, dec_tok_s))
+    # acceptance step: logit bytes read once by the stats pass (the draw pass
+    # rereads two rows); the layer's weights as in the decode line
+    acc_bytes = 4.0 * V * (2 * D + 1)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) or reps == 0:
+            a = mi[reps % n_inputs]
+            oracle.mtp_accept(a[0], a[1], a[2], tau, a[3])
+            reps += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": reps / el, "unit": "acceptance steps/s (oracle, one sequence, V=%d)" % V,
+               "cores": oracle.lib().oracle_num_threads(), "kind": "oracle",
+               "sample": "%d acceptance steps of the rotating inputs; the verify layer itself is in the "
+                         "decode_int4 line's baseline" % reps}
+    out = {
+        "metric": "MTP verify tokens/s (one int4 MoE layer + acceptance, synthetic drafts)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ver_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8+f64", "data": "synthetic (seeded layer weights, N(0,1) tokens, target logits N(0,9), "
+                                   "draft logits = target + N(0,1), %d rotating inputs, caches flushed)" % n_inputs,
+        "config": {"workload": "mtp_int4", "T": T, "drafts": D, "vocab": V, "temperature": tau,
+                   "hidden": wl.hidden, "inter": wl.inter, "n_experts": wl.n_experts, "top_k": wl.top_k,
+                   "wbits": wl.wbits, "path": "gemv"},
+        "roofline": {"bound": "hbm", "kernel": "mtp_accept", "achieved": acc_bytes / (acc_ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": acc_bytes / (acc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_per_launch": acc_bytes / 1e9, "avg_launch_us": acc_ms * 1e3},
+        "detail": {"tokens_per_step": tok_step, "draft_acceptance": per_draft,
+                   "verify_layer_us": lay_ms * 1e3, "acceptance_us": acc_ms * 1e3,
+                   "decode_layer_us": dec_ms * 1e3, "decode_tokens_per_s": dec_tok_s},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -240,6 +240,45 @@ int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *pe
                 int32_t *off, int32_t *inv, void *ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
 
+/* ---------------------------------------------------------------- MTP draft verification */
+/* moe_mtp_accept -- the acceptance step after a verify forward (GeekNews
+ * #31297, implemented features: the multi-token-prediction head drafts
+ * tokens, the main model verifies them in one batched forward whose MoE
+ * layers run as moe_layer_forward with T = 1 + D, and rejection sampling
+ * keeps sampled output lossless; useful options: --temp, 0 = greedy).
+ * For each of B sequences with D drafts:
+ *   tau > 0: p_i, q_i = softmax(logits_i / tau) in fp64; draft x_i is kept
+ *     while u[i] * q_i(x_i) < p_i(x_i) (i ascending); at the first refusal
+ *     (i = j) the emitted token is the inverse-CDF draw with u[D], in
+ *     ascending token order, of max(0, p_j - q_j) (of p_j if that has no
+ *     mass); after D kept drafts it is the draw of p_D.  This is speculative
+ *     sampling (Leviathan et al. 2023; Chen et al. 2023); no nucleus filter.
+ *   tau = 0: drafts are kept while they equal the target's argmax (lowest
+ *     token on ties) and the emitted token is the argmax at the first
+ *     mismatch, or of p_D.
+ * All device pointers:
+ *   draft    [B][D] int32, tokens in [0, V) (one outside is refused)
+ *   p_logits [B][D+1][V] fp32: the target model's logits at the D+1
+ *            verified positions (position i scores the token after draft i-1)
+ *   q_logits [B][D][V] fp32: the draft model's logits each draft was drawn
+ *            from (nullable when D = 0)
+ *   u        [B][D+1] fp64 uniforms in [0, 1), the caller's random numbers:
+ *            u[i] tests draft i, u[D] draws the emitted token
+ *   n_acc    [B] out: drafts kept (0 .. D)
+ *   next     [B] out: the token emitted after them
+ * Sizes: D <= 16, V <= 1,048,576; V % 4 == 0 with 16-byte aligned rows
+ * takes vector loads.  Logits must be finite.  Every token decision is made
+ * in fp64; the probabilities come from per-4096-token chunk sums combined
+ * in a fixed order, so results are run-to-run identical (and agree with a
+ * sequential fp64 evaluation except where a decision lies within rounding
+ * of its boundary).
+ * ws: at least moe_mtp_accept_workspace_bytes(B, D, V) bytes, 256-byte
+ *   aligned.  Three launches (two when tau = 0). */
+int moe_mtp_accept(int32_t B, int32_t D, int32_t V, const int32_t *draft, const float *p_logits,
+                   const float *q_logits, float tau, const double *u, int32_t *n_acc, int32_t *next,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_mtp_accept_workspace_bytes(int32_t B, int32_t D, int32_t V);
+
 #ifdef __cplusplus
 }
 #endif

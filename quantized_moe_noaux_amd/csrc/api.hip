@@ -424,4 +424,24 @@ int moe_permute(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *pe
     return hip_rc(launch_permute(idx, T, k, E, perm, off, inv, static_cast<int32_t *>(ws), nullptr, 0, stream));
 }
 
+size_t moe_mtp_accept_workspace_bytes(int32_t B, int32_t D, int32_t V)
+{
+    if (B < 0 || D < 0 || V < 1) return 0;
+    return mtp_workspace_bytes(B, D, V);
+}
+
+int moe_mtp_accept(int32_t B, int32_t D, int32_t V, const int32_t *draft, const float *p_logits,
+                   const float *q_logits, float tau, const double *u, int32_t *n_acc, int32_t *next, void *ws,
+                   size_t ws_bytes, hipStream_t stream)
+{
+    if (B < 0 || D < 0 || V < 1 || !(tau >= 0.f) || !(tau < INFINITY)) return MOE_EINVAL;
+    if (D > kMtpMaxDraft || mtp_chunks(V) > kMtpMaxChunks) return MOE_EUNSUPPORTED;
+    if (B == 0) return MOE_OK;
+    if (!p_logits || !u || !n_acc || !next || !ws || (D > 0 && (!draft || !q_logits))) return MOE_EINVAL;
+    if (!al(p_logits, 4) || !al(u, 8) || !al(ws, 256) || (D > 0 && !al(q_logits, 4))) return MOE_EINVAL;
+    if (ws_bytes < mtp_workspace_bytes(B, D, V)) return MOE_EWORKSPACE;
+    return hip_rc(launch_mtp_accept(B, D, V, draft, p_logits, D > 0 ? q_logits : p_logits, (double)tau, u, n_acc,
+                                    next, ws, stream));
+}
+
 } // extern "C"

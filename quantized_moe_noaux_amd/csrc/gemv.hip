@@ -803,13 +803,17 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     auto la_of = [&](int p) { return reinterpret_cast<uint32_t *>(act + p * pair_bytes); };
     auto ld_of = [&](int p) { return reinterpret_cast<float *>(act + p * pair_bytes + I); };
     auto lq_of = [&](int p) { return reinterpret_cast<int *>(act + p * pair_bytes + I + 4 * nbh); };
-    // every slot's kDsRows row scales, [slot][row]
-    float *lsc = reinterpret_cast<float *>(act + (size_t)pd.P * pair_bytes);
+    // every slot's kDsRows row scales, [slot][row], after a.down_pmax pairs
+    float *lsc = reinterpret_cast<float *>(act + (size_t)a.down_pmax * pair_bytes);
 
     for (int i = tid; i < pd.words; i += kDsThreads) plan[i] = a.plan[i];
     __syncthreads();
     if (!plan_ok(plan, pd, a.T, a.E) || plan[0] < 1) return;
     const int S = plan[0];
+    // every slot's pairs must fit one staging batch (the host sizes
+    // a.down_pmax >= T; a plan that breaks it writes nothing)
+    for (int u = 0; u < S; u++)
+        if (plan[pd.o_n + u] > a.down_pmax) return;
     // thread i < T * kDsRows writes output (token i / kDsRows, row i % kDsRows);
     // with MOE_ACCUMULATE it adds to the value read here, at the start
     static_assert(kGemvMaxT * kDsRows <= kDsThreads, "one output per thread");
@@ -845,6 +849,27 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
 #pragma unroll
         for (int j = 0; j < NSTEP; j++) wb[j] = ld16(src + j * step_bytes);
     };
+    constexpr int SB = stage_batch(WB);
+    const int pmax = a.down_pmax, nsc = S * kDsRows;
+    const int p0s = (plan[pd.o_e + S - 1] == -1) ? plan[pd.o_p0 + S - 1] : 0x7fffffff;
+    int bend = 0, rbase = 0, rcount = 0, nst = 0;  // the batch: slots .. bend - 1
+    auto batch_from = [&](int s0) {
+        int np = 0, nr = 0, s1 = s0;
+        while (s1 < S) {
+            const int n = plan[pd.o_n + s1];
+            if (np + n > pmax) break;
+            np += n;
+            if (plan[pd.o_e + s1] != -1) nr += n;
+            s1++;
+        }
+        bend = s1;
+        rbase = plan[pd.o_p0 + s0];
+        rcount = nr;
+        nst = np * cpr;
+    };
+    // staged index of pair p of the current batch
+    auto lidx = [&](int p) { return p >= p0s ? rcount + (p - p0s) : p - rbase; };
+    auto pair_of = [&](int i) { return i < rcount ? rbase + i : p0s + (i - rcount); };
     // a slot's pairs list its tokens in ascending order: walk the tokens in
     // compile-time order so every accumulator index is static
     auto use_slot = [&](int u, const uint4 (&wb)[NSTEP]) {
@@ -856,69 +881,89 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
 #pragma unroll
         for (int tt = 0; tt < TT; tt++) {
             if (q < n && plan[pd.o_t + p0 + q] == tt) {
-                const int p = p0 + q;
+                const int p = p0 + q, li = lidx(p);
                 const float pw = __int_as_float(plan[pd.o_w + p]);
                 Act<WB> A;
-                act_from_lds<WB>(A, la_of(p), ld_of(p), lq_of(p), pos);
+                act_from_lds<WB>(A, la_of(li), ld_of(li), lq_of(li), pos);
 #pragma unroll
                 for (int j = 0; j < NSTEP; j++) acc[tt][j] += A.dot(wb[j]) * (pw * sb[j]);
                 q++;
             }
         }
     };
-    // Staging of every pair's int8 h and every slot's row scales: SB chunks
-    // (and one scale) per thread per batch of loads; spare lanes of the last
-    // batch take the last chunk or scale again (same value, same place), so
-    // no load or store sits under a per-lane branch.
-    constexpr int SB = stage_batch(WB);
-    const PlanPairs pq = plan_pairs(plan, pd);
-    const int nst = pq.count() * cpr, nsc = S * kDsRows;
+    // Staging.  Every slot's row scales go to LDS once.  The pairs' int8 h
+    // go in batches of consecutive slots whose pairs fit the LDS pair space
+    // (a.down_pmax pairs): the whole plan at one token, a few batches for
+    // larger verify batches, so every routed expert of the batch is read
+    // once whatever its size.  A batch holds the routed pairs of its slots
+    // (consecutive pair numbers from rbase) and, when it reaches the last
+    // slot, the shared expert's pairs after them.  SB chunks (and one scale)
+    // per thread per round of loads; spare lanes of the last round take the
+    // last chunk or scale again (same value, same place), so no load or
+    // store sits under a per-lane branch.
     Act<WB> sa[SB];
     int scs[SB];
     float scv;
     int sci;
-    auto stage_issue = [&](int c0, int i0) {
+    auto stage_issue = [&](int c0) {
 #pragma unroll
         for (int b = 0; b < SB; b++) {
             scs[b] = min(c0 + b * kDsThreads + tid, nst - 1);
-            const int i = scs[b] / cpr, pp = scs[b] - i * cpr, p = pq(i);
+            const int i = scs[b] / cpr, pp = scs[b] - i * cpr, p = pair_of(i);
             sa[b].load_raw(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pp);
         }
-        sci = min(i0 + tid, nsc - 1);
-        const int u = sci / kDsRows;
-        scv = slot_w(u).down_s[(size_t)slot_ee(u) * a.H + row_base + sci % kDsRows];
     };
     auto stage_store = [&]() {
 #pragma unroll
         for (int b = 0; b < SB; b++) {
-            const int i = scs[b] / cpr, pp = scs[b] - i * cpr, p = pq(i);
+            const int i = scs[b] / cpr, pp = scs[b] - i * cpr;
             sa[b].finish();
-            store_act<WB>(sa[b], pp, la_of(p), ld_of(p), lq_of(p));
+            store_act<WB>(sa[b], pp, la_of(i), ld_of(i), lq_of(i));
         }
-        lsc[sci] = scv;
     };
-    // The first staging batch and then the first NB - 1 slots' rows are
-    // requested together, one plan round trip into the kernel; the staging
-    // stores wait for the staging loads only (the vector memory counter
-    // retires loads in issue order).  A plan with fewer slots requests its
-    // last slot again: straight-line code, so that wait counts exactly the
-    // loads issued after the staging.
-    stage_issue(0, 0);
+    auto scale_issue = [&](int i0) {
+        sci = min(i0 + tid, nsc - 1);
+        const int u = sci / kDsRows;
+        scv = slot_w(u).down_s[(size_t)slot_ee(u) * a.H + row_base + sci % kDsRows];
+    };
+    auto stage_rest = [&](int c0) {
+        for (; c0 < nst; c0 += SB * kDsThreads) {
+            stage_issue(c0);
+            stage_store();
+        }
+    };
+    // The first round of the first batch, the first scales and then the
+    // first NB - 1 slots' rows are requested together, one plan round trip
+    // into the kernel; the staging stores wait for the staging loads only
+    // (the vector memory counter retires loads in issue order).  A plan with
+    // fewer slots requests its last slot again: straight-line code, so that
+    // wait counts exactly the loads issued after the staging.
+    batch_from(0);
+    stage_issue(0);
+    scale_issue(0);
 #pragma unroll
     for (int b = 0; b < NB - 1; b++) load_slot(min(b, S - 1), wr[b]);
     // keep every load above issued before the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
     stage_store();
-    for (int c0 = SB * kDsThreads, i0 = kDsThreads; c0 < nst || i0 < nsc; c0 += SB * kDsThreads, i0 += kDsThreads) {
-        stage_issue(min(c0, nst - 1), min(i0, nsc - 1));
-        stage_store();
+    lsc[sci] = scv;
+    for (int i0 = kDsThreads; i0 < nsc; i0 += kDsThreads) {
+        scale_issue(i0);
+        lsc[sci] = scv;
     }
+    stage_rest(SB * kDsThreads);
     __syncthreads();
     for (int u0 = 0; u0 < S; u0 += NB) {
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             const int u = u0 + b;
             if (u + NB - 1 < S) load_slot(u + NB - 1, wr[(b + NB - 1) % NB]);
+            if (u < S && u == bend) {  // next batch of pairs (uniform)
+                __syncthreads();
+                batch_from(u);
+                stage_rest(0);
+                __syncthreads();
+            }
             if (u < S) use_slot(u, wr[b]);
         }
     }
@@ -953,7 +998,7 @@ template <int WB, int RPS, int TT>
 static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
     constexpr int NB = down_ring(WB, TT);
-    k_down_sw<WB, RPS, TT, NB><<<a.H / kDsRows, kDsThreads, down_lds_bytes(WB, a.I, pd), st>>>(a, cc, pd);
+    k_down_sw<WB, RPS, TT, NB><<<a.H / kDsRows, kDsThreads, down_sw_lds_bytes(WB, a.I, pd, a.down_pmax), st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
 
@@ -1002,6 +1047,32 @@ static int run_down(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, h
     default: return FN<__VA_ARGS__, 8>(a, cc, pd, st);                          \
     }
 
+// The production row widths take the token count of the chunk exactly (up
+// to 6; 7 and 8 share 8): per-token accumulators and activations are live
+// registers, and a kernel sized for 8 tokens runs one wave per SIMD.
+#define MOE_SW_TTX(FN, ...)                                                     \
+    switch (a.T <= 6 ? a.T : 8) {                                               \
+    case 1: return FN<__VA_ARGS__, 1>(a, cc, pd, st);                           \
+    case 2: return FN<__VA_ARGS__, 2>(a, cc, pd, st);                           \
+    case 3: return FN<__VA_ARGS__, 3>(a, cc, pd, st);                           \
+    case 4: return FN<__VA_ARGS__, 4>(a, cc, pd, st);                           \
+    case 5: return FN<__VA_ARGS__, 5>(a, cc, pd, st);                           \
+    case 6: return FN<__VA_ARGS__, 6>(a, cc, pd, st);                           \
+    default: return FN<__VA_ARGS__, 8>(a, cc, pd, st);                          \
+    }
+
+bool gemv_gate_up_sw(const moe_shape_t &s)
+{
+    ChunkCfg cc;
+    return chunk_cfg(s.hidden, s.wbits, cc) && gate_up_sw_kind(cc.cpr) != 0;
+}
+
+bool gemv_down_sw(const moe_shape_t &s)
+{
+    ChunkCfg cc;
+    return s.hidden % kDsRows == 0 && chunk_cfg(s.inter, s.wbits, cc) && down_sw_kind(cc.cpr) != 0;
+}
+
 bool gemv_inline_route(const moe_shape_t &s, int T)
 {
     ChunkCfg cc;
@@ -1014,29 +1085,31 @@ int launch_gate_up(const GemvArgs &a, hipStream_t st)
     if (!chunk_cfg(a.H, a.wbits, cc)) return (int)hipErrorInvalidValue;
     const PlanDims pd = plan_dims(a.T, a.rc.k, a.n_shared, a.logits == nullptr);
     const int kind = gate_up_sw_kind(cc.cpr);
-    if (kind == 1 && a.wbits == 4) { MOE_SW_TT(run_gate_up_sw, 4, 1, 1) }
+    if (kind == 1 && a.wbits == 4) { MOE_SW_TTX(run_gate_up_sw, 4, 1, 1) }
     if (kind == 1 && a.wbits == 8) { MOE_SW_TT(run_gate_up_sw, 8, 1, 1) }
     if (kind == 1 && a.wbits == 2) { MOE_SW_TT(run_gate_up_sw, 2, 1, 1) }
-    if (kind == 2 && a.wbits == 8) { MOE_SW_TT(run_gate_up_sw, 8, 2, 1) }
+    if (kind == 2 && a.wbits == 8) { MOE_SW_TTX(run_gate_up_sw, 8, 2, 1) }
     if (kind == 2 && a.wbits == 4) { MOE_SW_TT(run_gate_up_sw, 4, 2, 1) }
-    if (kind == 3 && a.wbits == 2) { MOE_SW_TT(run_gate_up_sw, 2, 1, 2) }
+    if (kind == 3 && a.wbits == 2) { MOE_SW_TTX(run_gate_up_sw, 2, 1, 2) }
     if (kind == 3 && a.wbits == 4) { MOE_SW_TT(run_gate_up_sw, 4, 1, 2) }
     MOE_DISPATCH(run_gate_up)
 }
 
-int launch_down(const GemvArgs &a, hipStream_t st)
+int launch_down(const GemvArgs &args, hipStream_t st)
 {
     ChunkCfg cc;
-    if (!chunk_cfg(a.I, a.wbits, cc)) return (int)hipErrorInvalidValue;
-    const PlanDims pd = plan_dims(a.T, a.rc.k, a.n_shared, a.logits == nullptr);
+    if (!chunk_cfg(args.I, args.wbits, cc)) return (int)hipErrorInvalidValue;
+    const PlanDims pd = plan_dims(args.T, args.rc.k, args.n_shared, args.logits == nullptr);
+    GemvArgs a = args;
+    a.down_pmax = down_pair_cap(a.wbits, a.I, pd);
     const int kind = down_sw_kind(cc.cpr);
     if (a.H % kDsRows == 0) {
-        if (kind == 1 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, 4) }
+        if (kind == 1 && a.wbits == 4) { MOE_SW_TTX(run_down_sw, 4, 4) }
         if (kind == 1 && a.wbits == 8) { MOE_SW_TT(run_down_sw, 8, 4) }
         if (kind == 1 && a.wbits == 2) { MOE_SW_TT(run_down_sw, 2, 4) }
-        if (kind == 2 && a.wbits == 8) { MOE_SW_TT(run_down_sw, 8, 2) }
+        if (kind == 2 && a.wbits == 8) { MOE_SW_TTX(run_down_sw, 8, 2) }
         if (kind == 2 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, 2) }
-        if (kind == 3 && a.wbits == 2) { MOE_SW_TT(run_down_sw, 2, 8) }
+        if (kind == 3 && a.wbits == 2) { MOE_SW_TTX(run_down_sw, 2, 8) }
         if (kind == 3 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, 8) }
     }
     MOE_DISPATCH(run_down)

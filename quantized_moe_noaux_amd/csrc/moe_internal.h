@@ -75,22 +75,57 @@ inline size_t down_lds_bytes(int wbits, int I, const PlanDims &pd)
     return sizeof(int) * (size_t)((pd.words + 3) & ~3) + (size_t)pd.P * act_lds_bytes(wbits, I) +
            sizeof(float) * (size_t)pd.S * kGemvDownRows;
 }
+// The row-sweep down kernel stages the pairs' h in batches of whole slots:
+// the pairs that fit the LDS left by the plan and the slots' row scales
+// (at least kGemvMaxT, the most pairs one slot can have).
+inline int down_pair_cap(int wbits, int I, const PlanDims &pd)
+{
+    const size_t fixed = sizeof(int) * (size_t)((pd.words + 3) & ~3) + sizeof(float) * (size_t)pd.S * kGemvDownRows;
+    const size_t per = act_lds_bytes(wbits, I);
+    const int cap = fixed < (size_t)kGemvMaxLdsAct ? (int)(((size_t)kGemvMaxLdsAct - fixed) / per) : 0;
+    return cap < pd.P ? cap : pd.P;
+}
+inline size_t down_sw_lds_bytes(int wbits, int I, const PlanDims &pd, int pmax)
+{
+    return sizeof(int) * (size_t)((pd.words + 3) & ~3) + (size_t)pmax * act_lds_bytes(wbits, I) +
+           sizeof(float) * (size_t)pd.S * kGemvDownRows;
+}
+bool gemv_gate_up_sw(const moe_shape_t &s);
+bool gemv_down_sw(const moe_shape_t &s);
 // LDS of the gate/up kernel: static plan / routing scratch plus Tc tokens of
 // staged activations over H.
 constexpr size_t kGateUpStaticLds = 12 * 1024;
 inline size_t gate_up_lds_bytes(int wbits, int H, int Tc) { return kGateUpStaticLds + Tc * act_lds_bytes(wbits, H); }
 // tokens per batch-union chunk: the largest count <= kGemvMaxT whose LDS fits
 // (0 if not even one token fits)
+// (the row-sweep kernels read x directly and stage h in batches, so only
+// the other kernels' full staging bounds the chunk)
 inline int gemv_chunk_tokens(const moe_shape_t &s, int T)
 {
+    const bool gsw = gemv_gate_up_sw(s), dsw = gemv_down_sw(s);
     for (int tc = (T < kGemvMaxT ? T : kGemvMaxT); tc >= 1; tc--) {
         const PlanDims pd = plan_dims(tc, s.top_k, s.n_shared, false);
-        if (down_lds_bytes(s.wbits, s.inter, pd) <= (size_t)kGemvMaxLdsAct &&
-            gate_up_lds_bytes(s.wbits, s.hidden, tc) <= (size_t)kGemvMaxLdsAct)
+        const bool down_ok = dsw ? down_pair_cap(s.wbits, s.inter, pd) >= (tc < pd.P ? tc : pd.P)
+                                 : down_lds_bytes(s.wbits, s.inter, pd) <= (size_t)kGemvMaxLdsAct;
+        if (down_ok && (gsw || gate_up_lds_bytes(s.wbits, s.hidden, tc) <= (size_t)kGemvMaxLdsAct))
             return tc;
     }
     return 0;
 }
+
+// ---------------------------------------------------------------- MTP draft verification
+constexpr int kMtpMaxDraft = 16;   // drafts per sequence
+constexpr int kMtpChunk = 4096;    // tokens per chunk of a logit row
+constexpr int kMtpMaxChunks = 256; // chunks per row: vocabularies up to 1,048,576 tokens
+inline int mtp_chunks(int V) { return (V + kMtpChunk - 1) / kMtpChunk; }
+// per-(row, chunk) stats: 16 bytes each, rows = B * (2D + 1)
+inline size_t mtp_stats_bytes(int B, int D, int V) { return align256((size_t)16 * B * (2 * D + 1) * mtp_chunks(V)); }
+inline size_t mtp_workspace_bytes(int B, int D, int V)
+{
+    return mtp_stats_bytes(B, D, V) + align256((size_t)16 * B * mtp_chunks(V));
+}
+int launch_mtp_accept(int B, int D, int V, const int32_t *draft, const float *p, const float *q, double tau,
+                      const double *u, int32_t *n_acc, int32_t *next, void *ws, hipStream_t st);
 
 struct GemvWs {
     size_t logits, xq, xd, plan, qh, dh, total;
@@ -149,6 +184,8 @@ struct GemvArgs {
     int accumulate;
     // one token, routed by the gate/up workgroups themselves (no plan launch)
     int inline_route;
+    // pairs the row-sweep down kernel stages at a time (down_pair_cap)
+    int down_pmax;
 };
 // Whether a T-token call of this shape routes inside the gate/up launch
 // (one token, row-sweep gate/up kernel) instead of in a plan launch.

@@ -69,6 +69,8 @@ def _load():
         "moe_rmsnorm": (ctypes.c_int, [vp, vp, ctypes.c_double, i32, i32, vp, vp]),
         "moe_permute": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
         "moe_permute_workspace_bytes": (sz, [i32, i32, i32]),
+        "moe_mtp_accept": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]),
+        "moe_mtp_accept_workspace_bytes": (sz, [i32, i32, i32]),
         "moe_stack_forward": (ctypes.c_int, [P(moe_shape_t), vp, i32, P(moe_layer_t), i32, ctypes.c_double,
                                              vp, vp, u32, vp, sz, vp]),
         "moe_stack_workspace_bytes": (sz, [P(moe_shape_t), i32, u32]),
@@ -221,3 +223,18 @@ def moe_stack_forward(sh, x, layer_array, eps, ws, idx_out=None, w_out=None, fla
     _chk("moe_stack_forward", lib.moe_stack_forward(
         ctypes.byref(sh), _ptr(x, torch.float32), x.shape[0], layer_array, len(layer_array), eps,
         _ptr(idx_out, torch.int32), _ptr(w_out, torch.float32), flags, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_mtp_accept_workspace_bytes(B, D, V):
+    return lib.moe_mtp_accept_workspace_bytes(B, D, V)
+
+
+def moe_mtp_accept(draft, p_logits, q_logits, tau, u, n_acc, next_tok, ws, stream=None):
+    """draft [B][D] int32, p_logits [B][D+1][V] and q_logits [B][D][V] float32,
+    u [B][D+1] float64 (device tensors); writes n_acc and next_tok [B] int32."""
+    B, D1, V = p_logits.shape
+    D = D1 - 1
+    _chk("moe_mtp_accept", lib.moe_mtp_accept(
+        B, D, V, _ptr(draft, torch.int32) if D else None, _ptr(p_logits, torch.float32),
+        _ptr(q_logits, torch.float32) if D else None, float(tau), _ptr(u, torch.float64),
+        _ptr(n_acc, torch.int32), _ptr(next_tok, torch.int32), _ptr(ws), ws.numel(), _stream(stream)))

@@ -73,7 +73,7 @@ def test_stage_count(m):
     # grouped path: logits, top-k, quant, permute, gate/up, down, combine
     assert m.moe_layer_stage_count(sh, 2048) == 7
     assert m.moe_layer_stage_count(sh, 1, m.MOE_PATH_GROUPED) == 7
-    assert m.moe_layer_stage_count(sh, 2048, m.MOE_PATH_GEMV) > 2 + 3 * 256   # chunks of <= 8 tokens
+    assert m.moe_layer_stage_count(sh, 2048, m.MOE_PATH_GEMV) == 2 + 3 * 256  # chunks of 8 tokens
     assert m.moe_layer_stage_count(sh, 1, 3) < 0
 
 
@@ -158,3 +158,23 @@ def test_other_entry_point_errors(m):
                             1 << 20, 1 << 30, None) == m.MOE_EINVAL      # expert out of range
     assert L.moe_permute(1 << 12, 4, 8, 600, 1 << 13, 1 << 14, 1 << 15, 1 << 20, 1 << 20,
                          None) == m.MOE_EUNSUPPORTED
+
+
+def test_mtp_accept_argument_checks(m):
+    """moe_mtp_accept rejects bad arguments before any launch (no GPU)."""
+    L = m.lib
+    P, Q, U, N, X, D_, WS = (k << 16 for k in range(1, 8))
+    need = L.moe_mtp_accept_workspace_bytes(2, 4, 320000)
+    assert need >= 16 * 2 * 9 * 79 + 16 * 2 * 79 and need % 256 == 0
+    assert L.moe_mtp_accept_workspace_bytes(-1, 4, 10) == 0
+    assert L.moe_mtp_accept(-1, 4, 100, D_, P, Q, 0.7, U, N, X, WS, need, None) == m.MOE_EINVAL
+    assert L.moe_mtp_accept(2, 4, 0, D_, P, Q, 0.7, U, N, X, WS, need, None) == m.MOE_EINVAL
+    assert L.moe_mtp_accept(2, 4, 100, D_, P, Q, -0.5, U, N, X, WS, need, None) == m.MOE_EINVAL
+    assert L.moe_mtp_accept(2, 4, 100, D_, P, Q, float("nan"), U, N, X, WS, need, None) == m.MOE_EINVAL
+    assert L.moe_mtp_accept(2, 17, 100, D_, P, Q, 0.7, U, N, X, WS, need, None) == m.MOE_EUNSUPPORTED
+    assert L.moe_mtp_accept(2, 4, 4096 * 256 + 1, D_, P, Q, 0.7, U, N, X, WS, 1 << 40, None) == m.MOE_EUNSUPPORTED
+    assert L.moe_mtp_accept(2, 4, 100, None, P, Q, 0.7, U, N, X, WS, need, None) == m.MOE_EINVAL
+    assert L.moe_mtp_accept(2, 4, 100, D_, P, None, 0.7, U, N, X, WS, need, None) == m.MOE_EINVAL
+    assert L.moe_mtp_accept(2, 4, 100, D_, P + 2, Q, 0.7, U, N, X, WS, need, None) == m.MOE_EINVAL  # misaligned
+    assert L.moe_mtp_accept(2, 4, 320000, D_, P, Q, 0.7, U, N, X, WS, need - 1, None) == m.MOE_EWORKSPACE
+    assert L.moe_mtp_accept(0, 4, 100, None, None, None, 0.7, None, None, None, None, 0, None) == m.MOE_OK
