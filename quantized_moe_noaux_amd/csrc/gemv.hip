@@ -788,7 +788,7 @@ constexpr bool kStageFirst = true;
 
 // down/combine: a step reads RPS consecutive down rows of one slot (4 KB);
 // kDsRows rows per workgroup, every slot in turn, prefetching the next slot.
-template <int WB, int RPS, int TT, int NB>
+template <int WB, int RPS, int TT, int NB, bool MB>
 __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -812,8 +812,10 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     const int S = plan[0];
     // every slot's pairs must fit one staging batch (the host sizes
     // a.down_pmax >= T; a plan that breaks it writes nothing)
-    for (int u = 0; u < S; u++)
-        if (plan[pd.o_n + u] > a.down_pmax) return;
+    if constexpr (MB) {
+        for (int u = 0; u < S; u++)
+            if (plan[pd.o_n + u] > a.down_pmax) return;
+    }
     // thread i < T * kDsRows writes output (token i / kDsRows, row i % kDsRows);
     // with MOE_ACCUMULATE it adds to the value read here, at the start
     static_assert(kGemvMaxT * kDsRows <= kDsThreads, "one output per thread");
@@ -938,7 +940,12 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     // (the vector memory counter retires loads in issue order).  A plan with
     // fewer slots requests its last slot again: straight-line code, so that
     // wait counts exactly the loads issued after the staging.
-    batch_from(0);
+    if constexpr (MB) {
+        batch_from(0);
+    } else {  // one batch: every pair (no data-dependent walk before the first loads)
+        const PlanPairs pq = plan_pairs(plan, pd);
+        bend = S; rbase = 0; rcount = pq.R; nst = pq.count() * cpr;
+    }
     stage_issue(0);
     scale_issue(0);
 #pragma unroll
@@ -958,7 +965,7 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
         for (int b = 0; b < NB; b++) {
             const int u = u0 + b;
             if (u + NB - 1 < S) load_slot(u + NB - 1, wr[(b + NB - 1) % NB]);
-            if (u < S && u == bend) {  // next batch of pairs (uniform)
+            if (MB && u < S && u == bend) {  // next batch of pairs (uniform)
                 __syncthreads();
                 batch_from(u);
                 stage_rest(0);
@@ -998,7 +1005,11 @@ template <int WB, int RPS, int TT>
 static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
     constexpr int NB = down_ring(WB, TT);
-    k_down_sw<WB, RPS, TT, NB><<<a.H / kDsRows, kDsThreads, down_sw_lds_bytes(WB, a.I, pd, a.down_pmax), st>>>(a, cc, pd);
+    const size_t lds = down_sw_lds_bytes(WB, a.I, pd, a.down_pmax);
+    // one staging batch holds every pair (one token at the production
+    // shapes): the kernel without the batch switch in its slot loop
+    if (a.down_pmax >= pd.P) k_down_sw<WB, RPS, TT, NB, false><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
+    else k_down_sw<WB, RPS, TT, NB, true><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
 
