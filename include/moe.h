@@ -273,7 +273,7 @@ size_t moe_permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
  * sequential fp64 evaluation except where a decision lies within rounding
  * of its boundary).
  * ws: at least moe_mtp_accept_workspace_bytes(B, D, V) bytes, 256-byte
- *   aligned.  Three launches (two when tau = 0). */
+ *   aligned.  Four launches (two when tau = 0). */
 int moe_mtp_accept(int32_t B, int32_t D, int32_t V, const int32_t *draft, const float *p_logits,
                    const float *q_logits, float tau, const double *u, int32_t *n_acc, int32_t *next,
                    void *ws, size_t ws_bytes, hipStream_t stream);

@@ -14,20 +14,20 @@
 // argmax (lowest index on ties) and emits the argmax at the first mismatch.
 // Everything that decides a token is fp64.
 //
-// Three launches over logit rows cut into chunks of kAcChunk tokens:
-//  k_ac_stats  per (row, chunk): the chunk's max logit, its first argmax
-//              and sum exp((z - max) / tau)
-//  k_ac_mass   per (sequence, chunk): the decision (every workgroup derives
-//              it from the stats: the drafts' probabilities are
-//              exp((z - M) / tau) / Z with M, Z combined over chunks in
-//              chunk order), then the chunk's mass of the distribution the
-//              emitted token is drawn from (and of p, for a residual
-//              without mass)
-//  k_ac_pick   per sequence: the decision again, the chunk where the
-//              cumulative mass crosses u_D * total (chunk order), and the
-//              token inside it (a block scan in token order)
-// Greedy needs only the stats and the pick.  Fixed reduction orders: the
-// results are run-to-run identical.
+// Four launches (two for greedy):
+//  k_ac_stats   per (row, 4096-token chunk): the chunk's max logit, its first
+//               argmax and sum exp((z - max) / tau)
+//  k_ac_decide  per sequence: each row's max and normaliser combined over
+//               its chunks in chunk order, the drafts' probabilities
+//               exp((z - M) / tau) / Z and the walk over the drafts; writes
+//               the kept count (and, greedy, the argmax token)
+//  k_ac_mass    per (sequence, 1024-token chunk): every token's weight in
+//               the distribution the emitted token is drawn from, and the
+//               chunk's masses of it and of p
+//  k_ac_pick    per sequence: the chunk where the cumulative mass crosses
+//               u_D * total (a block scan in chunk order) and the token
+//               inside it (a block scan in token order)
+// Fixed reduction orders: the results are run-to-run identical.
 #include "moe_dev.h"
 #include "moe_internal.h"
 
@@ -36,6 +36,8 @@ namespace moe {
 constexpr int kAcThreads = 256;
 constexpr int kAcPer = 16;                           // tokens per thread per chunk
 constexpr int kAcChunk = kAcThreads * kAcPer;        // 4096
+constexpr int kAcMassChunk = kAcThreads * 4;         // 1024: tokens per draw chunk
+static_assert(kAcMassChunk == kMtpDrawChunk, "draw chunk size (workspace sizing)");
 static_assert(kAcChunk == kMtpChunk, "chunk size (workspace sizing)");
 
 struct AcStat {
@@ -54,7 +56,20 @@ struct AcArgs {
     const double *u;            // [B][D+1]
     int32_t *n_acc, *next;      // [B]
     AcStat *stats;              // [B][2D+1][C]: rows 0..D target, D+1.. draft model
-    double2 *mass;              // [B][C]: (draw mass, target mass)
+    struct AcDec *dec;          // [B]: the decision
+    double2 *mass;              // [B][CM]: (draw mass, target mass) per 1024-token chunk
+    double *w;                  // [B][CM * 1024]: every token's weight in the draw
+    int CM;                     // draw chunks per row
+};
+
+// The decision of one sequence, as k_ac_decide writes it for the draw: the
+// kept drafts, whether the emitted token is drawn from the residual of the
+// target and draft rows (row_p, row_q) or from the target row alone, and the
+// rows' max logits and normalisers.
+struct AcDec {
+    int j, resid, row_p, row_q;
+    float Mp, Mq;
+    double Zp, Zq;
 };
 
 __device__ __forceinline__ const float *ac_row(const AcArgs &a, int b, int r)
@@ -239,50 +254,83 @@ __device__ __forceinline__ AcDecision ac_decide(const AcArgs &a, int b, AcDecLds
     return d;
 }
 
-// weight of token x in the draw (residual or target) and its target mass
-__device__ __forceinline__ void ac_weights(const AcDecision &d, double tau, float zp, float zq, double &w, double &pw)
+// ---------------------------------------------------------------- decision launch
+__global__ __launch_bounds__(kAcThreads) void k_ac_decide(const AcArgs a)
 {
-    const double P = exp(((double)zp - (double)d.np.M) / tau) / d.np.Z;
+    __shared__ AcDecLds dl;
+    const int b = blockIdx.x;
+    const AcDecision d = ac_decide(a, b, dl);
+    if (threadIdx.x == 0) {
+        AcDec o;
+        o.j = d.j;
+        o.resid = d.resid;
+        o.row_p = d.row_p;
+        o.row_q = d.resid ? a.D + 1 + d.j : d.row_p;
+        o.Mp = d.np.M; o.Zp = d.np.Z;
+        o.Mq = d.nq.M; o.Zq = d.nq.Z;
+        a.dec[b] = o;
+        a.n_acc[b] = d.j;
+        if (a.tau == 0.0) a.next[b] = d.np.arg;
+    }
+}
+
+// weight of a token in the draw: max(0, p - q) for a residual, else p; and
+// its target probability (p = exp((z - M) / tau) times 1 / Z)
+__device__ __forceinline__ void ac_weight(const AcDec &d, double tau, double ip, double iq, float zp, float zq,
+                                          double &w, double &pw)
+{
+    const double P = exp(((double)zp - (double)d.Mp) / tau) * ip;
     pw = P;
     if (d.resid) {
-        const double Q = exp(((double)zq - (double)d.nq.M) / tau) / d.nq.Z;
+        const double Q = exp(((double)zq - (double)d.Mq) / tau) * iq;
         w = P > Q ? P - Q : 0.0;
     } else {
         w = P;
     }
 }
 
-// ---------------------------------------------------------------- chunk masses
+// ---------------------------------------------------------------- draw weights and chunk masses
+// One workgroup per (sequence, 1024-token chunk): thread t takes tokens
+// c0 + 4t .. +3 (one float4 per row), stores their draw weights and adds
+// the chunk's draw and target masses (fixed order).
 template <bool VEC>
 __global__ __launch_bounds__(kAcThreads) void k_ac_mass(const AcArgs a)
 {
-    __shared__ AcDecLds dl;
     __shared__ double sw[kAcThreads / kWave], sp[kAcThreads / kWave];
-    const int c = blockIdx.x, b = blockIdx.y;
-    const AcDecision d = ac_decide(a, b, dl);
-    float zp[kAcPer], zq[kAcPer];
-    int pos[kAcPer];
-    ac_load<VEC>(ac_row(a, b, d.row_p), a.V, c * kAcChunk, zp, pos);
-    if (d.resid) ac_load<VEC>(ac_row(a, b, a.D + 1 + d.j), a.V, c * kAcChunk, zq, pos);
-    else {
+    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const AcDec d = a.dec[b];
+    const float *rp = ac_row(a, b, d.row_p), *rq = ac_row(a, b, d.row_q);
+    const int x0 = c * kAcMassChunk + 4 * tid;
+    float zp[4], zq[4];
+    if constexpr (VEC) {
+        const float4 vp = reinterpret_cast<const float4 *>(rp)[min(x0, a.V - 4) / 4];
+        const float4 vq = reinterpret_cast<const float4 *>(rq)[min(x0, a.V - 4) / 4];
+        zp[0] = vp.x; zp[1] = vp.y; zp[2] = vp.z; zp[3] = vp.w;
+        zq[0] = vq.x; zq[1] = vq.y; zq[2] = vq.z; zq[3] = vq.w;
+    } else {
 #pragma unroll
-        for (int i = 0; i < kAcPer; i++) zq[i] = zp[i];
+        for (int e = 0; e < 4; e++) { zp[e] = rp[min(x0 + e, a.V - 1)]; zq[e] = rq[min(x0 + e, a.V - 1)]; }
     }
-    double w = 0.0, pw = 0.0;
+    const double ip = 1.0 / d.Zp, iq = 1.0 / d.Zq;
+    double wv[4], w = 0.0, pw = 0.0;
 #pragma unroll
-    for (int i = 0; i < kAcPer; i++) {
+    for (int e = 0; e < 4; e++) {
         double wi, pi;
-        ac_weights(d, a.tau, zp[i], zq[i], wi, pi);
-        const bool ok = pos[i] < a.V;
-        w += ok ? wi : 0.0;
+        ac_weight(d, a.tau, ip, iq, zp[e], zq[e], wi, pi);
+        const bool ok = x0 + e < a.V;
+        wv[e] = ok ? wi : 0.0;
+        w += wv[e];
         pw += ok ? pi : 0.0;
     }
+    double2 *dst = reinterpret_cast<double2 *>(a.w + (size_t)b * a.CM * kAcMassChunk + x0);
+    dst[0] = make_double2(wv[0], wv[1]);
+    dst[1] = make_double2(wv[2], wv[3]);
     w = wave_sum_d(w);
     pw = wave_sum_d(pw);
     if (lane_id() == 0) { sw[wave_id()] = w; sp[wave_id()] = pw; }
     __syncthreads();
-    if (threadIdx.x == 0)
-        a.mass[(size_t)b * a.C + c] = make_double2(((sw[0] + sw[1]) + sw[2]) + sw[3], ((sp[0] + sp[1]) + sp[2]) + sp[3]);
+    if (tid == 0)
+        a.mass[(size_t)b * a.CM + c] = make_double2(((sw[0] + sw[1]) + sw[2]) + sw[3], ((sp[0] + sp[1]) + sp[2]) + sp[3]);
 }
 
 // Exclusive scan of two doubles over the 256 threads in thread order (a wave
@@ -314,118 +362,119 @@ __device__ __forceinline__ void block_scan2(double x, double y, double &ex, doub
 }
 
 // ---------------------------------------------------------------- the draw
-// Inside the chosen chunk thread t takes the kAcPer consecutive tokens
-// c0 + 16t .. +15 (token order), so an exclusive scan of the threads'
-// sums gives every token's cumulative mass.
+// The chunk the draw falls in (thread t holds chunks 4t .. 4t+3; an
+// exclusive block scan of the threads' sums gives every chunk's cumulative
+// mass in chunk order), then the token inside it (thread t holds tokens
+// c0 + 4t .. +3, the same scan in token order).  A residual without mass
+// falls back to the target row itself (its weights recomputed here).
 __global__ __launch_bounds__(kAcThreads) void k_ac_pick(const AcArgs a)
 {
-    __shared__ AcDecLds dl;
-    __shared__ int s_chunk, s_usep, s_hit, s_lastw;
+    __shared__ int s_chunk, s_hit, s_last;
     __shared__ double s_target;
-    __shared__ double wsum[2 * kAcThreads / kWave];
+    __shared__ double red[2 * kAcThreads / kWave];
     const int b = blockIdx.x, tid = threadIdx.x;
-    const AcDecision d = ac_decide(a, b, dl);
-    if (a.tau == 0.0) {
-        if (tid == 0) { a.n_acc[b] = d.j; a.next[b] = d.np.arg; }
-        return;
-    }
-    // the chunk the draw falls in: thread c holds chunk c's masses (the
-    // draw's and the target's); an exclusive block scan in chunk order gives
-    // each chunk's cumulative mass.  A residual without mass falls back to
-    // the target itself.
-    {
-        const double2 mc = a.mass[(size_t)b * a.C + min(tid, a.C - 1)];
-        const bool live = tid < a.C;
-        double wr = live ? mc.x : 0.0, wp = live ? mc.y : 0.0;
-        double er, ep, Wr, Wp;
-        block_scan2(wr, wp, er, ep, Wr, Wp, wsum);
-        const bool use_p = !(Wr > 0.0);
-        const double w = use_p ? wp : wr, e = use_p ? ep : er;
-        const double t = a.u[(size_t)b * (a.D + 1) + a.D] * (use_p ? Wp : Wr);
-        if (tid == 0) { s_usep = use_p; s_hit = 0x7fffffff; s_lastw = -1; }
-        __syncthreads();
-        if (w > 0.0) {
-            atomicMax(&s_lastw, tid);
-            if (e + w > t) atomicMin(&s_hit, tid);
-        }
-        __syncthreads();
-        // rounding can leave the target at the total: then the last
-        // weighted token of the last chunk with weight is drawn
-        const int cs = s_hit != 0x7fffffff ? s_hit : max(s_lastw, 0);
-        if (tid == cs) { s_chunk = cs; s_target = (s_hit != 0x7fffffff) ? t - e : INFINITY; }
-        __syncthreads();
-        if (tid == 0) { s_hit = 0x7fffffff; s_lastw = -1; }
-        __syncthreads();
-    }
-    AcDecision dd = d;
-    if (s_usep) dd.resid = false;
-    const int c0 = s_chunk * kAcChunk;
-    const float *rp = ac_row(a, b, dd.row_p);
-    const float *rq = dd.resid ? ac_row(a, b, a.D + 1 + d.j) : rp;
-    double w[kAcPer];
-    double tsum = 0.0;
+    const AcDec d = a.dec[b];
+    const double2 *ms = a.mass + (size_t)b * a.CM;
+    double wr[4], wp[4], sr = 0.0, sp = 0.0;
 #pragma unroll
-    for (int i = 0; i < kAcPer; i++) {
-        const int x = c0 + kAcPer * tid + i;
-        const int xc = min(x, a.V - 1);
-        double wi, pi;
-        ac_weights(dd, a.tau, rp[xc], rq[xc], wi, pi);
-        w[i] = (x < a.V) ? wi : 0.0;
-        tsum += w[i];
+    for (int e = 0; e < 4; e++) {
+        const int c = 4 * tid + e;
+        const double2 m = ms[min(c, a.CM - 1)];
+        wr[e] = c < a.CM ? m.x : 0.0;
+        wp[e] = c < a.CM ? m.y : 0.0;
+        sr += wr[e];
+        sp += wp[e];
     }
-    // exclusive scan of the thread sums in thread order (a wave scan, then
-    // the four wave totals in order)
-    const int l = lane_id(), wv = wave_id();
-    double incl = tsum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double y = __shfl_up(incl, o);
-        if (l >= o) incl += y;
-    }
-    if (l == kWave - 1) wsum[wv] = incl;
+    double er, ep, Wr, Wp;
+    block_scan2(sr, sp, er, ep, Wr, Wp, red);
+    const bool use_p = !(Wr > 0.0);
+    const double t = a.u[(size_t)b * (a.D + 1) + a.D] * (use_p ? Wp : Wr);
+    if (tid == 0) { s_hit = 0x7fffffff; s_last = -1; }
     __syncthreads();
-    double cum = incl - tsum;
-    for (int i = 0; i < wv; i++) cum += wsum[i];
-    // the answer is the lowest token with weight whose cumulative mass
-    // passes the target; the cumulative mass only grows with the token, so
-    // each thread's first such token, minimised over threads, is it
-    const double t = s_target;
-    int hit = 0x7fffffff, lastw = -1;
+    double cum = use_p ? ep : er, tloc = 0.0;
+    int hit = 0x7fffffff, last = -1;
 #pragma unroll
-    for (int i = 0; i < kAcPer; i++) {
-        if (w[i] > 0.0) {
-            const int x = c0 + kAcPer * tid + i;
-            cum += w[i];
-            if (hit == 0x7fffffff && cum > t) hit = x;
-            lastw = x;
+    for (int e = 0; e < 4; e++) {
+        const double wc = use_p ? wp[e] : wr[e];
+        if (wc > 0.0) {
+            last = 4 * tid + e;
+            if (hit == 0x7fffffff && cum + wc > t) { hit = 4 * tid + e; tloc = t - cum; }
+            cum += wc;
         }
     }
     if (hit != 0x7fffffff) atomicMin(&s_hit, hit);
-    if (lastw >= 0) atomicMax(&s_lastw, lastw);
+    if (last >= 0) atomicMax(&s_last, last);
     __syncthreads();
-    if (tid == 0) {
-        a.n_acc[b] = d.j;
-        a.next[b] = s_hit != 0x7fffffff ? s_hit : s_lastw;
+    // rounding can leave the target at the total: then the last weighted
+    // token of the last chunk with weight is drawn
+    const bool found = s_hit != 0x7fffffff;
+    const int cs = found ? s_hit : max(s_last, 0);
+    if (found && hit == cs) s_target = tloc;
+    if (!found && tid == 0) s_target = INFINITY;
+    if (tid == 0) s_chunk = cs;
+    __syncthreads();
+    const int c0 = s_chunk * kAcMassChunk, x0 = c0 + 4 * tid;
+    double w[4], tsum = 0.0;
+    if (!use_p) {
+        const double2 *src = reinterpret_cast<const double2 *>(a.w + (size_t)b * a.CM * kAcMassChunk + x0);
+        const double2 w01 = src[0], w23 = src[1];
+        w[0] = w01.x; w[1] = w01.y; w[2] = w23.x; w[3] = w23.y;
+    } else {
+        const float *rp = ac_row(a, b, d.row_p);
+        const double ip = 1.0 / d.Zp;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const double P = exp(((double)rp[min(x0 + e, a.V - 1)] - (double)d.Mp) / a.tau) * ip;
+            w[e] = x0 + e < a.V ? P : 0.0;
+        }
     }
+#pragma unroll
+    for (int e = 0; e < 4; e++) tsum += w[e];
+    double ex, ey, tx, ty;
+    block_scan2(tsum, 0.0, ex, ey, tx, ty, red);
+    if (tid == 0) { s_hit = 0x7fffffff; s_last = -1; }
+    __syncthreads();
+    const double tt = s_target;
+    double cw = ex;
+    hit = 0x7fffffff;
+    last = -1;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        if (w[e] > 0.0) {
+            cw += w[e];
+            if (hit == 0x7fffffff && cw > tt) hit = x0 + e;
+            last = x0 + e;
+        }
+    }
+    if (hit != 0x7fffffff) atomicMin(&s_hit, hit);
+    if (last >= 0) atomicMax(&s_last, last);
+    __syncthreads();
+    if (tid == 0) a.next[b] = s_hit != 0x7fffffff ? s_hit : s_last;
 }
 
 int launch_mtp_accept(int B, int D, int V, const int32_t *draft, const float *p, const float *q, double tau,
                       const double *u, int32_t *n_acc, int32_t *next, void *ws, hipStream_t st)
 {
     AcArgs a;
-    a.B = B; a.D = D; a.V = V; a.C = (V + kAcChunk - 1) / kAcChunk;
+    a.B = B; a.D = D; a.V = V; a.C = mtp_chunks(V); a.CM = mtp_draw_chunks(V);
     a.draft = draft; a.p = p; a.q = q; a.tau = tau; a.u = u; a.n_acc = n_acc; a.next = next;
-    a.stats = reinterpret_cast<AcStat *>(ws);
-    a.mass = reinterpret_cast<double2 *>(static_cast<unsigned char *>(ws) + mtp_stats_bytes(B, D, V));
+    unsigned char *w = static_cast<unsigned char *>(ws);
+    const MtpWs L = mtp_ws(B, D, V);
+    a.stats = reinterpret_cast<AcStat *>(w + L.stats);
+    a.dec = reinterpret_cast<AcDec *>(w + L.dec);
+    a.mass = reinterpret_cast<double2 *>(w + L.mass);
+    a.w = reinterpret_cast<double *>(w + L.w);
+    static_assert(sizeof(AcDec) <= 64, "decision size (workspace sizing)");
     const bool vec = V % 4 == 0 && (((uintptr_t)p | (uintptr_t)q) & 15) == 0;
-    const dim3 gs(a.C, B * (2 * D + 1)), gm(a.C, B);
+    const dim3 gs(a.C, B * (2 * D + 1)), gm(a.CM, B);
     if (vec) k_ac_stats<true><<<gs, kAcThreads, 0, st>>>(a);
     else k_ac_stats<false><<<gs, kAcThreads, 0, st>>>(a);
+    k_ac_decide<<<B, kAcThreads, 0, st>>>(a);
     if (tau > 0.0) {
         if (vec) k_ac_mass<true><<<gm, kAcThreads, 0, st>>>(a);
         else k_ac_mass<false><<<gm, kAcThreads, 0, st>>>(a);
+        k_ac_pick<<<B, kAcThreads, 0, st>>>(a);
     }
-    k_ac_pick<<<B, kAcThreads, 0, st>>>(a);
     return (int)hipGetLastError();
 }
 

@@ -118,12 +118,26 @@ constexpr int kMtpMaxDraft = 16;   // drafts per sequence
 constexpr int kMtpChunk = 4096;    // tokens per chunk of a logit row
 constexpr int kMtpMaxChunks = 256; // chunks per row: vocabularies up to 1,048,576 tokens
 inline int mtp_chunks(int V) { return (V + kMtpChunk - 1) / kMtpChunk; }
-// per-(row, chunk) stats: 16 bytes each, rows = B * (2D + 1)
-inline size_t mtp_stats_bytes(int B, int D, int V) { return align256((size_t)16 * B * (2 * D + 1) * mtp_chunks(V)); }
-inline size_t mtp_workspace_bytes(int B, int D, int V)
+constexpr int kMtpDrawChunk = 1024;  // tokens per chunk of the draw
+inline int mtp_draw_chunks(int V) { return (V + kMtpDrawChunk - 1) / kMtpDrawChunk; }
+// workspace: per-(row, chunk) stats (16 B, rows = B * (2D + 1)), the
+// decisions (64 B per sequence), per-draw-chunk masses (16 B) and every
+// token's draw weight (8 B, whole chunks)
+struct MtpWs {
+    size_t stats, dec, mass, w, total;
+};
+inline MtpWs mtp_ws(int B, int D, int V)
 {
-    return mtp_stats_bytes(B, D, V) + align256((size_t)16 * B * mtp_chunks(V));
+    MtpWs L;
+    size_t o = 0;
+    L.stats = o; o = align256(o + (size_t)16 * B * (2 * D + 1) * mtp_chunks(V));
+    L.dec = o;   o = align256(o + (size_t)64 * B);
+    L.mass = o;  o = align256(o + (size_t)16 * B * mtp_draw_chunks(V));
+    L.w = o;     o = align256(o + (size_t)8 * B * mtp_draw_chunks(V) * kMtpDrawChunk);
+    L.total = o;
+    return L;
 }
+inline size_t mtp_workspace_bytes(int B, int D, int V) { return mtp_ws(B, D, V).total; }
 int launch_mtp_accept(int B, int D, int V, const int32_t *draft, const float *p, const float *q, double tau,
                       const double *u, int32_t *n_acc, int32_t *next, void *ws, hipStream_t st);
 
