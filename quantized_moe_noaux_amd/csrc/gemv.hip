@@ -782,12 +782,14 @@ constexpr int kDsGroups = kDsThreads / 32;
 constexpr int kDsRows = 16;      // output rows per workgroup
 static_assert(kDsRows == kGemvDownRows, "rows per down workgroup (LDS sizing)");
 
-// slots of down rows in flight ahead of use, plus the one in use
-constexpr int down_ring(int wb, int tt) { return 3; }
-constexpr bool kStageFirst = true;
+// slot buffers of the down kernel's ring: two slots of rows in flight ahead
+// of the one in use (measured on MI355X: a ring that holds every slot of a
+// one-token plan at once ran ~1.5 us slower, its first use waiting for all)
+constexpr int kDownRing = 3;
 
 // down/combine: a step reads RPS consecutive down rows of one slot (4 KB);
-// kDsRows rows per workgroup, every slot in turn, prefetching the next slot.
+// kDsRows rows per workgroup, every slot in turn through a ring of NB slot
+// buffers.  MB: the plan's pairs take more than one staging batch.
 template <int WB, int RPS, int TT, int NB, bool MB>
 __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
@@ -1004,7 +1006,7 @@ static int run_gate_up_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims 
 template <int WB, int RPS, int TT>
 static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
-    constexpr int NB = down_ring(WB, TT);
+    constexpr int NB = kDownRing;
     const size_t lds = down_sw_lds_bytes(WB, a.I, pd, a.down_pmax);
     // one staging batch holds every pair (one token at the production
     // shapes): the kernel without the batch switch in its slot loop
