@@ -93,6 +93,22 @@ def test_verify_int8_full(dev, m):
     print("verify_int8: max rel err %.3g" % rel)
 
 
+@pytest.mark.parametrize("name,wbits,T", [("decode_int4", 4, 2), ("decode_int4", 4, 5), ("decode_int4", 4, 8),
+                                          ("stack_int2", 2, 6), ("verify_int8", 8, 7)])
+def test_verify_batches_full_size(dev, m, name, wbits, T):
+    """MTP verify batches (1 + drafts) at the full shapes: one batch-union
+    chunk whatever T (the down kernel stages the pairs in slot batches when
+    they exceed its LDS), the gate/up and down kernels at the exact token
+    count; every token compared with the oracle."""
+    wl = synth.workload(name, T=T)
+    sh = m.shape_of(wl)
+    assert m.moe_layer_stage_count(sh, T, m.MOE_PATH_GEMV) == 4   # router, plan, gate/up, down
+    print("verify batch: %s T=%d" % (name, T), flush=True)
+    L = DevLayer(wl, dev, layer=3 if wl.layers > 1 else 0)
+    rel = check(m, L)
+    print("verify batch %s T=%d: max rel err %.3g" % (name, T, rel))
+
+
 def test_stack_int2_layer(dev, m):
     L = DevLayer(synth.workload("stack_int2"), dev, layer=5)
     check(m, L)
