@@ -97,7 +97,7 @@ __device__ __forceinline__ PlanPairs plan_pairs(const int *plan, const PlanDims 
 // pending flat access anywhere in a kernel makes the compiler wait for all
 // outstanding loads wherever it waits for one.
 __device__ __forceinline__ void build_plan_one(const GemvArgs &a, const PlanDims &pd, int *plan, int *s_idx,
-                                               float *s_w, TopkLds &tl)
+                                               float *s_w)
 {
     const int tid = threadIdx.x, k = a.rc.k;
     int *slot_e = plan + pd.o_e, *slot_n = plan + pd.o_n, *slot_p0 = plan + pd.o_p0;
@@ -106,7 +106,11 @@ __device__ __forceinline__ void build_plan_one(const GemvArgs &a, const PlanDims
     // one token: slots are its kept experts in ascending order, then the
     // shared expert; the pair of a routed slot is the slot itself, the
     // shared expert's pair is k (also when top-p keeps fewer experts)
-    block_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias, s_idx, s_w, tl);
+    if (__builtin_amdgcn_readfirstlane(wave_id()) == 0) {  // the first wave routes the token
+        const WaveSel ws = wave_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias);
+        if (tid < k) { s_idx[tid] = ws.e; s_w[tid] = ws.w; }
+    }
+    __syncthreads();
     if (tid < k) {
         const int e = s_idx[tid];
         if (e >= 0) {
@@ -138,11 +142,10 @@ __device__ __forceinline__ void build_plan_one(const GemvArgs &a, const PlanDims
 //   slot(e)       = number of union experts below e
 //   first pair(e) = number of (token, expert) selections with expert below e
 //   pair of (t,e) = first pair(e) + number of tokens before t selecting e
-// tokbits: LDS scratch of kGemvMaxT x 16 words.
-// tl: ntl selection scratch sets; with ntl > 1 (and 256 * ntl threads)
-// groups of 256 threads route ntl tokens at once.
+// tokbits: LDS scratch of kGemvMaxT x 16 words (E <= 512).  Each wave of the
+// block routes every nw-th token (nw waves), so up to nw tokens route at once.
 __device__ __forceinline__ void build_plan(const GemvArgs &a, const PlanDims &pd, int *plan, int *s_idx, float *s_w,
-                           uint32_t (*tokbits)[16], TopkLds *tl, int ntl = 1)
+                           uint32_t (*tokbits)[16])
 {
     const int tid = threadIdx.x, nt = blockDim.x, T = a.T, k = a.rc.k;
     int *slot_e = plan + pd.o_e, *slot_n = plan + pd.o_n, *slot_p0 = plan + pd.o_p0;
@@ -155,41 +158,54 @@ __device__ __forceinline__ void build_plan(const GemvArgs &a, const PlanDims &pd
         return;
     }
     if (T == 1) {
-        build_plan_one(a, pd, plan, s_idx, s_w, *tl);
+        build_plan_one(a, pd, plan, s_idx, s_w);
         return;
     }
-    for (int i = tid; i < T * 16; i += nt) tokbits[i >> 4][i & 15] = 0u;
+    // each wave routes every nw-th token and writes that token's bitmap
+    // (lane w < 16 ORs together the selections that fall in word w)
     {
-        // ng groups of 256 threads route ng tokens per round; a group
-        // without a token in the last round routes that round's first token
-        // again into its own spare outputs (the rounds stay uniform)
-        const int ng = (ntl > 1 && nt >= 256 * ntl) ? ntl : 1;
-        const int gs = nt / ng, g = tid / gs;
-        __shared__ int spare_e[4][kMaxTopK];
-        __shared__ float spare_w[4][kMaxTopK];
-        for (int t0 = 0; t0 < T; t0 += ng) {
-            const int t = t0 + g, tr = (t < T) ? t : t0;
-            block_topk(a.rc, a.logits + (size_t)tr * a.E, a.lstride, a.lparts, a.bias,
-                       (t < T) ? s_idx + t * k : spare_e[g & 3], (t < T) ? s_w + t * k : spare_w[g & 3], tl[g],
-                       tid - g * gs, gs);
+        const int nw = nt >> 6, wv = __builtin_amdgcn_readfirstlane(wave_id()), lane = lane_id();
+        for (int t = wv; t < T; t += nw) {
+            const WaveSel ws = wave_topk(a.rc, a.logits + (size_t)t * a.E, a.lstride, a.lparts, a.bias);
+            if (lane < k) { s_idx[t * k + lane] = ws.e; s_w[t * k + lane] = ws.w; }
+            uint32_t word = 0u;
+            for (int i = 0; i < k; i++) {
+                const int e = __builtin_amdgcn_readlane(ws.e, i);  // e < 0: dropped by top-p
+                if (e >= 0 && (e >> 5) == lane) word |= 1u << (e & 31);
+            }
+            if (lane < 16) tokbits[t][lane] = word;
         }
     }
-    for (int i = tid; i < T * k; i += nt) {
-        const int e = s_idx[i];
-        if (e >= 0) atomicOr(&tokbits[i / k][e >> 5], 1u << (e & 31));  // e < 0: dropped by top-p
+    __syncthreads();
+    // per bitmap word: union experts and selections below it (exclusive
+    // prefix sums over the words, one wave), and the union's size
+    __shared__ int upre[16], cpre[16], s_u;
+    const int nwd = (a.E + 31) >> 5;
+    if (tid < kWave) {
+        uint32_t un = 0u;
+        int cnt = 0;
+        for (int tt = 0; tt < T; tt++) {
+            const uint32_t v = tokbits[tt][tid & 15];
+            un |= v;
+            cnt += __popc(v);
+        }
+        const bool live = tid < nwd;
+        const int uc = live ? __popc(un) : 0;
+        cnt = live ? cnt : 0;
+        int us = uc, cs = cnt;
+        for (int o = 1; o < 16; o <<= 1) {
+            const int ua = __shfl_up(us, o), ca = __shfl_up(cs, o);
+            if (tid >= o) { us += ua; cs += ca; }
+        }
+        if (tid < 16) { upre[tid] = us - uc; cpre[tid] = cs - cnt; }
+        if (tid == 15) s_u = us;
     }
     __syncthreads();
-    const int nw = (a.E + 31) >> 5;
     for (int i = tid; i < T * k; i += nt) {
         if (s_idx[i] < 0) continue;
         const int t = i / k, e = s_idx[i], wi = e >> 5;
         const uint32_t bit = 1u << (e & 31), below = bit - 1u;
-        int slot = 0, p0 = 0, n = 0, rank = 0;
-        for (int w = 0; w < wi; w++) {
-            uint32_t un = 0u;
-            for (int tt = 0; tt < T; tt++) { un |= tokbits[tt][w]; p0 += __popc(tokbits[tt][w]); }
-            slot += __popc(un);
-        }
+        int slot = upre[wi], p0 = cpre[wi], n = 0, rank = 0;
         uint32_t un = 0u;
         for (int tt = 0; tt < T; tt++) {
             const uint32_t v = tokbits[tt][wi];
@@ -205,12 +221,7 @@ __device__ __forceinline__ void build_plan(const GemvArgs &a, const PlanDims &pd
         pair_w[p0 + rank] = s_w[i];
     }
     if (tid == 0) {
-        int U = 0;
-        for (int w = 0; w < nw; w++) {
-            uint32_t un = 0u;
-            for (int tt = 0; tt < T; tt++) un |= tokbits[tt][w];
-            U += __popc(un);
-        }
+        const int U = s_u;
         plan[0] = U + a.n_shared;
         if (a.n_shared) { slot_e[U] = -1; slot_n[U] = T; slot_p0[U] = T * k; }
     }
@@ -227,17 +238,15 @@ __device__ __forceinline__ void build_plan(const GemvArgs &a, const PlanDims &pd
 // routing, when asked): for several tokens, measured on MI355X, one such
 // launch costs less than every gate/up workgroup re-deriving the union plan,
 // or than cross-workgroup signalling through a shared atomic counter.
-// Four groups of 256 threads route four tokens at a time (each selection is
-// a chain of dependent steps; ~4 us per token on MI355X).
-constexpr int kPlanGroups = 4;
-__global__ __launch_bounds__(256 * kPlanGroups) void k_plan(const GemvArgs a, const PlanDims pd)
+// One wave per token routes every token of the chunk at once.
+constexpr int kPlanThreads = kWave * kGemvMaxT;
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const GemvArgs a, const PlanDims pd)
 {
     __shared__ int plan[1 + 3 * (kGemvMaxT * kMaxTopK + 1) + 2 * kGemvMaxT * (kMaxTopK + 1)];
     __shared__ int s_idx[kGemvMaxT * kMaxTopK];
     __shared__ float s_w[kGemvMaxT * kMaxTopK];
     __shared__ uint32_t tokbits[kGemvMaxT][16];
-    __shared__ TopkLds tl[kPlanGroups];
-    build_plan(a, pd, plan, s_idx, s_w, tokbits, tl, kPlanGroups);
+    build_plan(a, pd, plan, s_idx, s_w, tokbits);
     const int tid = threadIdx.x, nt = blockDim.x;
     for (int i = tid; i < pd.words; i += nt) a.plan[i] = plan[i];
     if (a.logits && a.idx_out)
@@ -247,7 +256,7 @@ __global__ __launch_bounds__(256 * kPlanGroups) void k_plan(const GemvArgs a, co
 int launch_plan(const GemvArgs &a, hipStream_t st)
 {
     const PlanDims pd = plan_dims(a.T, a.rc.k, a.n_shared, a.logits == nullptr);
-    k_plan<<<1, 256 * kPlanGroups, 0, st>>>(a, pd);
+    k_plan<<<1, kPlanThreads, 0, st>>>(a, pd);
     return (int)hipGetLastError();
 }
 
@@ -730,7 +739,6 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
     __shared__ int plan[1 + 5 * (kMaxTopK + 1)];
     __shared__ int s_idx[kMaxTopK];
     __shared__ float s_w[kMaxTopK];
-    __shared__ TopkLds tl;
     const int v = blockIdx.x / tiles, tile = blockIdx.x % tiles, row0 = tile * 32;
     if (v < a.n_shared) {
         if (threadIdx.x == 0) plan[0] = 0;  // the token list of the shared slot: token 0
@@ -739,7 +747,7 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
         return;
     }
     const int u = v - a.n_shared;
-    build_plan_one(a, pd, plan, s_idx, s_w, tl);
+    build_plan_one(a, pd, plan, s_idx, s_w);
     if (u >= plan[0] - a.n_shared) return;  // a slot top-p dropped (uniform in the workgroup)
     if (u == 0 && tile == 0) {
         for (int i = threadIdx.x; i < pd.words; i += kSwThreads) a.plan[i] = plan[i];
@@ -966,7 +974,10 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             const int u = u0 + b;
-            if (u + NB - 1 < S) load_slot(u + NB - 1, wr[(b + NB - 1) % NB]);
+            // unconditional (past the end: the last slot again, an L2 hit),
+            // so the ring's registers carry no merge of loaded and unloaded
+            // values and every wait counts the ring's loads exactly
+            load_slot(min(u + NB - 1, S - 1), wr[(b + NB - 1) % NB]);
             if (MB && u < S && u == bend) {  // next batch of pairs (uniform)
                 __syncthreads();
                 batch_from(u);

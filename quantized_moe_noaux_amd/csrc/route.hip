@@ -265,21 +265,25 @@ int launch_router_logits_mfma(const float *x, int T, int H, const float *gate_w,
     return (int)hipGetLastError();
 }
 
-// one workgroup per token; the logits are the sum of `nparts` slices
+// one wave per token; the logits are the sum of `nparts` slices.  A wave
+// past the last token routes the last token again and stores nothing.
 __global__ __launch_bounds__(256) void k_topk(const RouteCfg rc, const double *__restrict__ logits, int nparts,
                                               const float *__restrict__ bias, int T,
                                               int32_t *__restrict__ idx, float *__restrict__ w)
 {
-    __shared__ TopkLds tl;
-    const int t = blockIdx.x;
-    block_topk(rc, logits + (size_t)t * rc.E, (size_t)T * rc.E, nparts, bias, idx + (size_t)t * rc.k,
-               w + (size_t)t * rc.k, tl);
+    const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave_id()), tr = min(t, T - 1);
+    const WaveSel ws = wave_topk(rc, logits + (size_t)tr * rc.E, (size_t)T * rc.E, nparts, bias);
+    const int lane = lane_id();
+    if (t < T && lane < rc.k) {
+        idx[(size_t)t * rc.k + lane] = ws.e;
+        w[(size_t)t * rc.k + lane] = ws.w;
+    }
 }
 
 int launch_topk(const RouteCfg &rc, const double *logits, int nparts, const float *bias, int T, int32_t *idx,
                 float *w, hipStream_t st)
 {
-    k_topk<<<T, 256, 0, st>>>(rc, logits, nparts, bias, T, idx, w);
+    k_topk<<<(T + 3) / 4, 256, 0, st>>>(rc, logits, nparts, bias, T, idx, w);
     return (int)hipGetLastError();
 }
 

@@ -48,212 +48,161 @@ template <int CTRL> __device__ __forceinline__ void dpp_top2(double &b1, double 
     merge_top2(b1, b2, dpp_d<CTRL>(b1), dpp_d<CTRL>(b2));
 }
 
-// LDS scratch of block_topk.  Keys are stored per group at a stride of
-// mpad = m rounded up to 8 (zero keys in the padding), so the in-group rank
-// loop reads whole 8-key steps with no bounds checks: a zero key never
-// outranks a real one.
-struct __align__(16) TopkLds {
-    // the last entry of s, c and key is a dump slot: a lane without an
-    // expert stores there, so its loads and stores need no branch
-    double s[kMaxExperts + 1];                       // sigmoid scores
-    double c[kMaxExperts + 1];                       // c = s + bias
-    uint64_t key[kMaxExperts + 7 * kMaxGroups + 1];  // order keys, group-strided
-    uint64_t fkey[kMaxExperts];                  // finalists' keys
-    int fe[kMaxExperts];                         // finalists' experts
-    int frank[kMaxExperts];                      // finalists' ranks among the finalists
-    int kept[kMaxGroups];                        // kept groups, ascending
-    int nkept;
-    int sel_e[kMaxTopK];
-    double sel_s[kMaxTopK];
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+template <int CTRL> __device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Largest value over the 64 lanes: DPP inside each row of 16 lanes, then the
+// four row maxima read into scalar registers (no LDS crossbar round trip).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    uint64_t o;
+    o = dpp_u64<0xB1>(v);  v = o > v ? o : v;   // lane ^ 1
+    o = dpp_u64<0x4E>(v);  v = o > v ? o : v;   // lane ^ 2
+    o = dpp_u64<0x141>(v); v = o > v ? o : v;   // the other quad of 8
+    o = dpp_u64<0x140>(v); v = o > v ? o : v;   // the other half of 16
+    const uint64_t r0 = readlane_u64(v, 0), r1 = readlane_u64(v, 16);
+    const uint64_t r2 = readlane_u64(v, 32), r3 = readlane_u64(v, 48);
+    const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    return a > b ? a : b;
+}
+
+// One routed selection as the calling wave's lanes hold it: lane i < k has
+// the expert of rank i and its weight (-1 and 0 for a slot top-p dropped).
+struct WaveSel {
+    int e;
+    float w;
 };
 
-// Number of keys among the 8 at p that outrank key ke at position pos
-// (position j outranks if its key is larger, or equal with j < pos).
-__device__ __forceinline__ int outrank8(const uint64_t *p, int j0, uint64_t ke, int pos)
-{
-    const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(p);
-    int cnt = 0;
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-        const ulonglong2 v = q[u];
-        cnt += (v.x > ke) || (v.x == ke && j0 + 2 * u < pos);
-        cnt += (v.y > ke) || (v.y == ke && j0 + 2 * u + 1 < pos);
-    }
-    return cnt;
-}
-
-// Block-wide noaux_tc routing of one token (every thread of the block calls
-// it; nt >= 64 threads take part).  Every phase spreads its work over many lanes with
-// independent loads: on MI355X a dependent LDS or cross-lane round trip costs
-// ~100 cycles, so serial chains, not arithmetic, set the latency of this step.
-//   1. s, c = s + bias and the order key of c for every expert (all logit
-//      loads issued before any arithmetic);
-//   2. one wave: group score = sum of the two largest c (lane l holds the
-//      experts epl*l ..; a group spans lpg lanes, merged by DPP), and the
-//      topk_group best groups (score desc, index asc) are kept;
-//   3. in-group rank of every candidate of a kept group; only a candidate
-//      with in-group rank < k can be among the top k, so each kept group
-//      has exactly min(m, k) finalists, stored at (kept slot, in-group rank);
-//   4. rank of every finalist among the finalists: for a finalist in the top
-//      k it equals its rank among all candidates (every candidate above it is
-//      a finalist too), and one outside the top k has rank >= k there too.
-//      Equal keys rank by position, which is expert order (kept groups
-//      ascend, and in-group ranks order equal keys by expert index), so a
-//      tie goes to the lower expert index.  The rank is the in-group rank
-//      plus, per other kept group, the length of that group's run of
-//      finalists that outrank it: a group's finalists sit in outrank order,
-//      so a binary search finds the run;
-//   5. the selected s normalised to sum one, times routed_scaling_factor;
-//      with adaptive top-p (rc.top_p in (0, 1)) only the shortest prefix of
-//      the selection whose share of the summed s reaches p is kept and
-//      renormalised, and the dropped slots read expert -1, weight 0.
-// All scores and comparisons are fp64 (order keys compare as the doubles).
-//   zt: the token's logits, as the sum of nparts slices pstride apart
-//   (added in slice order)
-//   tid, nt: this thread's index among the nt threads (a multiple of 64)
-//   that route this token; several groups of a workgroup may route
-//   different tokens at once, each with its own L, since the barriers are
-//   workgroup-wide and every group passes the same ones.
-__device__ __forceinline__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, size_t pstride, int nparts,
-                           const float *__restrict__ bias, int *sel_e, float *sel_w, TopkLds &L, int tid,
-                           int nt)
+// noaux_tc routing of one token by one wave: all 64 lanes call it together
+// (wave-uniform control flow), and it uses no LDS and no barrier, so the
+// waves of a workgroup can route different tokens at once.  Lane l holds
+// experts l*epl .. l*epl + epl - 1 in registers (EPL = epl, or 8 for any
+// epl <= 8 with the unused entries masked).
+//   1. s = sigmoid(z) and c = s + bias per expert, z being the sum of the
+//      nparts logit slices pstride apart in slice order (all loads issued
+//      at clamped indices first);
+//   2. group score = sum of the two largest c of the group (a group spans
+//      lpg lanes, merged by DPP moves and lane swaps); the topk_group best
+//      groups (score desc, index asc) are kept;
+//   3. k rounds of a wave-wide arg-max over the order keys of the kept
+//      candidates: the largest key, and on equal keys the lowest lane and
+//      then the lowest entry, which is the lowest expert index; the winner
+//      drops out of later rounds.  Round r leaves its expert and s in lane r;
+//   4. weights = selected s normalised to sum one (added in rank order),
+//      times routed_scaling_factor; with adaptive top-p (rc.top_p in (0, 1))
+//      the shortest rank prefix whose share of the sum reaches p is kept and
+//      renormalised.
+// Every score and comparison is fp64.
+template <int EPL>
+__device__ __forceinline__ WaveSel wave_topk_epl(const RouteCfg &rc, const double *__restrict__ zt, size_t pstride,
+                                                 int nparts, const float *__restrict__ bias)
 {
     const int lane = lane_id();
-    const int E = rc.E, G = rc.G, m = E / G, k = rc.k;
-    const int mpad = (m + 7) & ~7;
-    const int kdump = kMaxExperts + 7 * kMaxGroups;
-    for (int e0 = 0; e0 < E; e0 += 2 * nt) {
-        // both experts' loads at clamped indices, unconditionally (one round
-        // trip); a lane past E computes on a duplicate and stores it in the
-        // dump slots
-        const int ea = e0 + tid, eb = e0 + nt + tid;
-        const int ca = min(ea, E - 1), cb = min(eb, E - 1);
-        double za = zt[ca], zb = zt[cb];
-        const float ba = bias[ca], bb = bias[cb];
-        for (int p = 1; p < nparts; p++) {
-            za += zt[p * pstride + ca];
-            zb += zt[p * pstride + cb];
-        }
-        const double sa = 1.0 / (1.0 + exp(-za)), cva = sa + (double)ba;
-        const double sb = 1.0 / (1.0 + exp(-zb)), cvb = sb + (double)bb;
-        const int da = ea < E ? ea : kMaxExperts, db = eb < E ? eb : kMaxExperts;
-        L.s[da] = sa;
-        L.c[da] = cva;
-        L.key[ea < E ? (ea / m) * mpad + ea % m : kdump] = order_key(cva);
-        L.s[db] = sb;
-        L.c[db] = cvb;
-        L.key[eb < E ? (eb / m) * mpad + eb % m : kdump] = order_key(cvb);
-    }
-    for (int i = tid; i < G * (mpad - m); i += nt) L.key[(i / (mpad - m)) * mpad + m + i % (mpad - m)] = 0ull;
-    __syncthreads();
-    if (tid < 64) {
-        const int epl = rc.epl, lpg = rc.lpg;
-        // all eight reads issued at once (clamped in bounds, masked after),
-        // then a branch-free top-2 insertion
-        double cvs[8];
+    const int E = rc.E, G = rc.G, m = E / G, k = rc.k, lpg = rc.lpg;
+    const int epl = (EPL == 8) ? rc.epl : EPL;
+    double z[EPL];
+    float bv[EPL];
 #pragma unroll
-        for (int j = 0; j < 8; j++) cvs[j] = L.c[min(lane * epl + j, E - 1)];
-        double b1 = -INFINITY, b2 = -INFINITY;
+    for (int j = 0; j < EPL; j++) {
+        const int c = min(lane * epl + j, E - 1);
+        z[j] = zt[c];
+        bv[j] = bias[c];
+    }
+    for (int p = 1; p < nparts; p++) {
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const double cv = (j < epl && lane * epl + j < E) ? cvs[j] : -INFINITY;
-            b2 = fmax(b2, fmin(b1, cv));
-            b1 = fmax(b1, cv);
-        }
-        if (lpg > 1) dpp_top2<0xB1>(b1, b2);   // quad_perm [1,0,3,2]: lane ^ 1
-        if (lpg > 2) dpp_top2<0x4E>(b1, b2);   // quad_perm [2,3,0,1]: lane ^ 2
-        if (lpg > 4) dpp_top2<0x141>(b1, b2);  // row_half_mirror: the other quad of 8
-        if (lpg > 8) dpp_top2<0x140>(b1, b2);  // row_mirror: the other half of 16
-        for (int o = 16; o < lpg; o <<= 1) merge_top2(b1, b2, __shfl_xor(b1, o), __shfl_xor(b2, o));
-        const double gsv = (m >= 2) ? b1 + b2 : b1;
-        const int g = lane / lpg;
-        int grank = 0;
-        for (int h = 0; h < G; h++) {
-            const double o = readlane_d(gsv, h * lpg);
-            grank += (o > gsv) || (o == gsv && h < g);
-        }
-        const bool keep = g < G && lane % lpg == 0 && grank < rc.tg;
-        const unsigned long long kb = __ballot(keep);
-        if (keep) L.kept[__popcll(kb & ((1ull << lane) - 1))] = g;
-        if (lane == 0) L.nkept = __popcll(kb);
+        for (int j = 0; j < EPL; j++) z[j] += zt[p * pstride + min(lane * epl + j, E - 1)];
     }
-    __syncthreads();
-    const int nk = L.nkept, f1 = m < k ? m : k, nf = nk * f1;
-    for (int ci = tid; ci < nk * m; ci += nt) {
-        const int slot = ci / m, r = ci - slot * m, g = L.kept[slot];
-        const uint64_t *gk = L.key + g * mpad;
-        const uint64_t ke = gk[r];
-        int cnt = 0;
-        for (int j = 0; j < mpad; j += 8) cnt += outrank8(gk + j, j, ke, r);
-        if (cnt < f1) {
-            L.fkey[slot * f1 + cnt] = ke;
-            L.fe[slot * f1 + cnt] = g * m + r;
-            L.frank[slot * f1 + cnt] = 0;
-        }
-    }
-    __syncthreads();
-    int top = 1;  // largest power of two <= f1
-    while (2 * top <= f1) top *= 2;
-    for (int it = tid; it < nf * nk; it += nt) {
-        const int fi = it / nk, b = it - fi * nk, ga = fi / f1;
-        int cnt;
-        if (b == ga) {
-            cnt = fi - ga * f1;
+    double s[EPL], cv[EPL];
+    bool valid[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; j++) {
+        valid[j] = j < epl && lane * epl + j < E;
+        if (j < epl) {  // uniform: only the generic form skips entries
+            s[j] = 1.0 / (1.0 + exp(-z[j]));
+            cv[j] = s[j] + (double)bv[j];
         } else {
-            // group b's entries at positions before fi's group outrank it on
-            // equal keys too
-            const uint64_t kx = L.fkey[fi], *gb = L.fkey + b * f1;
-            cnt = 0;
-            for (int st = top; st > 0; st >>= 1) {
-                const int j = cnt + st - 1;
-                if (j < f1) {
-                    const uint64_t ky = gb[j];
-                    if (ky > kx || (ky == kx && b < ga)) cnt += st;
-                }
-            }
-        }
-        atomicAdd(&L.frank[fi], cnt);
-    }
-    __syncthreads();
-    for (int fi = tid; fi < nf; fi += nt) {
-        const int r = L.frank[fi];
-        if (r < k) {
-            const int e = L.fe[fi];
-            L.sel_e[r] = e;
-            L.sel_s[r] = L.s[e];
+            s[j] = 0.0;
+            cv[j] = -INFINITY;
         }
     }
-    __syncthreads();
-    if (tid < k) {
-        double sum = 0.0;
-        for (int i = 0; i < k; i++) sum += L.sel_s[i];
-        int kept = k;
-        if (rc.top_p > 0.f) {
-            // adaptive top-p: the shortest prefix whose share of the summed s
-            // reaches p (shares added in slot order), renormalised
-            const double p = (double)rc.top_p;
-            double cum = 0.0;
-            kept = 0;
-            while (kept < k) {
-                cum += L.sel_s[kept] / sum;
-                kept++;
-                if (cum >= p) break;
-            }
-            sum = 0.0;
-            for (int i = 0; i < kept; i++) sum += L.sel_s[i];
-        }
-        sel_e[tid] = (tid < kept) ? L.sel_e[tid] : -1;
-        sel_w[tid] = (tid < kept) ? (float)(L.sel_s[tid] / sum * (double)rc.rsf) : 0.f;
+    double b1 = -INFINITY, b2 = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; j++) {
+        const double c = valid[j] ? cv[j] : -INFINITY;
+        b2 = fmax(b2, fmin(b1, c));
+        b1 = fmax(b1, c);
     }
-    __syncthreads();
+    if (lpg > 1) dpp_top2<0xB1>(b1, b2);   // quad_perm [1,0,3,2]: lane ^ 1
+    if (lpg > 2) dpp_top2<0x4E>(b1, b2);   // quad_perm [2,3,0,1]: lane ^ 2
+    if (lpg > 4) dpp_top2<0x141>(b1, b2);  // row_half_mirror: the other quad of 8
+    if (lpg > 8) dpp_top2<0x140>(b1, b2);  // row_mirror: the other half of 16
+    for (int o = 16; o < lpg; o <<= 1) merge_top2(b1, b2, __shfl_xor(b1, o), __shfl_xor(b2, o));
+    const double gsv = (m >= 2) ? b1 + b2 : b1;
+    const int g = lane / lpg;
+    int grank = 0;
+    for (int h = 0; h < G; h++) {
+        const double o = readlane_d(gsv, h * lpg);
+        grank += (o > gsv) || (o == gsv && h < g);
+    }
+    const bool keep = g < G && grank < rc.tg;
+    uint64_t key[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; j++) key[j] = (valid[j] && keep) ? order_key(cv[j]) : 0ull;
+
+    int my_e = -1;
+    double my_s = 0.0, sum = 0.0;
+    for (int r = 0; r < k; r++) {
+        uint64_t bk = key[0];
+        int bj = 0;
+        double bs = s[0];
+#pragma unroll
+        for (int j = 1; j < EPL; j++)
+            if (key[j] > bk) { bk = key[j]; bj = j; bs = s[j]; }
+        // k <= kept candidates (checked on the host), so the maximum is a
+        // real candidate's key
+        const uint64_t M = wave_max_u64(bk);
+        const int w = __builtin_ctzll(__ballot(bk == M));
+        const int wj = __builtin_amdgcn_readlane(bj, w);
+        const double se = readlane_d(bs, w);
+        sum += se;
+        if (lane == r) { my_e = w * epl + wj; my_s = se; }
+#pragma unroll
+        for (int j = 0; j < EPL; j++)
+            if (lane == w && j == wj) key[j] = 0ull;
+    }
+    int kept = k;
+    if (rc.top_p > 0.f) {
+        const double p = (double)rc.top_p;
+        double cum = 0.0;
+        kept = 0;
+        while (kept < k) {
+            cum += readlane_d(my_s, kept) / sum;
+            kept++;
+            if (cum >= p) break;
+        }
+        sum = 0.0;
+        for (int i = 0; i < kept; i++) sum += readlane_d(my_s, i);
+    }
+    WaveSel o;
+    o.e = (lane < kept) ? my_e : -1;
+    o.w = (lane < kept) ? (float)(my_s / sum * (double)rc.rsf) : 0.f;
+    return o;
 }
 
-// the whole workgroup routes one token
-__device__ __forceinline__ void block_topk(const RouteCfg rc, const double *__restrict__ zt, size_t pstride,
-                                           int nparts, const float *__restrict__ bias, int *sel_e, float *sel_w,
-                                           TopkLds &L)
+__device__ __forceinline__ WaveSel wave_topk(const RouteCfg &rc, const double *__restrict__ zt, size_t pstride,
+                                             int nparts, const float *__restrict__ bias)
 {
-    block_topk(rc, zt, pstride, nparts, bias, sel_e, sel_w, L, threadIdx.x, blockDim.x);
+    if (rc.epl == 4) return wave_topk_epl<4>(rc, zt, pstride, nparts, bias);
+    return wave_topk_epl<8>(rc, zt, pstride, nparts, bias);
 }
 
 } // namespace moe
