@@ -91,8 +91,8 @@ __device__ __forceinline__ PlanPairs plan_pairs(const int *plan, const PlanDims 
     return q;
 }
 
-// The plan of one token (slots = its kept experts in ascending order, then
-// the shared expert).  Kept apart from the batch plan so that a caller that
+// The plan of one token (slots = its kept experts in rank order, slot r
+// taking pair r, then the shared expert; a batch of one needs no union).  Kept apart from the batch plan so that a caller that
 // only ever routes one token compiles no access through generic pointers: a
 // pending flat access anywhere in a kernel makes the compiler wait for all
 // outstanding loads wherever it waits for one.
@@ -103,24 +103,22 @@ __device__ __forceinline__ void build_plan_one(const GemvArgs &a, const PlanDims
     int *slot_e = plan + pd.o_e, *slot_n = plan + pd.o_n, *slot_p0 = plan + pd.o_p0;
     int *pair_t = plan + pd.o_t;
     float *pair_w = reinterpret_cast<float *>(plan + pd.o_w);
-    // one token: slots are its kept experts in ascending order, then the
-    // shared expert; the pair of a routed slot is the slot itself, the
-    // shared expert's pair is k (also when top-p keeps fewer experts)
+    // one token: slots are its kept experts in rank order, then the shared
+    // expert; the pair of a routed slot is the slot itself, the shared
+    // expert's pair is k (also when top-p keeps fewer experts)
     if (__builtin_amdgcn_readfirstlane(wave_id()) == 0) {  // the first wave routes the token
-        const WaveSel ws = wave_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias);
+        const WaveSel ws = wave_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias, k);
         if (tid < k) { s_idx[tid] = ws.e; s_w[tid] = ws.w; }
     }
     __syncthreads();
     if (tid < k) {
         const int e = s_idx[tid];
-        if (e >= 0) {
-            int slot = 0;
-            for (int j = 0; j < k; j++) slot += (s_idx[j] >= 0 && s_idx[j] < e);
-            slot_e[slot] = e;
-            slot_n[slot] = 1;
-            slot_p0[slot] = slot;
-            pair_t[slot] = 0;
-            pair_w[slot] = s_w[tid];
+        if (e >= 0) {  // top-p keeps a prefix of the ranks
+            slot_e[tid] = e;
+            slot_n[tid] = 1;
+            slot_p0[tid] = tid;
+            pair_t[tid] = 0;
+            pair_w[tid] = s_w[tid];
         }
     }
     if (tid == 0) {
@@ -166,7 +164,7 @@ __device__ __forceinline__ void build_plan(const GemvArgs &a, const PlanDims &pd
     {
         const int nw = nt >> 6, wv = __builtin_amdgcn_readfirstlane(wave_id()), lane = lane_id();
         for (int t = wv; t < T; t += nw) {
-            const WaveSel ws = wave_topk(a.rc, a.logits + (size_t)t * a.E, a.lstride, a.lparts, a.bias);
+            const WaveSel ws = wave_topk(a.rc, a.logits + (size_t)t * a.E, a.lstride, a.lparts, a.bias, k);
             if (lane < k) { s_idx[t * k + lane] = ws.e; s_w[t * k + lane] = ws.w; }
             uint32_t word = 0u;
             for (int i = 0; i < k; i++) {
@@ -727,11 +725,14 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
 // is range-checked, so a corrupt plan can only skip work, never steer a load
 // out of the weight tensors.
 // One token, no plan launch: the first n_shared * tiles workgroups take the
-// shared expert, which needs no routing, and start streaming at once; every
-// other workgroup runs the noaux_tc selection itself (the same inputs in the
-// same order, so every workgroup reaches the same result) and takes the u-th
-// selected expert in ascending order.  Workgroup (u = 0, tile 0) publishes the
-// plan for the down kernel, and the routing when asked.
+// shared expert, which needs no routing, and start streaming at once; the
+// workgroups of routed slot u take the expert of rank u, found by the first
+// u + 1 rounds of the selection in their first wave (the same inputs in the
+// same order, so every workgroup reaches the same ranking), so a slot's
+// stream starts as soon as its own rank is known.  Workgroup (u = 0, tile 0)
+// runs the whole selection and publishes the plan for the down kernel, and
+// the routing when asked; with adaptive top-p every workgroup does, since
+// whether rank u is kept depends on all the weights.
 template <int WB, int CPT, int RPS>
 __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, int tiles, float (*s_h)[32],
                                        float (*part)[1][kSwGroups][32])
@@ -747,18 +748,31 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
         return;
     }
     const int u = v - a.n_shared;
-    build_plan_one(a, pd, plan, s_idx, s_w);
-    if (u >= plan[0] - a.n_shared) return;  // a slot top-p dropped (uniform in the workgroup)
-    if (u == 0 && tile == 0) {
-        for (int i = threadIdx.x; i < pd.words; i += kSwThreads) a.plan[i] = plan[i];
-        if (a.idx_out && threadIdx.x < a.rc.k) {
-            a.idx_out[threadIdx.x] = s_idx[threadIdx.x];
-            a.w_out[threadIdx.x] = s_w[threadIdx.x];
+    int e;
+    if ((u == 0 && tile == 0) || a.rc.top_p > 0.f) {
+        build_plan_one(a, pd, plan, s_idx, s_w);
+        if (u >= plan[0] - a.n_shared) return;  // a slot top-p dropped (uniform in the workgroup)
+        if (u == 0 && tile == 0) {
+            for (int i = threadIdx.x; i < pd.words; i += kSwThreads) a.plan[i] = plan[i];
+            if (a.idx_out && threadIdx.x < a.rc.k) {
+                a.idx_out[threadIdx.x] = s_idx[threadIdx.x];
+                a.w_out[threadIdx.x] = s_w[threadIdx.x];
+            }
         }
+        e = plan[pd.o_e + u];
+        __syncthreads();  // plan[0] becomes the slot's token list below
+    } else {
+        if (__builtin_amdgcn_readfirstlane(wave_id()) == 0) {
+            const WaveSel ws = wave_topk(a.rc, a.logits, a.lstride, a.lparts, a.bias, u + 1);
+            if (threadIdx.x == 0) s_idx[0] = ws.last;
+        }
+        __syncthreads();
+        e = s_idx[0];
     }
-    const int e = plan[pd.o_e + u], p0 = plan[pd.o_p0 + u];
-    if (e < 0 || e >= a.E || p0 < 0 || p0 >= pd.P) return;
-    gate_up_tile_sw<WB, CPT, RPS, 1>(a, a.routed, e, row0, 1, plan + pd.o_t + p0, p0, s_h, part);
+    if (e < 0 || e >= a.E || u >= pd.P) return;
+    if (threadIdx.x == 0) plan[0] = 0;  // the slot's token list: token 0
+    __syncthreads();
+    gate_up_tile_sw<WB, CPT, RPS, 1>(a, a.routed, e, row0, 1, plan, u, s_h, part);
 }
 
 template <int WB, int CPT, int RPS, int TT>

@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void k_topk(const RouteCfg rc, const double *_
                                               int32_t *__restrict__ idx, float *__restrict__ w)
 {
     const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(wave_id()), tr = min(t, T - 1);
-    const WaveSel ws = wave_topk(rc, logits + (size_t)tr * rc.E, (size_t)T * rc.E, nparts, bias);
+    const WaveSel ws = wave_topk(rc, logits + (size_t)tr * rc.E, (size_t)T * rc.E, nparts, bias, rc.k);
     const int lane = lane_id();
     if (t < T && lane < rc.k) {
         idx[(size_t)t * rc.k + lane] = ws.e;

@@ -76,10 +76,12 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 }
 
 // One routed selection as the calling wave's lanes hold it: lane i < k has
-// the expert of rank i and its weight (-1 and 0 for a slot top-p dropped).
+// the expert of rank i and its weight (-1 and 0 for a slot top-p dropped);
+// last is the expert the final round picked (the same in every lane).
 struct WaveSel {
     int e;
     float w;
+    int last;
 };
 
 // noaux_tc routing of one token by one wave: all 64 lanes call it together
@@ -101,10 +103,12 @@ struct WaveSel {
 //      times routed_scaling_factor; with adaptive top-p (rc.top_p in (0, 1))
 //      the shortest rank prefix whose share of the sum reaches p is kept and
 //      renormalised.
+// With rounds < k only the first `rounds` ranks are found (no weights): the
+// expert of rank rounds - 1 is `last`.
 // Every score and comparison is fp64.
 template <int EPL>
 __device__ __forceinline__ WaveSel wave_topk_epl(const RouteCfg &rc, const double *__restrict__ zt, size_t pstride,
-                                                 int nparts, const float *__restrict__ bias)
+                                                 int nparts, const float *__restrict__ bias, int rounds)
 {
     const int lane = lane_id();
     const int E = rc.E, G = rc.G, m = E / G, k = rc.k, lpg = rc.lpg;
@@ -158,9 +162,9 @@ __device__ __forceinline__ WaveSel wave_topk_epl(const RouteCfg &rc, const doubl
 #pragma unroll
     for (int j = 0; j < EPL; j++) key[j] = (valid[j] && keep) ? order_key(cv[j]) : 0ull;
 
-    int my_e = -1;
+    int my_e = -1, last = -1;
     double my_s = 0.0, sum = 0.0;
-    for (int r = 0; r < k; r++) {
+    for (int r = 0; r < rounds; r++) {
         uint64_t bk = key[0];
         int bj = 0;
         double bs = s[0];
@@ -174,10 +178,18 @@ __device__ __forceinline__ WaveSel wave_topk_epl(const RouteCfg &rc, const doubl
         const int wj = __builtin_amdgcn_readlane(bj, w);
         const double se = readlane_d(bs, w);
         sum += se;
-        if (lane == r) { my_e = w * epl + wj; my_s = se; }
+        last = w * epl + wj;
+        if (lane == r) { my_e = last; my_s = se; }
 #pragma unroll
         for (int j = 0; j < EPL; j++)
             if (lane == w && j == wj) key[j] = 0ull;
+    }
+    WaveSel o;
+    o.last = last;
+    if (rounds < k) {
+        o.e = -1;
+        o.w = 0.f;
+        return o;
     }
     int kept = k;
     if (rc.top_p > 0.f) {
@@ -192,17 +204,17 @@ __device__ __forceinline__ WaveSel wave_topk_epl(const RouteCfg &rc, const doubl
         sum = 0.0;
         for (int i = 0; i < kept; i++) sum += readlane_d(my_s, i);
     }
-    WaveSel o;
     o.e = (lane < kept) ? my_e : -1;
     o.w = (lane < kept) ? (float)(my_s / sum * (double)rc.rsf) : 0.f;
     return o;
 }
 
+// rounds = k: the whole selection; fewer: the expert of rank rounds - 1
 __device__ __forceinline__ WaveSel wave_topk(const RouteCfg &rc, const double *__restrict__ zt, size_t pstride,
-                                             int nparts, const float *__restrict__ bias)
+                                             int nparts, const float *__restrict__ bias, int rounds)
 {
-    if (rc.epl == 4) return wave_topk_epl<4>(rc, zt, pstride, nparts, bias);
-    return wave_topk_epl<8>(rc, zt, pstride, nparts, bias);
+    if (rc.epl == 4) return wave_topk_epl<4>(rc, zt, pstride, nparts, bias, rounds);
+    return wave_topk_epl<8>(rc, zt, pstride, nparts, bias, rounds);
 }
 
 } // namespace moe
