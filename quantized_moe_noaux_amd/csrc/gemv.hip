@@ -812,9 +812,15 @@ constexpr int kDownRing = 3;
 // down/combine: a step reads RPS consecutive down rows of one slot (4 KB);
 // kDsRows rows per workgroup, every slot in turn through a ring of NB slot
 // buffers.  MB: the plan's pairs take more than one staging batch.
-template <int WB, int RPS, int TT, int NB, bool MB>
+// EARLY (one routed token with a shared expert): nothing the shared slot and
+// the staging read depends on the plan (every pair is staged, pair p at
+// LDS index p, and the shared expert's rows are known), so they are
+// requested together with the plan, one dependent round trip fewer, and
+// the shared slot is combined first.
+template <int WB, int RPS, int TT, int NB, bool MB, bool EARLY = false>
 __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
+    static_assert(!(EARLY && (MB || TT != 1)), "the early prologue is for one token, one batch");
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ float part[TT][kDsGroups][kDsRows];
     constexpr int NSTEP = kDsRows / RPS;
@@ -830,10 +836,17 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     // every slot's kDsRows row scales, [slot][row], after a.down_pmax pairs
     float *lsc = reinterpret_cast<float *>(act + (size_t)a.down_pmax * pair_bytes);
 
-    for (int i = tid; i < pd.words; i += kDsThreads) plan[i] = a.plan[i];
-    __syncthreads();
-    if (!plan_ok(plan, pd, a.T, a.E) || plan[0] < 1) return;
-    const int S = plan[0];
+    int pv = 0;
+    if constexpr (EARLY) {
+        pv = a.plan[min(tid, pd.words - 1)];  // pd.words <= kDsThreads (checked on the host)
+    } else {
+        for (int i = tid; i < pd.words; i += kDsThreads) plan[i] = a.plan[i];
+        __syncthreads();
+        if (!plan_ok(plan, pd, a.T, a.E) || plan[0] < 1) return;
+    }
+    // with EARLY, S and every plan entry are read only after the plan
+    // barrier further down
+    int S = EARLY ? 1 : plan[0];
     // every slot's pairs must fit one staging batch (the host sizes
     // a.down_pmax >= T; a plan that breaks it writes nothing)
     if constexpr (MB) {
@@ -847,6 +860,8 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
         const int i = min(tid, a.T * kDsRows - 1);
         return a.y[(size_t)(i / kDsRows) * a.H + blockIdx.x * kDsRows + i % kDsRows];
     }();
+    // processing order of the slots: the shared (last) slot first with EARLY
+    auto slot_at = [&](int v) { return EARLY ? (v == 0 ? S - 1 : v - 1) : v; };
 
     const int rowoff = tid / cpr, pos = tid % cpr, grp = tid >> 5;
     const int row_base = blockIdx.x * kDsRows;
@@ -870,14 +885,15 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     // (every index into the ring is static once the loops are unrolled, so
     // the buffers stay in registers)
     uint4 wr[NB][NSTEP];
-    auto load_slot = [&](int u, uint4 (&wb)[NSTEP]) {
-        const uint8_t *src = slot_src(u);
+    auto load_rows = [&](const uint8_t *src, uint4 (&wb)[NSTEP]) {
 #pragma unroll
         for (int j = 0; j < NSTEP; j++) wb[j] = ld16(src + j * step_bytes);
     };
+    auto load_slot = [&](int u, uint4 (&wb)[NSTEP]) { load_rows(slot_src(u), wb); };
     constexpr int SB = stage_batch(WB);
-    const int pmax = a.down_pmax, nsc = S * kDsRows;
-    const int p0s = (plan[pd.o_e + S - 1] == -1) ? plan[pd.o_p0 + S - 1] : 0x7fffffff;
+    const int pmax = a.down_pmax;
+    int nsc = S * kDsRows;
+    int p0s = EARLY ? 0x7fffffff : (plan[pd.o_e + S - 1] == -1) ? plan[pd.o_p0 + S - 1] : 0x7fffffff;
     int bend = 0, rbase = 0, rcount = 0, nst = 0;  // the batch: slots .. bend - 1
     auto batch_from = [&](int s0) {
         int np = 0, nr = 0, s1 = s0;
@@ -964,16 +980,35 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     // (the vector memory counter retires loads in issue order).  A plan with
     // fewer slots requests its last slot again: straight-line code, so that
     // wait counts exactly the loads issued after the staging.
-    if constexpr (MB) {
-        batch_from(0);
-    } else {  // one batch: every pair (no data-dependent walk before the first loads)
-        const PlanPairs pq = plan_pairs(plan, pd);
-        bend = S; rbase = 0; rcount = pq.R; nst = pq.count() * cpr;
-    }
-    stage_issue(0);
-    scale_issue(0);
+    if constexpr (EARLY) {
+        // every pair at its own index (pairs a top-p drop leaves are staged
+        // and never read), the shared expert's rows, then the plan itself
+        rbase = 0; rcount = pd.P; nst = pd.P * cpr;
+        stage_issue(0);
+        load_rows(a.shared.down + (size_t)row_base * rowbytes + (size_t)tid * 16, wr[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tid < pd.words) plan[tid] = pv;
+        __syncthreads();
+        if (!plan_ok(plan, pd, a.T, a.E) || plan[0] < 1) return;
+        S = plan[0];
+        if (plan[pd.o_e + S - 1] != -1) return;  // the shared slot is last
+        nsc = S * kDsRows;
+        bend = S;
+        scale_issue(0);
 #pragma unroll
-    for (int b = 0; b < NB - 1; b++) load_slot(min(b, S - 1), wr[b]);
+        for (int b = 1; b < NB - 1; b++) load_slot(slot_at(min(b, S - 1)), wr[b]);
+    } else {
+        if constexpr (MB) {
+            batch_from(0);
+        } else {  // one batch: every pair (no data-dependent walk before the first loads)
+            const PlanPairs pq = plan_pairs(plan, pd);
+            bend = S; rbase = 0; rcount = pq.R; nst = pq.count() * cpr;
+        }
+        stage_issue(0);
+        scale_issue(0);
+#pragma unroll
+        for (int b = 0; b < NB - 1; b++) load_slot(min(b, S - 1), wr[b]);
+    }
     // keep every load above issued before the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
     stage_store();
@@ -991,14 +1026,14 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
             // unconditional (past the end: the last slot again, an L2 hit),
             // so the ring's registers carry no merge of loaded and unloaded
             // values and every wait counts the ring's loads exactly
-            load_slot(min(u + NB - 1, S - 1), wr[(b + NB - 1) % NB]);
+            load_slot(slot_at(min(u + NB - 1, S - 1)), wr[(b + NB - 1) % NB]);
             if (MB && u < S && u == bend) {  // next batch of pairs (uniform)
                 __syncthreads();
                 batch_from(u);
                 stage_rest(0);
                 __syncthreads();
             }
-            if (u < S) use_slot(u, wr[b]);
+            if (u < S) use_slot(slot_at(u), wr[b]);
         }
     }
     const int l32 = lane & 31;
@@ -1035,6 +1070,12 @@ static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd
     const size_t lds = down_sw_lds_bytes(WB, a.I, pd, a.down_pmax);
     // one staging batch holds every pair (one token at the production
     // shapes): the kernel without the batch switch in its slot loop
+    if constexpr (TT == 1) {
+        if (a.T == 1 && a.logits && a.n_shared == 1 && pd.words <= kDsThreads && a.down_pmax >= pd.P) {
+            k_down_sw<WB, RPS, TT, NB, false, true><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
+            return (int)hipGetLastError();
+        }
+    }
     if (a.down_pmax >= pd.P) k_down_sw<WB, RPS, TT, NB, false><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
     else k_down_sw<WB, RPS, TT, NB, true><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
     return (int)hipGetLastError();
