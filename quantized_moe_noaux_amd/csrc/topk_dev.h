@@ -48,31 +48,35 @@ template <int CTRL> __device__ __forceinline__ void dpp_top2(double &b1, double 
     merge_top2(b1, b2, dpp_d<CTRL>(b1), dpp_d<CTRL>(b2));
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
+// Largest value over the 64 lanes: one max per step with the DPP move fused
+// into it inside each row of 16 lanes, then the four row maxima read into
+// scalar registers (no LDS crossbar round trip).
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v)
 {
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
+    const uint32_t o = __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
+    return o > v ? o : v;
 }
-template <int CTRL> __device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-    const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    return ((uint64_t)hi << 32) | lo;
+    v = dpp_max_u32<0xB1>(v);   // lane ^ 1
+    v = dpp_max_u32<0x4E>(v);   // lane ^ 2
+    v = dpp_max_u32<0x141>(v);  // the other quad of 8
+    v = dpp_max_u32<0x140>(v);  // the other half of 16
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
 }
-// Largest value over the 64 lanes: DPP inside each row of 16 lanes, then the
-// four row maxima read into scalar registers (no LDS crossbar round trip).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+// Mask of the lanes holding the largest 64-bit key: the upper halves first,
+// the lower halves only when several lanes tie on the upper half.
+__device__ __forceinline__ uint64_t wave_argmax_u64(uint64_t v)
 {
-    uint64_t o;
-    o = dpp_u64<0xB1>(v);  v = o > v ? o : v;   // lane ^ 1
-    o = dpp_u64<0x4E>(v);  v = o > v ? o : v;   // lane ^ 2
-    o = dpp_u64<0x141>(v); v = o > v ? o : v;   // the other quad of 8
-    o = dpp_u64<0x140>(v); v = o > v ? o : v;   // the other half of 16
-    const uint64_t r0 = readlane_u64(v, 0), r1 = readlane_u64(v, 16);
-    const uint64_t r2 = readlane_u64(v, 32), r3 = readlane_u64(v, 48);
-    const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-    return a > b ? a : b;
+    const uint32_t hi = (uint32_t)(v >> 32), mh = wave_max_u32(hi);
+    uint64_t cand = __ballot(hi == mh);
+    if (__popcll(cand) > 1) {  // uniform
+        const uint32_t lo = (hi == mh) ? (uint32_t)v : 0u, ml = wave_max_u32(lo);
+        cand = __ballot(hi == mh && (uint32_t)v == ml);
+    }
+    return cand;
 }
 
 // One routed selection as the calling wave's lanes hold it: lane i < k has
@@ -172,9 +176,8 @@ __device__ __forceinline__ WaveSel wave_topk_epl(const RouteCfg &rc, const doubl
         for (int j = 1; j < EPL; j++)
             if (key[j] > bk) { bk = key[j]; bj = j; bs = s[j]; }
         // k <= kept candidates (checked on the host), so the maximum is a
-        // real candidate's key
-        const uint64_t M = wave_max_u64(bk);
-        const int w = __builtin_ctzll(__ballot(bk == M));
+        // real candidate's key; on equal keys the lowest lane wins
+        const int w = __builtin_ctzll(wave_argmax_u64(bk));
         const int wj = __builtin_amdgcn_readlane(bj, w);
         const double se = readlane_d(bs, w);
         sum += se;
