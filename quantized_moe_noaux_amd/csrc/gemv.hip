@@ -7,10 +7,11 @@
 // wpnews.pro spec table: 8 routed + 1 shared expert per token.
 //
 // Per chunk of tokens, three launches after the router:
-//  k_plan       one workgroup routes the chunk's tokens (fp64 noaux_tc top-k)
-//               and publishes the batch-union plan: slots = the union of the
-//               selected experts in ascending order, then the shared expert;
-//               each slot lists its tokens (pairs) and their combine weights.
+//  k_plan       one workgroup routes the chunk's tokens (fp64 noaux_tc top-k,
+//               one wave per token) and publishes the batch-union plan:
+//               slots = the union of the selected experts in ascending
+//               order, then the shared expert; each slot lists its tokens
+//               (pairs) and their combine weights.
 //  k_gate_up_*  one workgroup per (slot, 32-row tile) of the intermediate
 //               dimension: g = W_gate x, u = W_up x as integer block dots,
 //               h = silu(g) * u, h quantised to int8 in blocks of 32 rows
@@ -23,8 +24,8 @@
 // The *_sw ("row-sweep") kernels serve the production shapes; the *_rg
 // ("row-group") kernels take any other shape the ABI accepts.  A single
 // token on the row-sweep kernels has no plan launch: its gate/up workgroups
-// run the selection themselves while the shared expert's workgroups, which
-// need no routing, already stream their rows.
+// run the selection themselves (slot u as far as rank u) while the shared
+// expert's workgroups, which need no routing, already stream their rows.
 #include "moe_dev.h"
 #include "moe_internal.h"
 #include "topk_dev.h"
