@@ -279,6 +279,66 @@ int moe_mtp_accept(int32_t B, int32_t D, int32_t V, const int32_t *draft, const 
                    void *ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_mtp_accept_workspace_bytes(int32_t B, int32_t D, int32_t V);
 
+/* ---------------------------------------------------------------- expert tier
+ * HBM / host expert tier (the pages' streaming design moved one tier up:
+ * GeekNews #31297, implemented features, per-layer expert caches and the
+ * pinned hot store; wpnews.pro feature list, "Live tier adaptation
+ * (--repin N)").  A model whose routed experts exceed HBM keeps every
+ * expert in pinned host memory and a fixed number of HBM slots per layer
+ * for the hot ones.  The layer reads each routed expert where the expert
+ * table says it is: from its HBM slot, or straight from pinned host memory
+ * over PCIe (no copy in the forward, no host synchronisation).  The routing
+ * counts every selection per expert on the device (the heat map).
+ *
+ * moe_tier_create -- one layer's tier.  host: that layer's routed stacks in
+ *   pinned, device-mapped host memory (hipHostMalloc; [E][rows][bytes] as in
+ *   moe_weights_t), owned by the caller and kept alive and unchanged until
+ *   moe_tier_destroy.  slots: HBM slots, 0..E.  Allocates the slots, the
+ *   table and the counts in device memory (synchronous); no expert is in
+ *   HBM until the first repin.  The shape must be int4 at the production
+ *   row widths (hidden and inter whose packed rows take the row-sweep
+ *   kernels: 6144 and 2048); else MOE_EUNSUPPORTED.  A host pointer that is
+ *   not device-mapped pinned memory: MOE_EINVAL.  *out = NULL on error.
+ * moe_tier_repin -- the live repin: reads the counts (synchronises stream),
+ *   applies moe_tier_plan with max_swaps = 4, copies each expert entering
+ *   HBM into its slot (asynchronous host-to-device copies on stream), then
+ *   updates the table and halves every count (the heat decays), all on
+ *   stream after the work already queued there.  *copied (if not NULL) =
+ *   experts copied.  Work queued on stream later sees the new table.
+ * moe_tier_plan -- the repin decision alone (host only, no GPU): heat[E],
+ *   slot_in[E] = current slot of each expert or -1; slot_out[E] = the slots
+ *   after the repin.  Free slots first take the hottest streamed experts
+ *   with heat > 0 (lowest slot first; hottest first, ties to the lower
+ *   index).  Then at most max_swaps replacements: the next hottest streamed
+ *   expert takes the slot of the coldest pinned one (ties: the higher
+ *   index goes first) while its heat exceeds 1.25 times the other's (the
+ *   25% hysteresis).  Returns the number of experts entering HBM, or minus
+ *   MOE_EINVAL for bad arguments (an inconsistent slot_in).
+ * moe_tier_resident -- slot_of[E] (host): each expert's HBM slot or -1.
+ * moe_tier_counts -- counts[E] (host) = the current heat (synchronises
+ *   stream).
+ * moe_layer_forward_tiered -- moe_layer_forward on the GEMV path (T <= 8;
+ *   MOE_PATH_GROUPED or T > 8: MOE_EUNSUPPORTED) with the routed experts
+ *   read through the tier's table and counted.  Arguments and errors as
+ *   moe_layer_forward, the workspace that of the GEMV path
+ *   (moe_workspace_bytes with MOE_PATH_GEMV).  The results equal
+ *   moe_layer_forward's on the same weights bit for bit, wherever each
+ *   expert is.  The counts and the table are shared by every call on the
+ *   tier: calls that overlap with a repin of the same tier race.
+ * moe_tier_destroy -- frees the tier (no work using it may be in flight). */
+typedef struct moe_tier moe_tier_t;
+int moe_tier_create(const moe_shape_t *shape, const moe_weights_t *host, int32_t slots, moe_tier_t **out);
+int moe_tier_repin(moe_tier_t *tier, int32_t *copied, hipStream_t stream);
+int moe_tier_plan(const uint32_t *heat, int32_t E, int32_t C, const int32_t *slot_in, int32_t *slot_out,
+                  int32_t max_swaps);
+int moe_tier_resident(const moe_tier_t *tier, int32_t *slot_of);
+int moe_tier_counts(const moe_tier_t *tier, uint32_t *counts, hipStream_t stream);
+int moe_layer_forward_tiered(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w,
+                             const float *bias, const moe_tier_t *tier, const moe_weights_t *shared, float *y,
+                             int32_t *topk_idx, float *topk_w, uint32_t flags, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+void moe_tier_destroy(moe_tier_t *tier);
+
 #ifdef __cplusplus
 }
 #endif

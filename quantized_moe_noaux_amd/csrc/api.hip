@@ -2,6 +2,9 @@
 // the launch sequences.  Declarations and contracts: include/moe.h.
 #include "moe_internal.h"
 
+#include <algorithm>
+#include <vector>
+
 using namespace moe;
 
 namespace {
@@ -244,7 +247,7 @@ int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t exp
 static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float *gate_w, const float *bias,
                       const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
                       float *w_out, uint32_t flags, void *ws, size_t ws_bytes, const float *ng, double eps,
-                      hipStream_t stream);
+                      hipStream_t stream, const int64_t *toff = nullptr, uint32_t *counts = nullptr);
 
 int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w, const float *bias,
                       const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
@@ -279,7 +282,7 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
 static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float *gate_w, const float *bias,
                       const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
                       float *w_out, uint32_t flags, void *ws, size_t ws_bytes, const float *ng, double eps,
-                      hipStream_t stream)
+                      hipStream_t stream, const int64_t *toff, uint32_t *counts)
 {
     const moe_shape_t *shape = &sh;
     if (shape->hidden % kGemvDownRows) return MOE_EUNSUPPORTED;
@@ -315,6 +318,8 @@ static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float 
         a.idx_out = idx_out ? idx_out + (size_t)c0 * k : nullptr;
         a.w_out = w_out ? w_out + (size_t)c0 * k : nullptr;
         a.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+        a.toff = toff;
+        a.counts = counts;
         return a;
     };
     int stage = 0;
@@ -343,6 +348,256 @@ static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float 
         stage++;
     }
     return MOE_OK;
+}
+
+// ---------------------------------------------------------------- expert tier
+} // extern "C"
+
+struct moe_tier {
+    moe_shape_t shape;
+    int E, C;
+    size_t bytes[6];        // one expert's gate, up, down codes and their scales
+    uintptr_t hdev[6];      // device addresses of the pinned host stacks
+    const uint8_t *hsrc[6]; // host addresses of the same stacks (copy sources)
+    uint8_t *pool[6];       // HBM slots [C][expert bytes]
+    moe_weights_t base;     // the base pointers the table's offsets refer to
+    int64_t *dtab, *htab;   // expert table (device) and its pinned host mirror
+    uint32_t *dcounts, *hcounts;
+    std::vector<int> slot_of, expert_in;
+};
+
+namespace {
+
+void tier_free(moe_tier *t)
+{
+    for (int i = 0; i < 6; i++)
+        if (t->pool[i]) (void)hipFree(t->pool[i]);
+    if (t->dtab) (void)hipFree(t->dtab);
+    if (t->dcounts) (void)hipFree(t->dcounts);
+    if (t->htab) (void)hipHostFree(t->htab);
+    if (t->hcounts) (void)hipHostFree(t->hcounts);
+    delete t;
+}
+
+uintptr_t base_addr(const moe_tier *t, int i)
+{
+    const void *p = i == 0 ? (const void *)t->base.gate : i == 1 ? (const void *)t->base.up
+                  : i == 2 ? (const void *)t->base.down : i == 3 ? (const void *)t->base.gate_s
+                  : i == 4 ? (const void *)t->base.up_s : (const void *)t->base.down_s;
+    return (uintptr_t)p;
+}
+
+// the host mirror's entry of expert e: its slot in HBM, else the host stack
+void tier_entry(moe_tier *t, int e)
+{
+    const int s = t->slot_of[e];
+    for (int i = 0; i < 6; i++) {
+        const uintptr_t a = (s >= 0) ? (uintptr_t)t->pool[i] + (uintptr_t)s * t->bytes[i]
+                                     : t->hdev[i] + (uintptr_t)e * t->bytes[i];
+        t->htab[(size_t)e * 6 + i] = (int64_t)(a - base_addr(t, i));
+    }
+}
+
+// experts by (count desc, index asc)
+std::vector<int> by_count(const uint32_t *c, int E)
+{
+    std::vector<int> o(E);
+    for (int e = 0; e < E; e++) o[e] = e;
+    std::stable_sort(o.begin(), o.end(), [&](int a, int b) { return c[a] > c[b]; });
+    return o;
+}
+
+} // namespace
+
+extern "C" {
+
+int moe_tier_plan(const uint32_t *heat, int32_t E, int32_t C, const int32_t *slot_in, int32_t *slot_out,
+                  int32_t max_swaps)
+{
+    if (!heat || !slot_in || !slot_out || E <= 0 || C < 0 || C > E || max_swaps < 0) return -MOE_EINVAL;
+    std::vector<int> expert_in(C, -1);
+    for (int e = 0; e < E; e++) {
+        const int s = slot_in[e];
+        if (s < -1 || s >= C || (s >= 0 && expert_in[s] >= 0)) return -MOE_EINVAL;
+        if (s >= 0) expert_in[s] = e;
+        slot_out[e] = s;
+    }
+    // streamed experts, hottest first (ties: lower index)
+    std::vector<int> hot;
+    for (int e : by_count(heat, E))
+        if (slot_in[e] < 0 && heat[e] > 0) hot.push_back(e);
+    size_t h = 0;
+    int copies = 0;
+    // free slots take the hottest streamed experts, lowest slot first
+    for (int s = 0; s < C && h < hot.size(); s++)
+        if (expert_in[s] < 0) {
+            slot_out[hot[h]] = s;
+            expert_in[s] = hot[h++];
+            copies++;
+        }
+    // then up to max_swaps replacements: the hottest streamed expert against
+    // the coldest pinned one (ties: higher index), while the first is more
+    // than 25% hotter
+    std::vector<int> cold;
+    for (int s = 0; s < C; s++)
+        if (expert_in[s] >= 0 && slot_in[expert_in[s]] >= 0) cold.push_back(expert_in[s]);
+    std::stable_sort(cold.begin(), cold.end(),
+                     [&](int a, int b) { return heat[a] != heat[b] ? heat[a] < heat[b] : a > b; });
+    for (size_t c = 0; c < cold.size() && h < hot.size() && c < (size_t)max_swaps; c++, h++) {
+        const int in = hot[h], out = cold[c];
+        if (!(4ull * heat[in] > 5ull * heat[out])) break;
+        slot_out[in] = slot_out[out];
+        slot_out[out] = -1;
+        copies++;
+    }
+    return copies;
+}
+
+int moe_tier_create(const moe_shape_t *shape, const moe_weights_t *host, int32_t slots, moe_tier_t **out)
+{
+    if (!out) return MOE_EINVAL;
+    *out = nullptr;
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_weights(host))) return rc;
+    if (!gemv_table_ok(*shape)) return MOE_EUNSUPPORTED;
+    const int E = shape->n_experts;
+    if (slots < 0 || slots > E) return MOE_EINVAL;
+    moe_tier *t = new moe_tier();
+    t->shape = *shape;
+    t->E = E;
+    t->C = slots;
+    const size_t H = shape->hidden, I = shape->inter, cb = H * I * shape->wbits / 8;
+    const size_t bytes[6] = {cb, cb, cb, 4 * I, 4 * I, 4 * H};
+    const void *hp[6] = {host->gate, host->up, host->down, host->gate_s, host->up_s, host->down_s};
+    for (int i = 0; i < 6; i++) {
+        t->bytes[i] = bytes[i];
+        t->hsrc[i] = static_cast<const uint8_t *>(hp[i]);
+        void *d = nullptr;
+        if (hipHostGetDevicePointer(&d, const_cast<void *>(hp[i]), 0) != hipSuccess || !d) {
+            (void)hipGetLastError();
+            tier_free(t);
+            return MOE_EINVAL;  // not pinned, device-mapped host memory
+        }
+        t->hdev[i] = (uintptr_t)d;
+        if (slots > 0 && hipMalloc(reinterpret_cast<void **>(&t->pool[i]), bytes[i] * slots) != hipSuccess) {
+            tier_free(t);
+            return MOE_EHIP;
+        }
+    }
+    const bool hbm = slots > 0;
+    t->base.gate = hbm ? t->pool[0] : reinterpret_cast<const uint8_t *>(t->hdev[0]);
+    t->base.up = hbm ? t->pool[1] : reinterpret_cast<const uint8_t *>(t->hdev[1]);
+    t->base.down = hbm ? t->pool[2] : reinterpret_cast<const uint8_t *>(t->hdev[2]);
+    t->base.gate_s = reinterpret_cast<const float *>(hbm ? (uintptr_t)t->pool[3] : t->hdev[3]);
+    t->base.up_s = reinterpret_cast<const float *>(hbm ? (uintptr_t)t->pool[4] : t->hdev[4]);
+    t->base.down_s = reinterpret_cast<const float *>(hbm ? (uintptr_t)t->pool[5] : t->hdev[5]);
+    if (hipMalloc(reinterpret_cast<void **>(&t->dtab), sizeof(int64_t) * 6 * E) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&t->dcounts), sizeof(uint32_t) * E) != hipSuccess ||
+        hipHostMalloc(reinterpret_cast<void **>(&t->htab), sizeof(int64_t) * 6 * E, 0) != hipSuccess ||
+        hipHostMalloc(reinterpret_cast<void **>(&t->hcounts), sizeof(uint32_t) * E, 0) != hipSuccess) {
+        tier_free(t);
+        return MOE_EHIP;
+    }
+    t->slot_of.assign(E, -1);
+    t->expert_in.assign(slots, -1);
+    for (int e = 0; e < E; e++) tier_entry(t, e);
+    for (int e = 0; e < E; e++) t->hcounts[e] = 0;
+    if (hipMemcpy(t->dtab, t->htab, sizeof(int64_t) * 6 * E, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(t->dcounts, t->hcounts, sizeof(uint32_t) * E, hipMemcpyHostToDevice) != hipSuccess) {
+        tier_free(t);
+        return MOE_EHIP;
+    }
+    *out = t;
+    return MOE_OK;
+}
+
+void moe_tier_destroy(moe_tier_t *t)
+{
+    if (t) tier_free(t);
+}
+
+// replacements of pinned experts per repin (the four-swap limit)
+constexpr int kTierSwaps = 4;
+
+int moe_tier_repin(moe_tier_t *t, int32_t *copied, hipStream_t stream)
+{
+    if (!t) return MOE_EINVAL;
+    const int E = t->E, C = t->C;
+    if (copied) *copied = 0;
+    if (hipMemcpyAsync(t->hcounts, t->dcounts, sizeof(uint32_t) * E, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return MOE_EHIP;
+    std::vector<int32_t> next(E);
+    const int nc = moe_tier_plan(t->hcounts, E, C, t->slot_of.data(), next.data(), kTierSwaps);
+    if (nc < 0) return -nc;
+    for (int e = 0; e < E; e++)  // experts leaving HBM first: their entries point to the host again
+        if (t->slot_of[e] >= 0 && next[e] < 0) {
+            t->expert_in[t->slot_of[e]] = -1;
+            t->slot_of[e] = -1;
+            tier_entry(t, e);
+        }
+    for (int e = 0; e < E; e++)
+        if (next[e] >= 0 && t->slot_of[e] < 0) {
+            const int s = next[e];
+            for (int k = 0; k < 6; k++)
+                if (hipMemcpyAsync(t->pool[k] + (size_t)s * t->bytes[k], t->hsrc[k] + (size_t)e * t->bytes[k],
+                                   t->bytes[k], hipMemcpyHostToDevice, stream) != hipSuccess)
+                    return MOE_EHIP;
+            t->slot_of[e] = s;
+            t->expert_in[s] = e;
+            tier_entry(t, e);
+        }
+    for (int e = 0; e < E; e++) t->hcounts[e] >>= 1;  // usage decays by half per repin
+    if (hipMemcpyAsync(t->dtab, t->htab, sizeof(int64_t) * 6 * E, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipMemcpyAsync(t->dcounts, t->hcounts, sizeof(uint32_t) * E, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return MOE_EHIP;
+    if (copied) *copied = nc;
+    return MOE_OK;
+}
+
+int moe_tier_resident(const moe_tier_t *t, int32_t *slot_of)
+{
+    if (!t || !slot_of) return MOE_EINVAL;
+    for (int e = 0; e < t->E; e++) slot_of[e] = t->slot_of[e];
+    return MOE_OK;
+}
+
+int moe_tier_counts(const moe_tier_t *t, uint32_t *counts, hipStream_t stream)
+{
+    if (!t || !counts) return MOE_EINVAL;
+    if (hipMemcpyAsync(counts, t->dcounts, sizeof(uint32_t) * t->E, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
+int moe_layer_forward_tiered(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w,
+                             const float *bias, const moe_tier_t *tier, const moe_weights_t *shared, float *y,
+                             int32_t *idx_out, float *w_out, uint32_t flags, void *ws, size_t ws_bytes,
+                             hipStream_t stream)
+{
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (!tier) return MOE_EINVAL;
+    const moe_shape_t &ts = tier->shape;
+    if (ts.hidden != shape->hidden || ts.inter != shape->inter || ts.n_experts != shape->n_experts ||
+        ts.wbits != shape->wbits)
+        return MOE_EINVAL;
+    if (shape->n_shared && (rc = check_weights(shared))) return rc;
+    if (!shape->n_shared && shared) return MOE_EINVAL;
+    if (T < 0) return MOE_EINVAL;
+    if (flags & ~(3u | MOE_ACCUMULATE | MOE_STAGE_MASK)) return MOE_EINVAL;
+    const uint32_t path = flags & 3u;
+    if (path == 3u) return MOE_EINVAL;
+    if (path == MOE_PATH_GROUPED || T > kGemvMaxT) return MOE_EUNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !gate_w || !bias || !y || !ws) return MOE_EINVAL;
+    if ((idx_out == nullptr) != (w_out == nullptr)) return MOE_EINVAL;
+    if (!al(x, 16) || !al(gate_w, 16) || !al(y, 4) || !al(ws, 256)) return MOE_EINVAL;
+    if (x == y) return MOE_EINVAL;
+    return layer_gemv(*shape, x, T, gate_w, bias, &tier->base, shared, y, idx_out, w_out, flags & ~3u, ws,
+                      ws_bytes, nullptr, 0.0, stream, tier->dtab, tier->dcounts);
 }
 
 int moe_rmsnorm(const float *x, const float *g, double eps, int32_t T, int32_t H, float *out, hipStream_t stream)

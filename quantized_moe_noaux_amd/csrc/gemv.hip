@@ -92,6 +92,23 @@ __device__ __forceinline__ PlanPairs plan_pairs(const int *plan, const PlanDims 
     return q;
 }
 
+// Expert e's tensors through the expert table: the routed base pointers
+// plus e's byte offsets (the offsets are workgroup-uniform scalar loads, and
+// the pointers stay derived from the kernel's own arguments, so every access
+// through them is a global one)
+__device__ __forceinline__ moe_weights_t table_view(const GemvArgs &a, int e)
+{
+    const int64_t *o = a.toff + (size_t)e * 6;
+    moe_weights_t v;
+    v.gate = a.routed.gate + o[0];
+    v.up = a.routed.up + o[1];
+    v.down = a.routed.down + o[2];
+    v.gate_s = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(a.routed.gate_s) + o[3]);
+    v.up_s = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(a.routed.up_s) + o[4]);
+    v.down_s = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(a.routed.down_s) + o[5]);
+    return v;
+}
+
 // The plan of one token (slots = its kept experts in rank order, slot r
 // taking pair r, then the shared expert; a batch of one needs no union).  Kept apart from the batch plan so that a caller that
 // only ever routes one token compiles no access through generic pointers: a
@@ -167,6 +184,7 @@ __device__ __forceinline__ void build_plan(const GemvArgs &a, const PlanDims &pd
         for (int t = wv; t < T; t += nw) {
             const WaveSel ws = wave_topk(a.rc, a.logits + (size_t)t * a.E, a.lstride, a.lparts, a.bias, k);
             if (lane < k) { s_idx[t * k + lane] = ws.e; s_w[t * k + lane] = ws.w; }
+            if (a.counts && lane < k && ws.e >= 0) atomicAdd(&a.counts[ws.e], 1u);
             uint32_t word = 0u;
             for (int i = 0; i < k; i++) {
                 const int e = __builtin_amdgcn_readlane(ws.e, i);  // e < 0: dropped by top-p
@@ -734,7 +752,7 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
 // runs the whole selection and publishes the plan for the down kernel, and
 // the routing when asked; with adaptive top-p every workgroup does, since
 // whether rank u is kept depends on all the weights.
-template <int WB, int CPT, int RPS>
+template <int WB, int CPT, int RPS, bool TAB>
 __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, int tiles, float (*s_h)[32],
                                        float (*part)[1][kSwGroups][32])
 {
@@ -759,6 +777,8 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
                 a.idx_out[threadIdx.x] = s_idx[threadIdx.x];
                 a.w_out[threadIdx.x] = s_w[threadIdx.x];
             }
+            if (a.counts && threadIdx.x < a.rc.k && s_idx[threadIdx.x] >= 0)
+                atomicAdd(&a.counts[s_idx[threadIdx.x]], 1u);
         }
         e = plan[pd.o_e + u];
         __syncthreads();  // plan[0] becomes the slot's token list below
@@ -773,10 +793,16 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
     if (e < 0 || e >= a.E || u >= pd.P) return;
     if (threadIdx.x == 0) plan[0] = 0;  // the slot's token list: token 0
     __syncthreads();
-    gate_up_tile_sw<WB, CPT, RPS, 1>(a, a.routed, e, row0, 1, plan, u, s_h, part);
+    if constexpr (TAB) {
+        const moe_weights_t V = table_view(a, e);
+        gate_up_tile_sw<WB, CPT, RPS, 1>(a, V, 0, row0, 1, plan, u, s_h, part);
+    } else {
+        gate_up_tile_sw<WB, CPT, RPS, 1>(a, a.routed, e, row0, 1, plan, u, s_h, part);
+    }
 }
 
-template <int WB, int CPT, int RPS, int TT>
+// TAB: routed experts through the expert table (a.toff)
+template <int WB, int CPT, int RPS, int TT, bool TAB = false>
 __global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
     __shared__ float s_h[TT][32];
@@ -784,7 +810,7 @@ __global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, con
     const int tiles = a.I / 32;
     if constexpr (TT == 1) {
         if (a.inline_route) {
-            gate_up_sw_routed_here<WB, CPT, RPS>(a, pd, tiles, s_h, part);
+            gate_up_sw_routed_here<WB, CPT, RPS, TAB>(a, pd, tiles, s_h, part);
             return;
         }
     }
@@ -796,6 +822,13 @@ __global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, con
     const int e = a.plan[pd.o_e + u], n_u = a.plan[pd.o_n + u], p0 = a.plan[pd.o_p0 + u];
     if (S > pd.S || u >= S) return;
     if (e < -1 || e >= a.E || n_u < 1 || n_u > a.T || p0 < 0 || p0 + n_u > pd.P) return;
+    if constexpr (TAB) {
+        if (e >= 0) {
+            const moe_weights_t V = table_view(a, e);
+            gate_up_tile_sw<WB, CPT, RPS, TT>(a, V, 0, row0, n_u, a.plan + pd.o_t + p0, p0, s_h, part);
+            return;
+        }
+    }
     gate_up_tile_sw<WB, CPT, RPS, TT>(a, (e >= 0) ? a.routed : a.shared, (e >= 0) ? e : 0, row0, n_u,
                                       a.plan + pd.o_t + p0, p0, s_h, part);
 }
@@ -818,7 +851,8 @@ constexpr int kDownRing = 3;
 // LDS index p, and the shared expert's rows are known), so they are
 // requested together with the plan, one dependent round trip fewer, and
 // the shared slot is combined first.
-template <int WB, int RPS, int TT, int NB, bool MB, bool EARLY = false>
+// TAB: routed experts through the expert table (a.toff).
+template <int WB, int RPS, int TT, int NB, bool MB, bool EARLY = false, bool TAB = false>
 __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
 {
     static_assert(!(EARLY && (MB || TT != 1)), "the early prologue is for one token, one batch");
@@ -874,6 +908,12 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     // loads then take a fixed per-lane offset
     auto slot_src = [&](int u) {
         const int uu = __builtin_amdgcn_readfirstlane(u);
+        if constexpr (TAB) {
+            const int e = plan[pd.o_e + uu];
+            const int64_t off = a.toff[(size_t)max(e, 0) * 6 + 2];
+            const uint8_t *b = (e >= 0) ? a.routed.down + off : a.shared.down;
+            return b + (size_t)row_base * rowbytes + (size_t)tid * 16;
+        }
         return slot_w(uu).down + ((size_t)slot_ee(uu) * a.H + row_base) * rowbytes + (size_t)tid * 16;
     };
     float acc[TT][NSTEP];
@@ -967,7 +1007,16 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     auto scale_issue = [&](int i0) {
         sci = min(i0 + tid, nsc - 1);
         const int u = sci / kDsRows;
-        scv = slot_w(u).down_s[(size_t)slot_ee(u) * a.H + row_base + sci % kDsRows];
+        if constexpr (TAB) {
+            const int e = plan[pd.o_e + u];
+            const int64_t off = a.toff[(size_t)max(e, 0) * 6 + 5];
+            const float *b = (e >= 0) ? reinterpret_cast<const float *>(
+                                            reinterpret_cast<const uint8_t *>(a.routed.down_s) + off)
+                                      : a.shared.down_s;
+            scv = b[row_base + sci % kDsRows];
+        } else {
+            scv = slot_w(u).down_s[(size_t)slot_ee(u) * a.H + row_base + sci % kDsRows];
+        }
     };
     auto stage_rest = [&](int c0) {
         for (; c0 < nst; c0 += SB * kDsThreads) {
@@ -1057,14 +1106,14 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     }
 }
 
-template <int WB, int CPT, int RPS, int TT>
+template <int WB, int CPT, int RPS, int TT, bool TAB = false>
 static int run_gate_up_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
-    k_gate_up_sw<WB, CPT, RPS, TT><<<pd.S * (a.I / 32), kSwThreads, 0, st>>>(a, cc, pd);
+    k_gate_up_sw<WB, CPT, RPS, TT, TAB><<<pd.S * (a.I / 32), kSwThreads, 0, st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
 
-template <int WB, int RPS, int TT>
+template <int WB, int RPS, int TT, bool TAB = false>
 static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
     constexpr int NB = kDownRing;
@@ -1073,12 +1122,13 @@ static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd
     // shapes): the kernel without the batch switch in its slot loop
     if constexpr (TT == 1) {
         if (a.T == 1 && a.logits && a.n_shared == 1 && pd.words <= kDsThreads && a.down_pmax >= pd.P) {
-            k_down_sw<WB, RPS, TT, NB, false, true><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
+            k_down_sw<WB, RPS, TT, NB, false, true, TAB><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
             return (int)hipGetLastError();
         }
     }
-    if (a.down_pmax >= pd.P) k_down_sw<WB, RPS, TT, NB, false><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
-    else k_down_sw<WB, RPS, TT, NB, true><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
+    if (a.down_pmax >= pd.P)
+        k_down_sw<WB, RPS, TT, NB, false, false, TAB><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
+    else k_down_sw<WB, RPS, TT, NB, true, false, TAB><<<a.H / kDsRows, kDsThreads, lds, st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
 
@@ -1153,6 +1203,13 @@ bool gemv_down_sw(const moe_shape_t &s)
     return s.hidden % kDsRows == 0 && chunk_cfg(s.inter, s.wbits, cc) && down_sw_kind(cc.cpr) != 0;
 }
 
+bool gemv_table_ok(const moe_shape_t &s)
+{
+    ChunkCfg cg, cd;
+    return s.wbits == 4 && s.hidden % kDsRows == 0 && chunk_cfg(s.hidden, 4, cg) && gate_up_sw_kind(cg.cpr) == 1 &&
+           chunk_cfg(s.inter, 4, cd) && down_sw_kind(cd.cpr) == 1;
+}
+
 bool gemv_inline_route(const moe_shape_t &s, int T)
 {
     ChunkCfg cc;
@@ -1165,6 +1222,11 @@ int launch_gate_up(const GemvArgs &a, hipStream_t st)
     if (!chunk_cfg(a.H, a.wbits, cc)) return (int)hipErrorInvalidValue;
     const PlanDims pd = plan_dims(a.T, a.rc.k, a.n_shared, a.logits == nullptr);
     const int kind = gate_up_sw_kind(cc.cpr);
+    if (a.toff) {  // expert table: the int4 production row widths (checked by the caller)
+        if (kind != 1 || a.wbits != 4) return (int)hipErrorInvalidValue;
+        return a.T == 1 ? run_gate_up_sw<4, 1, 1, 1, true>(a, cc, pd, st)
+                        : run_gate_up_sw<4, 1, 1, 8, true>(a, cc, pd, st);
+    }
     if (kind == 1 && a.wbits == 4) { MOE_SW_TTX(run_gate_up_sw, 4, 1, 1) }
     if (kind == 1 && a.wbits == 8) { MOE_SW_TT(run_gate_up_sw, 8, 1, 1) }
     if (kind == 1 && a.wbits == 2) { MOE_SW_TT(run_gate_up_sw, 2, 1, 1) }
@@ -1183,6 +1245,10 @@ int launch_down(const GemvArgs &args, hipStream_t st)
     GemvArgs a = args;
     a.down_pmax = down_pair_cap(a.wbits, a.I, pd);
     const int kind = down_sw_kind(cc.cpr);
+    if (a.toff) {
+        if (kind != 1 || a.wbits != 4 || a.H % kDsRows) return (int)hipErrorInvalidValue;
+        return a.T == 1 ? run_down_sw<4, 4, 1, true>(a, cc, pd, st) : run_down_sw<4, 4, 8, true>(a, cc, pd, st);
+    }
     if (a.H % kDsRows == 0) {
         if (kind == 1 && a.wbits == 4) { MOE_SW_TTX(run_down_sw, 4, 4) }
         if (kind == 1 && a.wbits == 8) { MOE_SW_TT(run_down_sw, 8, 4) }

@@ -200,9 +200,18 @@ struct GemvArgs {
     int inline_route;
     // pairs the row-sweep down kernel stages at a time (down_pair_cap)
     int down_pmax;
+    // expert table (tiered weights): expert e's six tensors are at the
+    // routed base pointers plus the byte offsets toff[6e .. 6e+5] (gate, up,
+    // down, gate_s, up_s, down_s); nullptr: the stacks [E][rows][bytes]
+    const int64_t *toff;
+    // per-expert selection counts, incremented by the routing (or nullptr)
+    uint32_t *counts;
 };
 // Whether a T-token call of this shape routes inside the gate/up launch
 // (one token, row-sweep gate/up kernel) instead of in a plan launch.
+// Whether the expert-table (tiered) GEMV kernels take this shape: int4
+// weights at the production row widths.
+bool gemv_table_ok(const moe_shape_t &s);
 bool gemv_inline_route(const moe_shape_t &s, int T);
 // one workgroup: routing of the chunk and its batch-union plan
 int launch_plan(const GemvArgs &a, hipStream_t st);

@@ -74,6 +74,14 @@ def _load():
         "moe_stack_forward": (ctypes.c_int, [P(moe_shape_t), vp, i32, P(moe_layer_t), i32, ctypes.c_double,
                                              vp, vp, u32, vp, sz, vp]),
         "moe_stack_workspace_bytes": (sz, [P(moe_shape_t), i32, u32]),
+        "moe_tier_create": (ctypes.c_int, [P(moe_shape_t), P(moe_weights_t), i32, P(vp)]),
+        "moe_tier_repin": (ctypes.c_int, [vp, P(i32), vp]),
+        "moe_tier_plan": (ctypes.c_int, [P(u32), i32, i32, P(i32), P(i32), i32]),
+        "moe_tier_resident": (ctypes.c_int, [vp, P(i32)]),
+        "moe_tier_counts": (ctypes.c_int, [vp, P(u32), vp]),
+        "moe_layer_forward_tiered": (ctypes.c_int, [P(moe_shape_t), vp, i32, vp, vp, vp, P(moe_weights_t), vp, vp,
+                                                    vp, u32, vp, sz, vp]),
+        "moe_tier_destroy": (None, [vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -238,3 +246,75 @@ def moe_mtp_accept(draft, p_logits, q_logits, tau, u, n_acc, next_tok, ws, strea
         B, D, V, _ptr(draft, torch.int32) if D else None, _ptr(p_logits, torch.float32),
         _ptr(q_logits, torch.float32) if D else None, float(tau), _ptr(u, torch.float64),
         _ptr(n_acc, torch.int32), _ptr(next_tok, torch.int32), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- expert tier
+def _host_ptr(t, dtype):
+    """pinned host tensor -> its address (the tier maps it for the device)"""
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("tier host tensors must be pinned host memory")
+    if not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError("expected a contiguous %s tensor" % dtype)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Tier:
+    """One layer's HBM / host expert tier (moe_tier_*).  host_w: the routed
+    stacks as pinned host tensors (kept referenced here)."""
+
+    def __init__(self, sh, host_w, slots):
+        self._host = host_w
+        hw = moe_weights_t(_host_ptr(host_w.gate, torch.uint8), _host_ptr(host_w.up, torch.uint8),
+                           _host_ptr(host_w.down, torch.uint8), _host_ptr(host_w.gate_s, torch.float32),
+                           _host_ptr(host_w.up_s, torch.float32), _host_ptr(host_w.down_s, torch.float32))
+        self.h = ctypes.c_void_p()
+        self.E = sh.n_experts
+        _chk("moe_tier_create", lib.moe_tier_create(ctypes.byref(sh), ctypes.byref(hw), slots, ctypes.byref(self.h)))
+
+    def repin(self, stream=None):
+        n = ctypes.c_int32(0)
+        _chk("moe_tier_repin", lib.moe_tier_repin(self.h, ctypes.byref(n), _stream(stream)))
+        return n.value
+
+    def resident(self):
+        out = (ctypes.c_int32 * self.E)()
+        _chk("moe_tier_resident", lib.moe_tier_resident(self.h, out))
+        return list(out)
+
+    def counts(self, stream=None):
+        out = (ctypes.c_uint32 * self.E)()
+        _chk("moe_tier_counts", lib.moe_tier_counts(self.h, out, _stream(stream)))
+        return list(out)
+
+    def close(self):
+        if self.h:
+            lib.moe_tier_destroy(self.h)
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def moe_tier_plan(heat, C, slot_in, max_swaps=4):
+    """The repin decision (host only): returns (copies, slot_out)."""
+    E = len(heat)
+    h = (ctypes.c_uint32 * E)(*heat)
+    si = (ctypes.c_int32 * E)(*slot_in)
+    so = (ctypes.c_int32 * E)()
+    n = lib.moe_tier_plan(h, E, C, si, so, max_swaps)
+    if n < 0:
+        raise MoeError("moe_tier_plan", -n)
+    return n, list(so)
+
+
+def moe_layer_forward_tiered(sh, x, gate_w, bias, tier, shared, y, ws, idx_out=None, w_out=None, flags=0,
+                             stream=None):
+    sw = weights(shared) if shared is not None else None
+    _chk("moe_layer_forward_tiered", lib.moe_layer_forward_tiered(
+        ctypes.byref(sh), _ptr(x, torch.float32), x.shape[0], _ptr(gate_w, torch.float32),
+        _ptr(bias, torch.float32), tier.h, ctypes.byref(sw) if sw is not None else None,
+        _ptr(y, torch.float32), _ptr(idx_out, torch.int32), _ptr(w_out, torch.float32), flags,
+        _ptr(ws), ws.numel(), _stream(stream)))

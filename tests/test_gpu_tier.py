@@ -1,0 +1,112 @@
+"""GPU parity of the HBM / host expert tier: the layer read through the
+expert table, with every routed expert in pinned host memory or some of them
+in HBM slots after a repin, equals moe_layer_forward on the same weights in
+HBM bit for bit, and the oracle within the layer tolerance.  The selection
+counts equal the routing's own.  A decode-width layer (hidden 6144,
+inter 2048, int4) with 16 routed experts keeps the host copy small."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import DevLayer, assert_close
+from test_gpu_layer import forward, reference
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m(dev):
+    from quantized_moe_noaux_amd import moe
+    return moe
+
+
+def pinned_copy(w):
+    return synth.DeviceWeights(*[getattr(w, f).cpu().pin_memory() for f in
+                                 ("gate", "up", "down", "gate_s", "up_s", "down_s")])
+
+
+def tiered(m, L, tier, T):
+    wl = L.wl
+    sh = m.shape_of(wl)
+    dev = L.x.device
+    y = torch.empty((T, wl.hidden), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, wl.top_k), dtype=torch.float32, device=dev)
+    ws = m.workspace(m.moe_workspace_bytes(sh, T, m.MOE_PATH_GEMV), dev)
+    m.moe_layer_forward_tiered(sh, L.x[:T], L.gate_w, L.bias, tier, L.shared, y, ws, idx, w)
+    torch.cuda.synchronize()
+    return y, idx.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def layer(dev):
+    wl = synth.workload("decode_int4", n_experts=16, n_group=4, topk_group=2, top_k=4, T=8)
+    L = DevLayer(wl, dev)
+    return L, pinned_copy(L.routed)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_all_experts_on_the_host(m, layer, T):
+    L, host = layer
+    tier = m.Tier(m.shape_of(L.wl), host, 4)
+    try:
+        print("tier parity: all on host, T=%d" % T, flush=True)
+        y, idx, w = tiered(m, L, tier, T)
+        y0, idx0, w0 = forward(m, L, T)
+        assert np.array_equal(idx, idx0) and np.array_equal(w, w0)
+        assert torch.equal(y, y0)
+        counts = tier.counts()
+        assert counts == list(np.bincount(idx.ravel(), minlength=L.wl.n_experts))
+        y_ref, idx_ref, _ = reference(L, T)
+        assert np.array_equal(idx, idx_ref)
+        assert_close(y.cpu().numpy(), y_ref)
+    finally:
+        tier.close()
+
+
+def test_repin_moves_the_hot_experts(m, layer):
+    L, host = layer
+    E, C = L.wl.n_experts, 5
+    tier = m.Tier(m.shape_of(L.wl), host, C)
+    try:
+        y0, _, _ = forward(m, L, 8)
+        for step in range(3):
+            print("tier parity: repin round %d" % step, flush=True)
+            yt, idx, _ = tiered(m, L, tier, 8)
+            assert torch.equal(yt, y0)
+            heat = tier.counts()
+            before = tier.resident()
+            n_exp, after_exp = m.moe_tier_plan(heat, C, before)
+            n = tier.repin()
+            assert n == n_exp and tier.resident() == after_exp
+            assert tier.counts() == [h >> 1 for h in heat]
+        assert sum(s >= 0 for s in tier.resident()) == C   # 32 selections a round fill every slot
+        for T in (1, 8):
+            yt, _, _ = tiered(m, L, tier, T)
+            y0, _, _ = forward(m, L, T)
+            assert torch.equal(yt, y0)
+    finally:
+        tier.close()
+
+
+def test_tier_argument_errors(m, layer, dev):
+    L, host = layer
+    sh = m.shape_of(L.wl)
+    with pytest.raises(ValueError):
+        m.Tier(sh, L.routed, 2)                       # device tensors, not pinned host memory
+    with pytest.raises(m.MoeError):
+        m.Tier(sh, host, L.wl.n_experts + 1)          # more slots than experts
+    tiny = synth.workload("tiny")
+    Lt = DevLayer(tiny, dev)
+    with pytest.raises(m.MoeError):
+        m.Tier(m.shape_of(tiny), pinned_copy(Lt.routed), 2)   # row widths without the table kernels
+    tier = m.Tier(sh, host, 2)
+    try:
+        ws = m.workspace(m.moe_workspace_bytes(sh, 9, m.MOE_PATH_GEMV), dev)
+        y = torch.empty((9, L.wl.hidden), dtype=torch.float32, device=dev)
+        x9 = torch.zeros((9, L.wl.hidden), dtype=torch.float32, device=dev)
+        with pytest.raises(m.MoeError):
+            m.moe_layer_forward_tiered(sh, x9, L.gate_w, L.bias, tier, L.shared, y, ws)   # T > 8
+    finally:
+        tier.close()
