@@ -33,6 +33,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -185,7 +186,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_int4",
-                    choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2", "mtp_int4"])
+                    choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2", "mtp_int4", "tier_int4"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--graph", action="store_true", help="launch each step as a captured HIP graph")
     ap.add_argument("--top-p", type=float, default=0.0, help="adaptive expert top-p (decode / verify)")
@@ -194,6 +195,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=None,
                     help="decode_int4 / verify_int8: tokens per step (the verify batch 1 + drafts)")
     ap.add_argument("--temp", type=float, default=0.7, help="mtp_int4: sampling temperature (0 = greedy)")
+    ap.add_argument("--slots", type=int, default=32, help="tier_int4: HBM slots for routed experts (of 256)")
+    ap.add_argument("--repin", type=int, default=16, help="tier_int4: tokens between live repins")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -223,6 +226,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "mtp_int4":
         return bench_mtp(args)
+    if args.workload == "tier_int4":
+        return bench_tier(args)
     wl = synth.workload(args.workload)
     if args.top_p:
         if wl.layers > 1 or args.workload == "prefill_int4":
@@ -743,6 +748,120 @@ def bench_mtp(args):
                    "verify_layer_us": lay_ms * 1e3, "acceptance_us": acc_ms * 1e3,
                    "decode_layer_us": dec_ms * 1e3, "decode_tokens_per_s": dec_tok_s},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_tier(args):
+    """Decode through the HBM / host expert tier: the int4 decode layer with
+    every routed expert in pinned host memory and --slots of them in HBM,
+    the live repin every --repin tokens inside the timed loop.  The router
+    bias is the skewed N(0, 0.5) of the prefill workload, so that some
+    experts are hotter than others.  A step is one token; the timed loop is
+    back to back (no cache flush: the misses' host reads dominate), its time
+    covers the layer and the repins (whose count read-back synchronises).
+    The hit rate is measured afterwards over the same number of tokens with
+    the resident set the timed loop left."""
+    import numpy as np
+    import torch
+    import synth
+    from quantized_moe_noaux_amd import moe
+
+    dev = "cuda:0"
+    wl = synth.workload("decode_int4", bias_sigma=math.sqrt(0.5))
+    C, R = args.slots, args.repin
+    n_inputs = 64
+    steps = args.steps if args.steps is not None else 256
+    warmup = args.warmup if args.warmup is not None else 64
+    sh = moe.shape_of(wl)
+    flags = moe.MOE_PATH_GEMV
+    log("bench: tier_int4 decode, %d of %d routed experts in HBM, repin every %d tokens" % (C, wl.n_experts, R))
+    host = synth.HostLayer(wl)
+    gate_w = torch.from_numpy(host.gate_w).to(dev)
+    bias = torch.from_numpy(host.bias).to(dev)
+    routed = synth.device_weights(wl, 0, 0, wl.n_experts, dev)
+    shared = synth.device_weights(wl, 0, wl.n_experts, 1, dev)
+    pinned = []
+    for f in ("gate", "up", "down", "gate_s", "up_s", "down_s"):
+        d = getattr(routed, f)
+        h = torch.empty(d.shape, dtype=d.dtype, pin_memory=True)
+        h.copy_(d)
+        pinned.append(h)
+    hostw = synth.DeviceWeights(*pinned)
+    tier = moe.Tier(sh, hostw, C)
+    xs = torch.stack([torch.from_numpy(
+        synth.host_normals(wl.seed + i, synth.stream_id(0, synth.X), wl.hidden, 1.0).reshape(1, wl.hidden))
+        for i in range(n_inputs)]).to(dev)
+    y = torch.empty((1, wl.hidden), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, wl.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, wl.top_k), dtype=torch.float32, device=dev)
+    ws = moe.workspace(moe.moe_workspace_bytes(sh, 1, flags), dev)
+    torch.cuda.synchronize()
+    log("bench: pinned host copy of the routed experts ready (%.2f GB)" % (wl.n_experts * wl.expert_bytes / 1e9))
+
+    def step(i):
+        moe.moe_layer_forward_tiered(sh, xs[i % n_inputs], gate_w, bias, tier, shared, y, ws, idx, wts)
+
+    def resident_step(i):
+        moe.moe_layer_forward(sh, xs[i % n_inputs], gate_w, bias, routed, shared, y, ws, idx, wts, flags=flags)
+
+    copied = 0
+    for i in range(warmup):
+        step(i)
+        if (i + 1) % R == 0:
+            copied += tier.repin()
+    torch.cuda.synchronize()
+    log("bench: %d warmup tokens, %d experts copied into HBM" % (warmup, copied))
+    copied = 0
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+        if (i + 1) % R == 0:
+            copied += tier.repin()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # the same layer with every expert in HBM, timed the same way
+    for i in range(warmup):
+        resident_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        resident_step(warmup + i)
+    torch.cuda.synchronize()
+    ms_res = (time.perf_counter() - t0) * 1e3 / steps
+    # hit rate with the resident set the timed loop left (no repin)
+    slot_of = tier.resident()
+    hits = sel = 0
+    for i in range(steps):
+        step(warmup + steps + i)
+        e = idx.cpu().numpy().ravel()
+        e = e[e >= 0]
+        sel += len(e)
+        hits += sum(slot_of[k] >= 0 for k in e)
+    hit = hits / max(sel, 1)
+    tier.close()
+    value = 1e3 / ms
+    weight_bytes = (wl.top_k + 1) * wl.expert_bytes
+    miss_bytes = wl.top_k * (1.0 - hit) * wl.expert_bytes
+    log("bench: step %.1f us (%.0f tok/s), hit rate %.1f%%, %.1f experts copied per repin; "
+        "all experts in HBM: %.1f us" % (ms * 1e3, value, 100 * hit, copied / max(1, steps // R), ms_res * 1e3))
+    out = {
+        "metric": "MoE-layer tokens/s, int4 decode through the HBM / host expert tier",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8", "data": "synthetic (seeded SplitMix64 weights, router bias N(0,0.5), N(0,1) tokens, "
+                               "%d rotating inputs, no cache flush)" % n_inputs,
+        "config": {"workload": "tier_int4", "T": 1, "hbm_slots": C, "repin_every": R, "hidden": wl.hidden,
+                   "inter": wl.inter, "n_experts": wl.n_experts, "top_k": wl.top_k, "n_shared": wl.n_shared,
+                   "wbits": wl.wbits, "path": "gemv"},
+        "roofline": {"bound": "hbm", "kernel": "layer", "achieved": weight_bytes / (ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_per_launch": weight_bytes / 1e9, "avg_launch_us": ms * 1e3},
+        "detail": {"hit_rate": hit, "host_bytes_per_token": miss_bytes,
+                   "host_read_GBps": miss_bytes / (ms * 1e-3) / 1e9, "experts_copied_timed": copied,
+                   "resident_step_us": ms_res * 1e3},
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 
