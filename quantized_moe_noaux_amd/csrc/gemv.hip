@@ -43,7 +43,7 @@ bool chunk_cfg(int in_dim, int wbits, ChunkCfg &cc)
 GemvWs gemv_ws(const moe_shape_t &s, int T, int Tc, bool single)
 {
     GemvWs w;
-    const int H = s.hidden, I = s.inter, E = s.n_experts;
+    const int H = s.hidden, I = s.inter;
     // plan and h buffers hold one chunk of Tc tokens
     PlanDims pd = plan_dims(Tc, s.top_k, s.n_shared, single);
     size_t o = 0;
