@@ -119,7 +119,10 @@ def test_route_bit_exact(dev, m, name, T):
 
 @pytest.mark.parametrize("E,G,tg,k,H", [(12, 3, 1, 4, 64), (32, 8, 3, 5, 96), (8, 8, 8, 3, 32),
                                         (512, 8, 4, 8, 128), (160, 5, 2, 6, 64), (24, 8, 2, 2, 32),
-                                        (1, 1, 1, 1, 32)])
+                                        (1, 1, 1, 1, 32),
+                                        # experts per lane 2, 6 and 2 with 16-lane groups; one 64-lane group
+                                        (128, 8, 4, 8, 64), (384, 8, 4, 8, 64), (96, 3, 2, 4, 32),
+                                        (64, 1, 1, 6, 32)])
 def test_route_other_shapes(dev, m, E, G, tg, k, H):
     wl = synth.workload("tiny", n_experts=E, n_group=G, topk_group=tg, top_k=k, hidden=H)
     L = synth.HostLayer(wl, T=37)

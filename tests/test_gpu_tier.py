@@ -90,6 +90,29 @@ def test_repin_moves_the_hot_experts(m, layer):
         tier.close()
 
 
+@pytest.mark.parametrize("T", [1, 5])
+def test_tiered_top_p_and_accumulate(m, layer, dev, T):
+    """adaptive top-p and MOE_ACCUMULATE through the table: equal to the HBM layer"""
+    L, host = layer
+    sh = m.shape_of(L.wl, top_p=0.7)
+    tier = m.Tier(sh, host, 6)
+    try:
+        ws = m.workspace(m.moe_workspace_bytes(sh, T, m.MOE_PATH_GEMV), dev)
+        y0 = torch.randn((T, L.wl.hidden), dtype=torch.float32, device=dev)
+        ya, yb = y0.clone(), y0.clone()
+        for rnd in range(2):
+            print("tier parity: top-p 0.7, accumulate, T=%d, round %d" % (T, rnd), flush=True)
+            m.moe_layer_forward_tiered(sh, L.x[:T], L.gate_w, L.bias, tier, L.shared, ya, ws,
+                                       flags=m.MOE_ACCUMULATE)
+            m.moe_layer_forward(sh, L.x[:T], L.gate_w, L.bias, L.routed, L.shared, yb, ws,
+                                flags=m.MOE_PATH_GEMV | m.MOE_ACCUMULATE)
+            torch.cuda.synchronize()
+            assert torch.equal(ya, yb)
+            tier.repin()
+    finally:
+        tier.close()
+
+
 def test_tier_argument_errors(m, layer, dev):
     L, host = layer
     sh = m.shape_of(L.wl)
