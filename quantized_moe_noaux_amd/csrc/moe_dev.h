@@ -51,18 +51,42 @@ __device__ __forceinline__ int wave_sum_i(int v)
     return v;
 }
 
+// Lane exchanges without the LDS crossbar: DPP moves (quad_perm, row
+// mirrors) stay inside the VALU, and readlane takes one lane's value into
+// scalar registers; a cross-lane permute through the LDS crossbar costs a
+// round trip of ~100 cycles per step on MI355X.
+template <int CTRL> __device__ __forceinline__ double dpp_d(double v)
+{
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int l)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
+// Sum and maximum over the 64 lanes (all lanes active), the same value in
+// every lane: pairs inside each row of 16 lanes by DPP (lane ^ 1, lane ^ 2,
+// the other quad of 8, the other half of 16; a commutative step leaves both
+// partners equal), then the four row results in a fixed order.
 __device__ __forceinline__ double wave_sum_d(double v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += dpp_d<0xB1>(v);
+    v += dpp_d<0x4E>(v);
+    v += dpp_d<0x141>(v);
+    v += dpp_d<0x140>(v);
+    return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
 }
 
 __device__ __forceinline__ double wave_max_d(double v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-    return v;
+    v = fmax(v, dpp_d<0xB1>(v));
+    v = fmax(v, dpp_d<0x4E>(v));
+    v = fmax(v, dpp_d<0x141>(v));
+    v = fmax(v, dpp_d<0x140>(v));
+    return fmax(fmax(readlane_d(v, 0), readlane_d(v, 16)), fmax(readlane_d(v, 32), readlane_d(v, 48)));
 }
 
 // ---------------------------------------------------------------- RMSNorm pieces

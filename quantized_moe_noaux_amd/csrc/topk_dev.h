@@ -21,20 +21,6 @@ __device__ __forceinline__ uint64_t order_key(double v)
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// Lane exchanges for the group phase.  DPP moves (quad_perm, row mirrors)
-// stay inside the VALU; a cross-lane permute through the LDS crossbar costs
-// a round trip of ~100 cycles per step on MI355X.
-template <int CTRL> __device__ __forceinline__ double dpp_d(double v)
-{
-    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
-    return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ double readlane_d(double v, int l)
-{
-    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
-                            __builtin_amdgcn_readlane(__double2loint(v), l));
-}
 // (b1, b2) = the two largest of the multiset {b1, b2, o1, o2}, where b1 >= b2
 // and o1 >= o2
 __device__ __forceinline__ void merge_top2(double &b1, double &b2, double o1, double o2)
