@@ -579,7 +579,25 @@ __global__ __launch_bounds__(256) void k_down_rg(const GemvArgs a, const ChunkCf
 // values they do not keep with the lane O apart and add the received half.
 // NA and O are compile-time, so every register index is static (a runtime
 // width would turn v[j + NA/2] into compare/select ladders).
-template <int N, int O, int NA>
+// The partner of a lane at level O: a lane whose bit O differs and whose
+// bits above O agree.  With DPP, inside a row of 16 that is a DPP move in
+// the VALU (lane ^ 1, lane ^ 2, then the mirror of 8 and of 16, which flip
+// bit 2 and bit 3 together with the bits below) and only level 16 crosses
+// rows; without, every level is a swap through the LDS crossbar.  Measured
+// on MI355X: DPP pays where a workgroup reduces several token rows at once
+// (verify batches of 3 and 5 tokens, 3-4% faster); one token keeps the
+// crossbar, which leaves its VALU-heavy int2 sweep to the VALU.
+template <int O, bool DPP> __device__ __forceinline__ float rs_partner(float v)
+{
+    if constexpr (O == 16 || !DPP) {
+        return __shfl_xor(v, O);
+    } else {
+        constexpr int CTRL = O == 1 ? 0xB1 : O == 2 ? 0x4E : O == 4 ? 0x141 : 0x140;
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    }
+}
+
+template <int N, int O, int NA, bool DPP>
 __device__ __forceinline__ void reduce_scatter_level(float (&v)[N], int lane)
 {
     if constexpr (NA > 1) {
@@ -589,21 +607,21 @@ __device__ __forceinline__ void reduce_scatter_level(float (&v)[N], int lane)
         for (int j = 0; j < HALF; j++) {
             const float send = upper ? v[j] : v[j + HALF];
             const float keep = upper ? v[j + HALF] : v[j];
-            v[j] = keep + __shfl_xor(send, O);
+            v[j] = keep + rs_partner<O, DPP>(send);
         }
     } else {
-        v[0] += __shfl_xor(v[0], O);
+        v[0] += rs_partner<O, DPP>(v[0]);
     }
-    if constexpr (O > 1) reduce_scatter_level<N, O / 2, (NA > 1 ? NA / 2 : 1)>(v, lane);
+    if constexpr (O > 1) reduce_scatter_level<N, O / 2, (NA > 1 ? NA / 2 : 1), DPP>(v, lane);
 }
 
 // Sum of N values over the 32 lanes of a half-wave, scattered: lane l ends
 // with the total of value j = l / (32 / N) (fixed pairing and order, so the
 // result is run-to-run identical).
-template <int N>
+template <int N, bool DPP = false>
 __device__ __forceinline__ float group32_reduce_scatter(float (&v)[N])
 {
-    reduce_scatter_level<N, 16, N>(v, lane_id());
+    reduce_scatter_level<N, 16, N, DPP>(v, lane_id());
     return v[0];
 }
 
@@ -713,8 +731,8 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
 #pragma unroll
             for (int tt = 0; tt < TT; tt++) {
                 if (tt < n_u) {
-                    const float g = group32_reduce_scatter<PS>(accg[tt]);
-                    const float v = group32_reduce_scatter<PS>(accu[tt]);
+                    const float g = group32_reduce_scatter<PS, (TT > 1)>(accg[tt]);
+                    const float v = group32_reduce_scatter<PS, (TT > 1)>(accu[tt]);
                     if (writer) {
                         part[0][tt][grp][pass * 8 + jj * RPS + rowoff] = g;
                         part[1][tt][grp][pass * 8 + jj * RPS + rowoff] = v;
