@@ -186,7 +186,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_int4",
-                    choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2", "mtp_int4", "tier_int4"])
+                    choices=["decode_int4", "verify_int8", "prefill_int4", "stack_int2", "mtp_int4", "tier_int4",
+                             "tier_stack_int4"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--graph", action="store_true", help="launch each step as a captured HIP graph")
     ap.add_argument("--top-p", type=float, default=0.0, help="adaptive expert top-p (decode / verify)")
@@ -197,6 +198,7 @@ def main():
     ap.add_argument("--temp", type=float, default=0.7, help="mtp_int4: sampling temperature (0 = greedy)")
     ap.add_argument("--slots", type=int, default=32, help="tier_int4: HBM slots for routed experts (of 256)")
     ap.add_argument("--repin", type=int, default=16, help="tier_int4: tokens between live repins")
+    ap.add_argument("--layers", type=int, default=4, help="tier_stack_int4: layers")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -228,6 +230,8 @@ def main():
         return bench_mtp(args)
     if args.workload == "tier_int4":
         return bench_tier(args)
+    if args.workload == "tier_stack_int4":
+        return bench_tier_stack(args)
     wl = synth.workload(args.workload)
     if args.top_p:
         if wl.layers > 1 or args.workload == "prefill_int4":
@@ -861,6 +865,152 @@ def bench_tier(args):
         "detail": {"hit_rate": hit, "host_bytes_per_token": miss_bytes,
                    "host_read_GBps": miss_bytes / (ms * 1e-3) / 1e9, "experts_copied_timed": copied,
                    "resident_step_us": ms_res * 1e3},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_tier_stack(args):
+    """Decode through a stack of --layers int4 layers, each with its routed
+    experts in pinned host memory and --slots of them in HBM (one tier per
+    layer, the live repin every --repin tokens), x <- x + MoE_l(RMSNorm(x)),
+    once without and once with the router lookahead: before layer l runs,
+    layer l+1's router is applied to RMSNorm(x_l) on a side stream, its
+    experts are read back and prefetched into layer l+1's tier on that
+    stream, and layer l+1 waits for the prefetch.  The router bias is the
+    decode workload's N(0, 0.01), so no small hot set exists.  Each mode
+    runs --warmup tokens, then --steps timed tokens (a step is one token
+    through every layer, repins included)."""
+    import numpy as np
+    import torch
+    import synth
+    from quantized_moe_noaux_amd import moe
+
+    dev = "cuda:0"
+    Ln, C, R = args.layers, args.slots, args.repin
+    steps = args.steps if args.steps is not None else 16
+    warmup = args.warmup if args.warmup is not None else 16
+    wl = synth.workload("decode_int4", layers=Ln)
+    sh = moe.shape_of(wl)
+    log("bench: tier_stack_int4, %d layers, %d of %d routed experts in HBM per layer, repin every %d tokens" %
+        (Ln, C, wl.n_experts, R))
+    layers = []
+    for l in range(Ln):
+        host = synth.HostLayer(wl, layer=l, T=1)
+        routed = synth.device_weights(wl, l, 0, wl.n_experts, dev)
+        pinned = []
+        for f in ("gate", "up", "down", "gate_s", "up_s", "down_s"):
+            d = getattr(routed, f)
+            h = torch.empty(d.shape, dtype=d.dtype, pin_memory=True)
+            h.copy_(d)
+            pinned.append(h)
+        del routed
+        torch.cuda.synchronize()
+        layers.append(dict(gate_w=torch.from_numpy(host.gate_w).to(dev), bias=torch.from_numpy(host.bias).to(dev),
+                           g=torch.ones(wl.hidden, dtype=torch.float32, device=dev),
+                           shared=synth.device_weights(wl, l, wl.n_experts, 1, dev),
+                           host=synth.DeviceWeights(*pinned)))
+        torch.cuda.empty_cache()
+    log("bench: %d layers' routed experts in pinned host memory (%.1f GB)" %
+        (Ln, Ln * wl.n_experts * wl.expert_bytes / 1e9))
+    n_inputs = 64
+    xs = torch.stack([torch.from_numpy(
+        synth.host_normals(wl.seed + i, synth.stream_id(0, synth.X), wl.hidden, 1.0).reshape(1, wl.hidden))
+        for i in range(n_inputs)]).to(dev)
+    x0 = xs[0]
+    x = torch.empty_like(x0)
+    nrm = torch.empty_like(x0)
+    lnrm = torch.empty_like(x0)
+    idx = torch.empty((1, wl.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, wl.top_k), dtype=torch.float32, device=dev)
+    pidx = torch.empty((1, wl.top_k), dtype=torch.int32, device=dev)
+    pw = torch.empty((1, wl.top_k), dtype=torch.float32, device=dev)
+    ws = moe.workspace(moe.moe_workspace_bytes(sh, 1, moe.MOE_PATH_GEMV), dev)
+    rws = moe.workspace(moe.moe_route_workspace_bytes(sh, 1), dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def run(lookahead, ntok, t0, record=None):
+        tiers = [moe.Tier(sh, L["host"], C) for L in layers]
+        evs = [torch.cuda.Event() for _ in range(Ln)]
+        stats = {"pred": 0, "hit": 0, "sel": 0, "resident": 0, "copies": 0}
+        try:
+            def token(t, measure):
+                x.copy_(xs[t % n_inputs])   # rotating N(0, 1) tokens
+                for l in range(Ln):
+                    L = layers[l]
+                    if lookahead and l + 1 < Ln:
+                        side.wait_stream(main)
+                        with torch.cuda.stream(side):
+                            N = layers[l + 1]
+                            moe.moe_rmsnorm(x, N["g"], 1e-6, lnrm, stream=side)
+                            moe.moe_route(sh, lnrm, N["gate_w"], N["bias"], pidx, pw, rws, stream=side)
+                        ids = pidx.cpu().numpy().ravel()           # waits for the side stream
+                        stats["copies"] += tiers[l + 1].prefetch(ids, stream=side)
+                        evs[l + 1].record(side)
+                    if lookahead and l > 0:
+                        main.wait_event(evs[l])
+                    moe.moe_rmsnorm(x, L["g"], 1e-6, nrm)
+                    res = tiers[l].resident() if measure else None
+                    moe.moe_layer_forward_tiered(sh, nrm, L["gate_w"], L["bias"], tiers[l], L["shared"], x, ws,
+                                                 idx, wts, flags=moe.MOE_ACCUMULATE)
+                    if measure:
+                        sel = idx.cpu().numpy().ravel()
+                        stats["sel"] += len(sel)
+                        stats["resident"] += sum(res[e] != -1 for e in sel)
+                        if lookahead and l > 0:
+                            stats["pred"] += len(sel)
+                            stats["hit"] += len(set(sel.tolist()) & set(prev_pred[l].tolist()))
+                    if lookahead and l + 1 < Ln and measure:
+                        prev_pred[l + 1] = ids
+                if (t + 1) % R == 0:
+                    for tr in tiers:
+                        stats["copies"] += tr.repin()
+            prev_pred = {}
+            for t in range(t0, t0 + warmup):
+                token(t, False)
+            torch.cuda.synchronize()
+            stats["copies"] = 0
+            tic = time.perf_counter()
+            for t in range(t0 + warmup, t0 + warmup + ntok):
+                token(t, False)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - tic) * 1e3 / ntok
+            copies = stats["copies"]
+            for t in range(t0 + warmup + ntok, t0 + warmup + 2 * ntok):
+                token(t, True)
+            torch.cuda.synchronize()
+            return ms, copies, stats
+        finally:
+            for tr in tiers:
+                tr.close()
+
+    ms0, cp0, st0 = run(False, steps, 0)
+    log("bench: no lookahead: %.2f ms per token, hits %.1f%%, %d experts copied" %
+        (ms0, 100 * st0["resident"] / max(1, st0["sel"]), cp0))
+    ms1, cp1, st1 = run(True, steps, 0)
+    recall = st1["hit"] / max(1, st1["pred"])
+    log("bench: lookahead: %.2f ms per token, hits %.1f%%, lookahead recall %.1f%%, %d experts copied" %
+        (ms1, 100 * st1["resident"] / max(1, st1["sel"]), 100 * recall, cp1))
+    value = 1e3 / ms1
+    weight_bytes = Ln * (wl.top_k + 1) * wl.expert_bytes
+    out = {
+        "metric": "decode tokens/s, %d-layer int4 stack through the HBM / host expert tier with router lookahead" % Ln,
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8", "data": "synthetic (seeded SplitMix64 weights, router bias N(0,0.01), %d rotating "
+                               "N(0,1) tokens, one token a step)" % n_inputs,
+        "config": {"workload": "tier_stack_int4", "layers": Ln, "T": 1, "hbm_slots": C, "prefetch_slots": 16,
+                   "repin_every": R, "hidden": wl.hidden, "inter": wl.inter, "n_experts": wl.n_experts,
+                   "top_k": wl.top_k, "wbits": wl.wbits, "path": "gemv"},
+        "roofline": {"bound": "hbm", "kernel": "stack", "achieved": weight_bytes / (ms1 * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": weight_bytes / (ms1 * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_per_launch": weight_bytes / 1e9, "avg_launch_us": ms1 * 1e3},
+        "detail": {"no_lookahead_ms": ms0, "lookahead_ms": ms1, "lookahead_recall": recall,
+                   "hit_rate_no_lookahead": st0["resident"] / max(1, st0["sel"]),
+                   "hit_rate_lookahead": st1["resident"] / max(1, st1["sel"]),
+                   "copies_timed_no_lookahead": cp0, "copies_timed_lookahead": cp1},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

@@ -314,7 +314,23 @@ size_t moe_mtp_accept_workspace_bytes(int32_t B, int32_t D, int32_t V);
  *   index goes first) while its heat exceeds 1.25 times the other's (the
  *   25% hysteresis).  Returns the number of experts entering HBM, or minus
  *   MOE_EINVAL for bad arguments (an inconsistent slot_in).
- * moe_tier_resident -- slot_of[E] (host): each expert's HBM slot or -1.
+ * moe_tier_prefetch -- the router lookahead's prefetch (wpnews.pro feature
+ *   list, "Router-lookahead prefetch (PILOT=1)": layer L+1's router run on
+ *   layer L's state predicts its experts, which a separate I/O thread
+ *   fetches while layer L computes; here a side stream's copies): experts[n] (host) are
+ *   one layer's predicted experts, in priority order.  Each one neither
+ *   pinned nor already prefetched is copied into the tier's next prefetch
+ *   slot (a ring of min(16, E) slots, apart from the pinned ones; the
+ *   ring's oldest prefetch returns to the host stack) by asynchronous
+ *   host-to-device copies on stream, then the table is updated on stream;
+ *   at most one ring's worth per call, entries < 0 or >= E ignored.  The
+ *   routing is unchanged wherever an expert is read from.  *copied (if not
+ *   NULL) = experts copied.  The caller orders stream against every
+ *   forward on the same tier (events): a forward that overlaps a prefetch or
+ *   a repin of its tier races.  A repin frees the prefetch slot of an
+ *   expert it pins.
+ * moe_tier_resident -- slot_of[E] (host): each expert's pinned HBM slot,
+ *   -2 for a prefetched expert, else -1.
  * moe_tier_counts -- counts[E] (host) = the current heat (synchronises
  *   stream).
  * moe_layer_forward_tiered -- moe_layer_forward on the GEMV path (T <= 8;
@@ -331,6 +347,7 @@ int moe_tier_create(const moe_shape_t *shape, const moe_weights_t *host, int32_t
 int moe_tier_repin(moe_tier_t *tier, int32_t *copied, hipStream_t stream);
 int moe_tier_plan(const uint32_t *heat, int32_t E, int32_t C, const int32_t *slot_in, int32_t *slot_out,
                   int32_t max_swaps);
+int moe_tier_prefetch(moe_tier_t *tier, const int32_t *experts, int32_t n, int32_t *copied, hipStream_t stream);
 int moe_tier_resident(const moe_tier_t *tier, int32_t *slot_of);
 int moe_tier_counts(const moe_tier_t *tier, uint32_t *counts, hipStream_t stream);
 int moe_layer_forward_tiered(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w,

@@ -353,6 +353,9 @@ static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float 
 // ---------------------------------------------------------------- expert tier
 } // extern "C"
 
+// prefetch slots per tier (router lookahead)
+constexpr int kTierPrefetch = 16;
+
 struct moe_tier {
     moe_shape_t shape;
     int E, C;
@@ -364,14 +367,25 @@ struct moe_tier {
     int64_t *dtab, *htab;   // expert table (device) and its pinned host mirror
     uint32_t *dcounts, *hcounts;
     std::vector<int> slot_of, expert_in;
+    // prefetch slots (a ring): experts brought in ahead of use by the
+    // router lookahead, apart from the pinned slots
+    int P = 0, pnext = 0;
+    uint8_t *ppool[6] = {};
+    std::vector<int> pslot_of, pexpert;
+    // the last host-to-device copy of the table's host mirror: the mirror
+    // is changed only once it has completed
+    hipEvent_t uploaded = nullptr;
 };
 
 namespace {
 
 void tier_free(moe_tier *t)
 {
-    for (int i = 0; i < 6; i++)
+    for (int i = 0; i < 6; i++) {
         if (t->pool[i]) (void)hipFree(t->pool[i]);
+        if (t->ppool[i]) (void)hipFree(t->ppool[i]);
+    }
+    if (t->uploaded) (void)hipEventDestroy(t->uploaded);
     if (t->dtab) (void)hipFree(t->dtab);
     if (t->dcounts) (void)hipFree(t->dcounts);
     if (t->htab) (void)hipHostFree(t->htab);
@@ -387,15 +401,31 @@ uintptr_t base_addr(const moe_tier *t, int i)
     return (uintptr_t)p;
 }
 
-// the host mirror's entry of expert e: its slot in HBM, else the host stack
+// the host mirror's entry of expert e: its pinned slot, else its prefetch
+// slot, else the host stack
 void tier_entry(moe_tier *t, int e)
 {
-    const int s = t->slot_of[e];
+    const int s = t->slot_of[e], q = t->pslot_of[e];
     for (int i = 0; i < 6; i++) {
-        const uintptr_t a = (s >= 0) ? (uintptr_t)t->pool[i] + (uintptr_t)s * t->bytes[i]
-                                     : t->hdev[i] + (uintptr_t)e * t->bytes[i];
+        const uintptr_t a = (s >= 0)   ? (uintptr_t)t->pool[i] + (uintptr_t)s * t->bytes[i]
+                            : (q >= 0) ? (uintptr_t)t->ppool[i] + (uintptr_t)q * t->bytes[i]
+                                       : t->hdev[i] + (uintptr_t)e * t->bytes[i];
         t->htab[(size_t)e * 6 + i] = (int64_t)(a - base_addr(t, i));
     }
+}
+
+// the table's host mirror may change (its last upload has completed)
+int tier_mirror_free(moe_tier *t)
+{
+    return hipEventSynchronize(t->uploaded) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int tier_upload(moe_tier *t, hipStream_t stream)
+{
+    if (hipMemcpyAsync(t->dtab, t->htab, sizeof(int64_t) * 6 * t->E, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipEventRecord(t->uploaded, stream) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
 }
 
 // experts by (count desc, index asc)
@@ -501,10 +531,23 @@ int moe_tier_create(const moe_shape_t *shape, const moe_weights_t *host, int32_t
     }
     t->slot_of.assign(E, -1);
     t->expert_in.assign(slots, -1);
+    t->P = E < kTierPrefetch ? E : kTierPrefetch;
+    t->pslot_of.assign(E, -1);
+    t->pexpert.assign(t->P, -1);
+    for (int i = 0; i < 6; i++)
+        if (hipMalloc(reinterpret_cast<void **>(&t->ppool[i]), t->bytes[i] * t->P) != hipSuccess) {
+            tier_free(t);
+            return MOE_EHIP;
+        }
+    if (hipEventCreateWithFlags(&t->uploaded, hipEventDisableTiming) != hipSuccess) {
+        tier_free(t);
+        return MOE_EHIP;
+    }
     for (int e = 0; e < E; e++) tier_entry(t, e);
     for (int e = 0; e < E; e++) t->hcounts[e] = 0;
     if (hipMemcpy(t->dtab, t->htab, sizeof(int64_t) * 6 * E, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(t->dcounts, t->hcounts, sizeof(uint32_t) * E, hipMemcpyHostToDevice) != hipSuccess) {
+        hipMemcpy(t->dcounts, t->hcounts, sizeof(uint32_t) * E, hipMemcpyHostToDevice) != hipSuccess ||
+        hipEventRecord(t->uploaded, nullptr) != hipSuccess) {
         tier_free(t);
         return MOE_EHIP;
     }
@@ -531,6 +574,7 @@ int moe_tier_repin(moe_tier_t *t, int32_t *copied, hipStream_t stream)
     std::vector<int32_t> next(E);
     const int nc = moe_tier_plan(t->hcounts, E, C, t->slot_of.data(), next.data(), kTierSwaps);
     if (nc < 0) return -nc;
+    if (tier_mirror_free(t)) return MOE_EHIP;
     for (int e = 0; e < E; e++)  // experts leaving HBM first: their entries point to the host again
         if (t->slot_of[e] >= 0 && next[e] < 0) {
             t->expert_in[t->slot_of[e]] = -1;
@@ -546,12 +590,46 @@ int moe_tier_repin(moe_tier_t *t, int32_t *copied, hipStream_t stream)
                     return MOE_EHIP;
             t->slot_of[e] = s;
             t->expert_in[s] = e;
+            if (t->pslot_of[e] >= 0) {  // a prefetched expert now pinned: its prefetch slot is free
+                t->pexpert[t->pslot_of[e]] = -1;
+                t->pslot_of[e] = -1;
+            }
             tier_entry(t, e);
         }
     for (int e = 0; e < E; e++) t->hcounts[e] >>= 1;  // usage decays by half per repin
-    if (hipMemcpyAsync(t->dtab, t->htab, sizeof(int64_t) * 6 * E, hipMemcpyHostToDevice, stream) != hipSuccess ||
+    if (tier_upload(t, stream) ||
         hipMemcpyAsync(t->dcounts, t->hcounts, sizeof(uint32_t) * E, hipMemcpyHostToDevice, stream) != hipSuccess)
         return MOE_EHIP;
+    if (copied) *copied = nc;
+    return MOE_OK;
+}
+
+int moe_tier_prefetch(moe_tier_t *t, const int32_t *experts, int32_t n, int32_t *copied, hipStream_t stream)
+{
+    if (!t || n < 0 || (n > 0 && !experts)) return MOE_EINVAL;
+    if (copied) *copied = 0;
+    if (tier_mirror_free(t)) return MOE_EHIP;
+    int nc = 0;
+    for (int i = 0; i < n && nc < t->P; i++) {
+        const int e = experts[i];
+        if (e < 0 || e >= t->E || t->slot_of[e] >= 0 || t->pslot_of[e] >= 0) continue;
+        const int p = t->pnext;
+        t->pnext = (t->pnext + 1) % t->P;
+        const int old = t->pexpert[p];
+        if (old >= 0) {  // the ring's oldest prefetch goes back to the host stack
+            t->pslot_of[old] = -1;
+            tier_entry(t, old);
+        }
+        for (int k = 0; k < 6; k++)
+            if (hipMemcpyAsync(t->ppool[k] + (size_t)p * t->bytes[k], t->hsrc[k] + (size_t)e * t->bytes[k],
+                               t->bytes[k], hipMemcpyHostToDevice, stream) != hipSuccess)
+                return MOE_EHIP;
+        t->pexpert[p] = e;
+        t->pslot_of[e] = p;
+        tier_entry(t, e);
+        nc++;
+    }
+    if (nc && tier_upload(t, stream)) return MOE_EHIP;
     if (copied) *copied = nc;
     return MOE_OK;
 }
@@ -559,7 +637,7 @@ int moe_tier_repin(moe_tier_t *t, int32_t *copied, hipStream_t stream)
 int moe_tier_resident(const moe_tier_t *t, int32_t *slot_of)
 {
     if (!t || !slot_of) return MOE_EINVAL;
-    for (int e = 0; e < t->E; e++) slot_of[e] = t->slot_of[e];
+    for (int e = 0; e < t->E; e++) slot_of[e] = t->slot_of[e] >= 0 ? t->slot_of[e] : t->pslot_of[e] >= 0 ? -2 : -1;
     return MOE_OK;
 }
 

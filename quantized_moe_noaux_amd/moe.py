@@ -77,6 +77,7 @@ def _load():
         "moe_tier_create": (ctypes.c_int, [P(moe_shape_t), P(moe_weights_t), i32, P(vp)]),
         "moe_tier_repin": (ctypes.c_int, [vp, P(i32), vp]),
         "moe_tier_plan": (ctypes.c_int, [P(u32), i32, i32, P(i32), P(i32), i32]),
+        "moe_tier_prefetch": (ctypes.c_int, [vp, P(i32), i32, P(i32), vp]),
         "moe_tier_resident": (ctypes.c_int, [vp, P(i32)]),
         "moe_tier_counts": (ctypes.c_int, [vp, P(u32), vp]),
         "moe_layer_forward_tiered": (ctypes.c_int, [P(moe_shape_t), vp, i32, vp, vp, vp, P(moe_weights_t), vp, vp,
@@ -274,6 +275,13 @@ class Tier:
     def repin(self, stream=None):
         n = ctypes.c_int32(0)
         _chk("moe_tier_repin", lib.moe_tier_repin(self.h, ctypes.byref(n), _stream(stream)))
+        return n.value
+
+    def prefetch(self, experts, stream=None):
+        ids = [int(e) for e in experts]
+        arr = (ctypes.c_int32 * max(1, len(ids)))(*ids)
+        n = ctypes.c_int32(0)
+        _chk("moe_tier_prefetch", lib.moe_tier_prefetch(self.h, arr, len(ids), ctypes.byref(n), _stream(stream)))
         return n.value
 
     def resident(self):

@@ -113,6 +113,43 @@ def test_tiered_top_p_and_accumulate(m, layer, dev, T):
         tier.close()
 
 
+def test_prefetch_keeps_results_and_fills_the_ring(m, layer, dev):
+    """prefetched experts are read from their prefetch slots, results unchanged;
+    the ring holds min(16, E) experts; a repin that pins one frees its slot"""
+    L, host = layer
+    E = L.wl.n_experts
+    tier = m.Tier(m.shape_of(L.wl), host, 2)
+    try:
+        y0, idx0, _ = forward(m, L, 4)
+        side = torch.cuda.Stream()
+        print("tier prefetch: the routed experts of 4 tokens", flush=True)
+        want = list(dict.fromkeys(int(e) for e in idx0.ravel()))
+        with torch.cuda.stream(side):
+            n = tier.prefetch(want, stream=side)
+        side.synchronize()
+        assert n == len(want)
+        res = tier.resident()
+        assert all(res[e] == -2 for e in want) and sum(r == -2 for r in res) == len(want)
+        yt, idx, _ = tiered(m, L, tier, 4)
+        assert torch.equal(yt, y0) and np.array_equal(idx, idx0)
+        assert tier.prefetch(want) == 0          # already there
+        print("tier prefetch: every expert, the ring keeps 16", flush=True)
+        n = tier.prefetch(list(range(E)) * 2)
+        torch.cuda.synchronize()
+        assert n == min(16, E) - len(want) or n == min(16, E)
+        assert sum(r == -2 for r in tier.resident()) == min(16, E)
+        yt, _, _ = tiered(m, L, tier, 4)
+        assert torch.equal(yt, y0)
+        tier.repin()
+        torch.cuda.synchronize()
+        res = tier.resident()
+        assert sum(r >= 0 for r in res) == 2 and sum(r == -2 for r in res) == min(16, E) - 2
+        yt, _, _ = tiered(m, L, tier, 4)
+        assert torch.equal(yt, y0)
+    finally:
+        tier.close()
+
+
 def test_tier_argument_errors(m, layer, dev):
     L, host = layer
     sh = m.shape_of(L.wl)
