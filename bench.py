@@ -945,7 +945,7 @@ def bench_tier_stack(args):
                             N = layers[l + 1]
                             moe.moe_rmsnorm(x, N["g"], 1e-6, lnrm, stream=side)
                             moe.moe_route(sh, lnrm, N["gate_w"], N["bias"], pidx, pw, rws, stream=side)
-                        ids = pidx.cpu().numpy().ravel()           # waits for the side stream
+                            ids = pidx.cpu().numpy().ravel()       # read back on the side stream, after the route
                         stats["copies"] += tiers[l + 1].prefetch(ids, stream=side)
                         evs[l + 1].record(side)
                     if lookahead and l > 0:
