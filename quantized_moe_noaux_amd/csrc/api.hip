@@ -414,7 +414,8 @@ void tier_entry(moe_tier *t, int e)
     }
 }
 
-// the table's host mirror may change (its last upload has completed)
+// the table's host mirror (and the host counts) may change: their last
+// upload has completed
 int tier_mirror_free(moe_tier *t)
 {
     return hipEventSynchronize(t->uploaded) == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -568,13 +569,15 @@ int moe_tier_repin(moe_tier_t *t, int32_t *copied, hipStream_t stream)
     if (!t) return MOE_EINVAL;
     const int E = t->E, C = t->C;
     if (copied) *copied = 0;
+    // the host counts are overwritten below: the last repin's upload of
+    // them (possibly on another stream) must have completed
+    if (tier_mirror_free(t)) return MOE_EHIP;
     if (hipMemcpyAsync(t->hcounts, t->dcounts, sizeof(uint32_t) * E, hipMemcpyDeviceToHost, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess)
         return MOE_EHIP;
     std::vector<int32_t> next(E);
     const int nc = moe_tier_plan(t->hcounts, E, C, t->slot_of.data(), next.data(), kTierSwaps);
     if (nc < 0) return -nc;
-    if (tier_mirror_free(t)) return MOE_EHIP;
     for (int e = 0; e < E; e++)  // experts leaving HBM first: their entries point to the host again
         if (t->slot_of[e] >= 0 && next[e] < 0) {
             t->expert_in[t->slot_of[e]] = -1;
@@ -597,8 +600,9 @@ int moe_tier_repin(moe_tier_t *t, int32_t *copied, hipStream_t stream)
             tier_entry(t, e);
         }
     for (int e = 0; e < E; e++) t->hcounts[e] >>= 1;  // usage decays by half per repin
-    if (tier_upload(t, stream) ||
-        hipMemcpyAsync(t->dcounts, t->hcounts, sizeof(uint32_t) * E, hipMemcpyHostToDevice, stream) != hipSuccess)
+    // the counts first: the upload event then covers both host buffers
+    if (hipMemcpyAsync(t->dcounts, t->hcounts, sizeof(uint32_t) * E, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        tier_upload(t, stream))
         return MOE_EHIP;
     if (copied) *copied = nc;
     return MOE_OK;

@@ -90,6 +90,29 @@ def test_repin_moves_the_hot_experts(m, layer):
         tier.close()
 
 
+def test_repin_on_two_streams(m, layer):
+    """Two repins back to back on different streams: the second reads the
+    heat the first one halved and uploaded, and the results stay exact."""
+    L, host = layer
+    tier = m.Tier(m.shape_of(L.wl), host, 5)
+    try:
+        print("tier parity: repins on two streams", flush=True)
+        y0, _, _ = forward(m, L, 8)
+        yt, _, _ = tiered(m, L, tier, 8)
+        assert torch.equal(yt, y0)
+        heat = np.array(tier.counts(), dtype=np.uint32)
+        assert heat.sum() > 0
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        tier.repin(stream=a)
+        tier.repin(stream=b)
+        torch.cuda.synchronize()
+        assert tier.counts() == list(heat >> 2)
+        yt, _, _ = tiered(m, L, tier, 8)
+        assert torch.equal(yt, y0)
+    finally:
+        tier.close()
+
+
 @pytest.mark.parametrize("T", [1, 5])
 def test_tiered_top_p_and_accumulate(m, layer, dev, T):
     """adaptive top-p and MOE_ACCUMULATE through the table: equal to the HBM layer"""
