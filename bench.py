@@ -199,6 +199,8 @@ def main():
     ap.add_argument("--slots", type=int, default=32, help="tier_int4: HBM slots for routed experts (of 256)")
     ap.add_argument("--repin", type=int, default=16, help="tier_int4: tokens between live repins")
     ap.add_argument("--layers", type=int, default=4, help="tier_stack_int4: layers")
+    ap.add_argument("--lookahead-ranks", type=int, default=None,
+                    help="tier_stack_int4: prefetch only the first N ranks of each predicted selection")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -877,7 +879,8 @@ def bench_tier_stack(args):
     once without and once with the router lookahead: before layer l runs,
     layer l+1's router is applied to RMSNorm(x_l) on a side stream, its
     experts are read back and prefetched into layer l+1's tier on that
-    stream, and layer l+1 waits for the prefetch.  The router bias is the
+    stream, and layer l+1 waits for the prefetch (--lookahead-ranks N: only
+    the first N ranks of each prediction are prefetched).  The router bias is the
     decode workload's N(0, 0.01), so no small hot set exists.  Each mode
     runs --warmup tokens, then --steps timed tokens (a step is one token
     through every layer, repins included)."""
@@ -933,7 +936,7 @@ def bench_tier_stack(args):
     def run(lookahead, ntok, t0, record=None):
         tiers = [moe.Tier(sh, L["host"], C) for L in layers]
         evs = [torch.cuda.Event() for _ in range(Ln)]
-        stats = {"pred": 0, "hit": 0, "sel": 0, "resident": 0, "copies": 0}
+        stats = {"pred": 0, "hit": 0, "sel": 0, "resident": 0, "copies": 0, "pre": 0, "pre_hit": 0}
         try:
             def token(t, measure):
                 x.copy_(xs[t % n_inputs])   # rotating N(0, 1) tokens
@@ -946,7 +949,8 @@ def bench_tier_stack(args):
                             moe.moe_rmsnorm(x, N["g"], 1e-6, lnrm, stream=side)
                             moe.moe_route(sh, lnrm, N["gate_w"], N["bias"], pidx, pw, rws, stream=side)
                             ids = pidx.cpu().numpy().ravel()       # read back on the side stream, after the route
-                        stats["copies"] += tiers[l + 1].prefetch(ids, stream=side)
+                        pre = ids if args.lookahead_ranks is None else ids[:args.lookahead_ranks]
+                        stats["copies"] += tiers[l + 1].prefetch(pre, stream=side)
                         evs[l + 1].record(side)
                     if lookahead and l > 0:
                         main.wait_event(evs[l])
@@ -961,12 +965,15 @@ def bench_tier_stack(args):
                         if lookahead and l > 0:
                             stats["pred"] += len(sel)
                             stats["hit"] += len(set(sel.tolist()) & set(prev_pred[l].tolist()))
+                            stats["pre"] += len(prev_pre[l])
+                            stats["pre_hit"] += len(set(sel.tolist()) & set(prev_pre[l].tolist()))
                     if lookahead and l + 1 < Ln and measure:
                         prev_pred[l + 1] = ids
+                        prev_pre[l + 1] = pre
                 if (t + 1) % R == 0:
                     for tr in tiers:
                         stats["copies"] += tr.repin()
-            prev_pred = {}
+            prev_pred, prev_pre = {}, {}
             for t in range(t0, t0 + warmup):
                 token(t, False)
             torch.cuda.synchronize()
@@ -990,8 +997,11 @@ def bench_tier_stack(args):
         (ms0, 100 * st0["resident"] / max(1, st0["sel"]), cp0))
     ms1, cp1, st1 = run(True, steps, 0)
     recall = st1["hit"] / max(1, st1["pred"])
-    log("bench: lookahead: %.2f ms per token, hits %.1f%%, lookahead recall %.1f%%, %d experts copied" %
-        (ms1, 100 * st1["resident"] / max(1, st1["sel"]), 100 * recall, cp1))
+    log("bench: lookahead: %.2f ms per token, hits %.1f%%, lookahead recall %.1f%%, %d experts copied "
+        "(prefetched ranks: %s, %.1f%% of them used)" %
+        (ms1, 100 * st1["resident"] / max(1, st1["sel"]), 100 * recall, cp1,
+         "all" if args.lookahead_ranks is None else "first %d" % args.lookahead_ranks,
+         100 * st1["pre_hit"] / max(1, st1["pre"])))
     value = 1e3 / ms1
     weight_bytes = Ln * (wl.top_k + 1) * wl.expert_bytes
     out = {
