@@ -336,7 +336,16 @@ __device__ __forceinline__ void act_from_lds(Act<WB> &A, const uint32_t *la, con
     }
 }
 
-__device__ __forceinline__ uint4 ld16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+// A 16-byte weight load, marked non-temporal: every weight byte of a GEMV
+// launch is read once, so the request asks the caches not to keep it
+// (global_load_dwordx4 ... nt), which leaves L2 to the activations, plans
+// and h rows that are read again.
+typedef unsigned v4u_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16(const uint8_t *p)
+{
+    const v4u_nt v = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // ---------------------------------------------------------------- gate / up
 constexpr int kGuLanes = 8;   // lanes per row in k_gate_up
