@@ -597,6 +597,7 @@ def bench_stack(args, wl):
         cpu = {"value": tokens / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": "%d tokens through all %d layers (RMSNorm, layer forward, residual add), expert "
                          "generation excluded" % (tokens, wl.layers), "seconds": round(spent, 2)}
+        cpu.update(host_info())
         log("bench: oracle %.3f tok/s on %d threads (%d tokens, %.1f s)" % (cpu["value"], cpu["cores"], tokens, spent))
 
     out = {
@@ -737,6 +738,7 @@ def bench_mtp(args):
                "cores": oracle.lib().oracle_num_threads(), "kind": "oracle",
                "sample": "%d acceptance steps of the rotating inputs; the verify layer itself is in the "
                          "decode_int4 line's baseline" % reps}
+        cpu.update(host_info())
     out = {
         "metric": "MTP verify tokens/s (one int4 MoE layer + acceptance, synthetic drafts)",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
@@ -1026,36 +1028,73 @@ def bench_tier_stack(args):
     print(json.dumps(out), flush=True)
 
 
+def host_info():
+    """The host the oracle ran on: CPU model, the CPUs this process may use,
+    and the OpenMP thread setting it inherited."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"cpu_model": model, "nproc": nproc, "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(args, wl, host, xs, n_inputs):
     """The oracle, as it stands, on a bounded sample of the same inputs:
     whole inputs for decode / verify (cycled until the time budget is spent),
     groups of 4 tokens of the first input for prefill (every token's output
-    depends only on its own row).  Expert generation is excluded."""
+    depends only on its own row).  Expert generation is excluded.  For the
+    small batches (decode, verify) a second, shorter sample runs the oracle
+    on one thread."""
     import oracle
     osh = oracle.shape_of(wl)
     per = 4 if wl.T > 64 else wl.T
-    done, spent, tokens = 0, 0.0, 0
-    t_start = time.perf_counter()
-    while spent < args.cpu_seconds and time.perf_counter() - t_start < 4 * args.cpu_seconds:
-        if wl.T > 64:
-            x = xs[0, (done * per) % wl.T:(done * per) % wl.T + per].cpu().numpy()
-        else:
-            x = xs[done % n_inputs].cpu().numpy()
-        ridx, _ = oracle.route(osh, x, host.gate_w, host.bias)
-        experts = oracle.layer_experts(host, ridx)       # generated outside the timing
-        c0 = time.perf_counter()
-        oracle.layer_forward(osh, x, host.gate_w, host.bias, experts, host.shared)
-        spent += time.perf_counter() - c0
-        tokens += x.shape[0]
-        done += 1
-        host._experts = {k: v for k, v in host._experts.items() if k == wl.n_experts}
-    sample = ("%d forwards of %d-token slices of one %d-token %s input" % (done, per, wl.T, wl.name)
-              if wl.T > 64 else
-              "%d forwards cycling the %d rotating %s inputs (T=%d each)" % (done, n_inputs, wl.name, wl.T))
-    cpu = {"value": tokens / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-           "sample": sample + ", full layer forward (router, experts, combine), expert generation excluded",
+
+    def sample(budget, first=0):
+        done, spent, tokens = 0, 0.0, 0
+        t_start = time.perf_counter()
+        while done == 0 or (spent < budget and time.perf_counter() - t_start < 4 * budget):
+            j = first + done
+            if wl.T > 64:
+                x = xs[0, (j * per) % wl.T:(j * per) % wl.T + per].cpu().numpy()
+            else:
+                x = xs[j % n_inputs].cpu().numpy()
+            ridx, _ = oracle.route(osh, x, host.gate_w, host.bias)
+            experts = oracle.layer_experts(host, ridx)       # generated outside the timing
+            c0 = time.perf_counter()
+            oracle.layer_forward(osh, x, host.gate_w, host.bias, experts, host.shared)
+            spent += time.perf_counter() - c0
+            tokens += x.shape[0]
+            done += 1
+            host._experts = {k: v for k, v in host._experts.items() if k == wl.n_experts}
+        return tokens, spent, done
+
+    threads = oracle.num_threads()
+    tokens, spent, done = sample(args.cpu_seconds)
+    sample_desc = ("%d forwards of %d-token slices of one %d-token %s input" % (done, per, wl.T, wl.name)
+                   if wl.T > 64 else
+                   "%d forwards cycling the %d rotating %s inputs (T=%d each)" % (done, n_inputs, wl.name, wl.T))
+    cpu = {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": sample_desc + ", full layer forward (router, experts, combine), expert generation excluded",
            "seconds": round(spent, 2)}
-    log("bench: oracle %.3f tok/s on %d threads (%d forwards, %.1f s)" % (cpu["value"], cpu["cores"], done, spent))
+    cpu.update(host_info())
+    log("bench: oracle %.3f tok/s on %d threads (%d forwards, %.1f s)" % (cpu["value"], threads, done, spent))
+    if wl.T <= 64:
+        oracle.set_num_threads(1)
+        try:
+            t1, s1, d1 = sample(args.cpu_seconds / 3, first=done)
+        finally:
+            oracle.set_num_threads(threads)
+        cpu["single_thread"] = {"value": t1 / s1, "unit": "tokens/s", "forwards": d1, "seconds": round(s1, 2)}
+        log("bench: oracle %.3f tok/s on 1 thread (%d forwards, %.1f s)" % (t1 / s1, d1, s1))
     return cpu
 
 

@@ -19,7 +19,15 @@
  *    moe_shape_t / moe_weights_t structs themselves live in host memory.
  *  - The caller owns every buffer.  The library never allocates or frees,
  *    never synchronises, and keeps no global state; calls are thread-safe
- *    as long as concurrent calls use distinct workspaces and outputs.
+ *    as long as concurrent calls use distinct workspaces and outputs.  The
+ *    one exception is the expert tier below: moe_tier_create allocates the
+ *    tier's device memory (moe_tier_destroy frees it), and moe_tier_repin
+ *    and moe_tier_counts synchronise the stream they are given.
+ *  - Workspaces ("ws") are device scratch of at least the matching
+ *    *_workspace_bytes size, 256-byte aligned.  They need no initial
+ *    contents: a call writes every workspace byte it reads before reading
+ *    it, and a later call depends on nothing left in it (except a MOE_STAGE
+ *    call, which reads what the earlier stages of its sequence wrote).
  *  - Work is enqueued on `stream` (NULL = the default stream) and the call
  *    returns at once.  Inputs are never written.  Outputs are overwritten,
  *    except with MOE_ACCUMULATE, which adds into y.  y must not alias x.

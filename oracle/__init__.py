@@ -45,12 +45,16 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        # ORACLE_LIB names a sanitizer build of oracle.c to load in place of LIB
+        path = os.environ.get("ORACLE_LIB") or LIB
+        if path == LIB and not os.path.exists(LIB):
             build()
-        L = ctypes.CDLL(LIB)
+        L = ctypes.CDLL(path)
         vp, i32, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         L.oracle_num_threads.restype = i32
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [i32]
         L.oracle_code.restype = i32
         L.oracle_code.argtypes = [i32, vp, i32]
         L.oracle_route.restype = i32
@@ -98,6 +102,10 @@ def _expert_struct(ex):
 
 def num_threads():
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n):
+    lib().oracle_set_num_threads(int(n))
 
 
 def code(wbits, row, j):

@@ -29,6 +29,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* sets the thread count of later OpenMP regions (timing only: every result
+ * is the same for any count, each output's arithmetic order being fixed) */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_code(int wbits, const uint8_t *row, int j)
 {
     if (wbits == 8)

@@ -51,6 +51,7 @@ typedef struct {
  * low nibble of byte m; int2: element 4m+i sits at bits 2i..2i+1) */
 int oracle_code(int wbits, const uint8_t *row, int j);
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 int oracle_route(const oracle_shape *sh, const float *x, int T, const float *gate_w,
                  const float *bias, int32_t *idx, float *w, double *margins);

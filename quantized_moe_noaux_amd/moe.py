@@ -50,9 +50,13 @@ moe_layer_t._fields_ = [("gate_w", ctypes.c_void_p), ("bias", ctypes.c_void_p), 
 
 
 def _load():
-    if not os.path.exists(_build.LIB):
-        raise ImportError("libmoe.so is not built (%s); run __graft_entry__.build()" % _build.LIB)
-    L = ctypes.CDLL(_build.LIB)
+    # MOE_LIB names another build of the same sources to load in place of the
+    # in-tree library (the sanitizer build of the host code, for CPU-only tests)
+    path = os.environ.get("MOE_LIB") or _build.LIB
+    if not os.path.exists(path):
+        raise ImportError("libmoe.so is not built (%s); run __graft_entry__.build()" % path)
+    L = ctypes.CDLL(path)
+    L.path = path
     vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
     P = ctypes.POINTER
     sig = {
@@ -138,9 +142,9 @@ def weights(w):
 
 
 def workspace(nbytes, device="cuda"):
-    """A zero-filled device buffer for the *_workspace_bytes sizes (torch keeps
-    256-byte alignment; moe_layer_forward needs zeros before the first use)."""
-    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A device buffer for the *_workspace_bytes sizes (torch's allocations
+    are 256-byte aligned; the calls need no initial contents)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def moe_route_workspace_bytes(sh, T):

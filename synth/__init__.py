@@ -101,9 +101,11 @@ _host = None
 def _host_lib():
     global _host
     if _host is None:
-        if not os.path.exists(_build.HOST_LIB):
+        # SYNTH_HOST_LIB names a sanitizer build of synth.c to load in place of HOST_LIB
+        path = os.environ.get("SYNTH_HOST_LIB") or _build.HOST_LIB
+        if path == _build.HOST_LIB and not os.path.exists(path):
             _build.build_host()
-        lib = ctypes.CDLL(_build.HOST_LIB)
+        lib = ctypes.CDLL(path)
         u64 = ctypes.c_uint64
         lib.synth_key.restype = u64
         lib.synth_key.argtypes = [u64, u64]

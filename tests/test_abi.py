@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
 
 
 def test_library_exports_every_declared_symbol(m):
-    lib = ctypes.CDLL(m._build.LIB)
+    lib = ctypes.CDLL(m.lib.path)
     missing = [f for f in header_functions() if not hasattr(lib, f)]
     assert not missing, missing
 

@@ -3,11 +3,12 @@ through the C ABI.
 
 Kept-draft counts and emitted tokens are integers decided in fp64 on both
 sides; the GPU sums its softmax normalisers and draw masses per 4096-token
-chunk in a fixed order, the oracle sequentially, so the two agree except
-where a sampled decision lies within rounding of its boundary.  The oracle
-reports each sequence's smallest relative decision margin; sequences with
-a margin under 1e-10 (none at these seeds) are left out of the comparison
-and counted.  Greedy decisions compare fp32 logits and are exact.
+chunk in a fixed order, the oracle sequentially, so the two could differ
+only where a sampled decision lies within rounding of its boundary.  The
+oracle reports each sequence's smallest relative decision margin: at the
+seeds used here every margin exceeds 1e-10 (asserted), far above the
+~1e-15 relative rounding of either side, so every sequence must match the
+oracle exactly.  Greedy decisions compare fp32 logits and are exact.
 """
 import numpy as np
 import pytest
@@ -48,11 +49,11 @@ def check(m, dev, draft, p, q, tau, u, what=""):
           flush=True)
     n, nx = run(m, dev, draft, p, q, tau, u)
     n_ref, nx_ref, mg = oracle.mtp_accept(draft, p, q, tau, u)
-    ok = mg > 1e-10 if tau > 0 else np.ones_like(mg, bool)
-    assert ok.mean() >= 0.9, "too many decisions within rounding of their boundary"
-    assert np.array_equal(n[ok], n_ref[ok]), (n, n_ref)
-    assert np.array_equal(nx[ok], nx_ref[ok]), (nx, nx_ref)
-    assert ((0 <= n) & (n <= p.shape[1] - 1)).all() and ((0 <= nx) & (nx < p.shape[2])).all()
+    if tau > 0:
+        low = np.flatnonzero(mg <= 1e-10)
+        assert low.size == 0, "sequences %s decide within 1e-10 of a boundary (margins %s)" % (low, mg[low])
+    assert np.array_equal(n, n_ref), (n, n_ref)
+    assert np.array_equal(nx, nx_ref), (nx, nx_ref)
     return n, nx
 
 

@@ -2,10 +2,12 @@
 and int8 MFMA grouped GEMMs) against the CPU oracle, through the C ABI.
 
 Expert indices are bit-exact; float outputs are held to max-abs error
-<= 1e-3 x max|ref|.  At the full prefill size (2048 tokens) the routing of
-every token is compared, and the layer output on a sample of tokens: each
-token's output depends only on its own row, so the oracle runs those rows
-alone."""
+<= 1e-3 x max|ref|.  At the full prefill size (2048 tokens, every tile of
+every expert the skewed routing loads) the routing and the whole [2048][6144]
+output are compared with the oracle element by element, and with the GEMV
+path.  At the decode shape, batches of 3, 8, 16 and 64 independent tokens
+run on both paths and against the oracle (the two paths are the forced
+equivalence of the batch-union GEMV and the grouped GEMM)."""
 import numpy as np
 import pytest
 import torch
@@ -139,17 +141,47 @@ def test_prefill_routing_full(dev, m, prefill):
     assert np.bincount(idx.ravel(), minlength=256).max() > 256
 
 
-def test_prefill_sampled_tokens(dev, m, prefill):
+@pytest.mark.timeout(900)
+def test_prefill_full_output(dev, m, prefill):
+    """Every one of the 2048 tokens against the oracle (about a minute of
+    oracle time on 16 host threads), and against the GEMV path."""
     L = prefill
     T = L.wl.T
-    print("prefill output: T=%d, sampled rows" % T, flush=True)
-    y, idx, _ = forward(m, L, m.MOE_PATH_AUTO)
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, T - 1], rng.choice(T, 7, replace=False)]))
-    y_ref, idx_ref, _ = reference(L, rows)
-    assert np.array_equal(idx[rows], idx_ref)
-    rel = assert_close(y.cpu().numpy()[rows], y_ref)
-    print("prefill sampled rows: max rel err %.3g" % rel)
+    print("prefill output: T=%d, all rows, grouped path" % T, flush=True)
+    y, idx, w = forward(m, L, m.MOE_PATH_AUTO)
+    yv, idxv, wv = forward(m, L, m.MOE_PATH_GEMV)
+    assert np.array_equal(idx, idxv) and np.array_equal(w, wv)
+    y = y.cpu().numpy()
+    print("prefill output: oracle on %d tokens (%d threads)" % (T, oracle.num_threads()), flush=True)
+    y_ref, idx_ref, w_ref = reference(L, np.arange(T))
+    assert np.array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=1e-6)
+    rel = assert_close(y, y_ref)
+    print("prefill full output: max err %.3g of max|ref|" % rel)
+    assert_close(yv.cpu().numpy(), y_ref, what="GEMV path at T=2048")
+    # rows of every tile: the busiest experts span many 64-row tiles
+    counts = np.bincount(idx.ravel(), minlength=L.wl.n_experts)
+    assert counts.max() > 4 * 64
+
+
+@pytest.fixture(scope="module")
+def decode_batch(dev):
+    return DevLayer(synth.workload("decode_int4"), dev, T=64)
+
+
+@pytest.mark.parametrize("T", [3, 8, 16, 64])
+def test_decode_shape_batches_both_paths(dev, m, decode_batch, T):
+    L = decode_batch
+    print("decode shape batch: T=%d, GEMV and grouped" % T, flush=True)
+    yg, ig, wg = forward(m, L, m.MOE_PATH_GROUPED, T)
+    yv, iv, wv = forward(m, L, m.MOE_PATH_GEMV, T)
+    assert np.array_equal(ig, iv) and np.array_equal(wg, wv)
+    y_ref, idx_ref, w_ref = reference(L, np.arange(T))
+    assert np.array_equal(ig, idx_ref)
+    np.testing.assert_allclose(wg, w_ref, rtol=1e-6)
+    assert_close(yg.cpu().numpy(), y_ref, what="grouped")
+    assert_close(yv.cpu().numpy(), y_ref, what="gemv")
+    assert_close(yg.cpu().numpy(), yv.cpu().numpy().astype(np.float64), what="grouped vs gemv")
 
 
 # ---------------------------------------------------------------- adaptive expert top-p
