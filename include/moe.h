@@ -91,7 +91,9 @@ enum {
     MOE_EINVAL = 1,        /* null pointer, negative size, inconsistent shape */
     MOE_EUNSUPPORTED = 2,  /* valid but outside what the kernels implement */
     MOE_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes */
-    MOE_EHIP = 4           /* a launch failed (hipGetLastError) */
+    MOE_EHIP = 4,          /* a launch failed (hipGetLastError) */
+    MOE_ESCRATCH = 5       /* the call needs more than the fixed scratch of
+                              moe_layer_forward_noalloc */
 };
 const char *moe_strerror(int code);
 
@@ -184,6 +186,29 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
                       float *y, int32_t *idx_out, float *w_out, uint32_t flags,
                       void *ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags);
+
+/* moe_layer_forward_noalloc -- moe_layer_forward without a workspace
+ * argument, for callers that cannot allocate device memory: code under
+ * stream capture, tight serving loops, hosts that forbid allocation on the
+ * hot path.  It calls no allocator.  Its workspace is a fixed device buffer
+ * of MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends; the first call on a device looks up that
+ * device's copy (a one-time symbol lookup, no allocation).
+ * Arguments, results and errors are those of moe_layer_forward on the same
+ * inputs (bit for bit), plus MOE_ESCRATCH, returned before anything is
+ * launched, when moe_workspace_bytes(shape, T, flags) exceeds the buffer:
+ * at hidden 6144 / intermediate 2048 / 256 experts / top-8, the GEMV path
+ * for up to 8 tokens needs under 1 MB, the grouped path about 0.3 MB per
+ * token, so batches above about 100 tokens take moe_layer_forward.
+ * All calls on one GPU share its buffer: calls that overlap in time on one
+ * GPU (different streams, or threads without ordering) race; calls ordered
+ * on one stream do not.  Nothing in the buffer needs clearing between
+ * calls. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_layer_forward_noalloc(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w,
+                              const float *bias, const moe_weights_t *routed, const moe_weights_t *shared,
+                              float *y, int32_t *idx_out, float *w_out, uint32_t flags, hipStream_t stream);
+
 /* number of stages moe_layer_forward runs for these arguments (the n of
  * MOE_STAGE(n) runs from 0 to this minus 1); < 0 on bad arguments.
  * GEMV path: router + quantiser (one launch for T <= 8, else two), then

@@ -6,7 +6,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "gemv.hip", "grouped.hip", "misc.hip", "accept.hip"]
+SOURCES = ["api.hip", "route.hip", "gemv.hip", "grouped.hip", "misc.hip", "accept.hip", "noalloc.hip"]
 
 HIPCC = "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -139,6 +139,7 @@ const char *moe_strerror(int code)
     case MOE_EUNSUPPORTED: return "unsupported shape or parameter";
     case MOE_EWORKSPACE: return "workspace too small";
     case MOE_EHIP: return "HIP launch failed";
+    case MOE_ESCRATCH: return "call exceeds the fixed scratch buffer of moe_layer_forward_noalloc";
     default: return "unknown error";
     }
 }

@@ -14,7 +14,8 @@ import torch
 
 from . import _build
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = range(6)
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GROUPED, MOE_ACCUMULATE = 0, 1, 2, 4
 
 
@@ -69,6 +70,8 @@ def _load():
         "moe_layer_forward": (ctypes.c_int, [P(moe_shape_t), vp, i32, vp, vp, P(moe_weights_t),
                                              P(moe_weights_t), vp, vp, vp, u32, vp, sz, vp]),
         "moe_workspace_bytes": (sz, [P(moe_shape_t), i32, u32]),
+        "moe_layer_forward_noalloc": (ctypes.c_int, [P(moe_shape_t), vp, i32, vp, vp, P(moe_weights_t),
+                                                     P(moe_weights_t), vp, vp, vp, u32, vp]),
         "moe_layer_stage_count": (ctypes.c_int, [P(moe_shape_t), i32, u32]),
         "moe_rmsnorm": (ctypes.c_int, [vp, vp, ctypes.c_double, i32, i32, vp, vp]),
         "moe_permute": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
@@ -194,6 +197,18 @@ def moe_layer_forward(sh, x, gate_w, bias, routed, shared, y, ws, idx_out=None, 
         _ptr(bias, torch.float32), ctypes.byref(rw), ctypes.byref(sw) if sw is not None else None,
         _ptr(y, torch.float32), _ptr(idx_out, torch.int32), _ptr(w_out, torch.float32), flags,
         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_layer_forward_noalloc(sh, x, gate_w, bias, routed, shared, y, idx_out=None, w_out=None, flags=0,
+                              stream=None):
+    """moe_layer_forward on the library's fixed scratch buffer (no workspace)."""
+    rw = weights(routed)
+    sw = weights(shared) if shared is not None else None
+    _chk("moe_layer_forward_noalloc", lib.moe_layer_forward_noalloc(
+        ctypes.byref(sh), _ptr(x, torch.float32), x.shape[0], _ptr(gate_w, torch.float32),
+        _ptr(bias, torch.float32), ctypes.byref(rw), ctypes.byref(sw) if sw is not None else None,
+        _ptr(y, torch.float32), _ptr(idx_out, torch.int32), _ptr(w_out, torch.float32), flags,
+        _stream(stream)))
 
 
 def moe_rmsnorm(x, g, eps, out, stream=None):
