@@ -103,10 +103,8 @@ int layer_grouped(const moe_shape_t &s, const float *x, int T, const float *gate
     if (shared) a.shared = *shared;
     a.xq = static_cast<const int8_t *>(at(L.xq));
     a.xd = static_cast<const float *>(at(L.xd));
-    a.xs = static_cast<const float *>(at(L.xs));
     a.qh = static_cast<int8_t *>(at(L.qh));
     a.dh = static_cast<float *>(at(L.dh));
-    a.zh = static_cast<float *>(at(L.zh));
     a.yrows = static_cast<float *>(at(L.y));
     a.y = y;
     a.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
@@ -114,8 +112,7 @@ int layer_grouped(const moe_shape_t &s, const float *x, int T, const float *gate
     const int ksplit = router_ksplit(T, H, E);
     if (run(0) && launch_router_logits_mfma(x, T, H, gate_w, E, ksplit, logits, st)) return MOE_EHIP;
     if (run(1) && launch_topk(rc, logits, ksplit, bias, T, idx, w, st)) return MOE_EHIP;
-    if (run(2) && launch_gg_quant(x, T, H, const_cast<int8_t *>(a.xq), const_cast<float *>(a.xd),
-                                  const_cast<float *>(a.xs), st))
+    if (run(2) && launch_gg_quant(x, T, H, s.wbits, const_cast<int8_t *>(a.xq), const_cast<float *>(a.xd), st))
         return MOE_EHIP;
     if (run(3) && launch_permute(idx, T, k, E, const_cast<int32_t *>(a.perm), static_cast<int32_t *>(at(L.off)),
                                  const_cast<int32_t *>(a.inv), static_cast<int32_t *>(at(L.pscr)),

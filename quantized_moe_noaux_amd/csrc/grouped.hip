@@ -8,28 +8,40 @@
 //
 // After routing, the T*k (token, slot) assignments are sorted by expert
 // (stable counting sort, moe_permute's kernels) into "rows", followed by T
-// rows for the shared expert.  Rows are cut into tiles of kGgTN rows that
-// never straddle two experts; every tile is a small GEMM against its
-// expert's weights:
-//   k_gg_gate_up  one workgroup per (tile, 64 intermediate channels): the
-//                 int4/int2 codes are expanded to int8 in LDS, the tile's
-//                 activation rows are gathered into LDS, and
-//                 v_mfma_i32_32x32x32_i8 gives the exact int32 dot of every
-//                 (channel, row, 32-block); each is scaled by its activation
-//                 block scale and summed in fp32.  Then g, u -> h = silu(g) u
-//                 -> int8 h in blocks of 32 channels.
-//   k_gg_down     one workgroup per (tile, 128 hidden channels): the same
-//                 over the int8 h rows; the result is scaled by the row's
-//                 combine weight and written to the row's output slot.
+// rows for the shared expert.  Rows are cut into tiles of kGgTN = 128 rows
+// that never straddle two experts; every tile is a small GEMM against its
+// expert's weights, on v_mfma_i32_32x32x32_i8: one MFMA is exactly one
+// activation block of 32, so its int32 result is that block's exact integer
+// dot for 32 x 32 (channel, row) pairs, scaled by the row's block scale and
+// summed in fp32.
+//   k_gg_gate_up  workgroup = (tile, 128 intermediate channels): 256 weight
+//                 rows (the channels' gate and up rows) against the tile's
+//                 128 activation rows; then g, u -> h = silu(g) u -> int8 h
+//                 in blocks of 32 channels.
+//   k_gg_down     workgroup = (tile, 256 hidden channels), over the int8 h
+//                 rows; the result is scaled by the row's combine weight and
+//                 written to the row's output slot.
 //   k_gg_combine  out[t] = t's k routed slots in slot order, then the shared
 //                 row.
 // No float atomics anywhere: results are run-to-run identical.
 //
-// Weight codes are expanded in offset form (c + 8 for int4, c + 2 for int2,
-// both non-negative), so an MFMA block dot is sum (c + o) q = sum c q + o S
-// with S the block's activation code sum.  The offset term depends on the
-// activation row only, so it is removed once per row at the end:
-// acc - o * sum_b d_b S_b, with that sum formed where the row is quantised.
+// Code forms.  A packed weight code is masked in place into the top bits of
+// its byte, where the byte reads as the signed value 16c (int4) or 64c
+// (int2): two's-complement codes keep their sign there, so the MFMA gives
+// 16 (or 64) times the exact block dot, |16 I| <= 520192, and the power of
+// two is folded into the row scale.  The two halves of a wave's MFMA operand
+// (lanes 0-31 and 32-63 hold K = 0-15 and 16-31 of the block) take
+// different fields of the same packed bytes (int4: lanes 0-31 the low
+// nibbles, lanes 32-63 the high ones), so the activation codes of every
+// block are stored once in that code order (gg_act_src below): by the row
+// quantiser for x, by the gate/up epilogue for h.
+//
+// Work order.  The 1-D grid is dealt round-robin over the 8 XCDs (each with
+// its own L2).  XCD x takes the channel groups [x cpx, (x+1) cpx) of every
+// tile, and its workgroups walk tile by tile with a tile's channel groups
+// back to back: a tile's activation rows are fetched once per XCD, and the
+// tiles of one expert, running at the same time, share each weight slice in
+// that XCD's L2.
 #include "moe_dev.h"
 #include "moe_internal.h"
 
@@ -37,11 +49,11 @@ namespace moe {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kGgKS = 64;           // K per pipeline step (two 32-blocks)
-constexpr int kGgRow = kGgKS + 16;  // LDS bytes per staged row (padding: conflict-free 16-byte reads)
-constexpr int kGgWRows = 128;       // weight rows staged per workgroup
-constexpr int kGgThreads = 256;
+constexpr int kGgThreads = 1024;
+constexpr int kGgWRows = 256;  // weight rows staged per workgroup
 
 GgWs gg_ws(const moe_shape_t &s, int T)
 {
@@ -54,7 +66,6 @@ GgWs gg_ws(const moe_shape_t &s, int T)
     w.w = o;      o = align256(o + sizeof(float) * Tk);
     w.xq = o;     o = align256(o + (size_t)T * H);
     w.xd = o;     o = align256(o + sizeof(float) * (size_t)T * (H / 32));
-    w.xs = o;     o = align256(o + sizeof(float) * (size_t)T);
     w.perm = o;   o = align256(o + sizeof(int32_t) * Tk);
     w.off = o;    o = align256(o + sizeof(int32_t) * (E + 1));
     w.inv = o;    o = align256(o + sizeof(int32_t) * Tk);
@@ -62,230 +73,292 @@ GgWs gg_ws(const moe_shape_t &s, int T)
     w.tiles = o;  o = align256(o + sizeof(int4) * (size_t)(gg_max_tiles(s, T) + 1));
     w.qh = o;     o = align256(o + R * I);
     w.dh = o;     o = align256(o + sizeof(float) * R * (I / 32));
-    w.zh = o;     o = align256(o + sizeof(float) * R * (I / 32));
     w.y = o;      o = align256(o + sizeof(float) * R * H);
     w.total = o;
     return w;
 }
 
+// ---------------------------------------------------------------- code order
+// Natural index (within its block of 32) of the activation code stored at
+// position p of the block, for weights of WB bits:
+//   int8: p;
+//   int4: lanes 0-31 take the low nibbles of the block's 16 bytes (codes
+//         0, 2, .., 30), lanes 32-63 the high ones (1, 3, .., 31);
+//   int2: lane half h takes fields 2h and 2h+1 of the block's 8 bytes; its
+//         dword o = 2j + f is field 2h + f of weight dword j, whose byte m
+//         holds code 16j + 4m + 2h + f.
+template <int WB> __host__ __device__ __forceinline__ int gg_act_src(int p)
+{
+    if constexpr (WB == 4) {
+        return p < 16 ? 2 * p : 2 * (p - 16) + 1;
+    } else if constexpr (WB == 2) {
+        const int h = p >> 4, o = (p >> 2) & 3, m = p & 3;
+        return 16 * (o >> 1) + 4 * m + 2 * h + (o & 1);
+    } else {
+        return p;
+    }
+}
+
+// Four bytes of a block in natural order (src[0..31]) at stored positions
+// 4o .. 4o+3, packed little-endian into a dword.
+template <int WB> __device__ __forceinline__ uint32_t gg_pack_dword(const uint8_t *src, int o)
+{
+    uint32_t v = 0;
+#pragma unroll
+    for (int m = 0; m < 4; m++) v |= (uint32_t)src[gg_act_src<WB>(4 * o + m)] << (8 * m);
+    return v;
+}
+
 // ---------------------------------------------------------------- row quantiser
 // One workgroup per row of D values: Q8_0-style blocks (8 lanes per block,
-// quant_block8) and xs[row] = sum_b d_b * S_b in fp64 (S_b = the block's
-// code sum), the offset correction of the grouped GEMMs.
+// quant_block8), the codes gathered in LDS in natural order, then written
+// out in the weights' code order.
+template <int WB>
 __global__ __launch_bounds__(256) void k_gg_quant(const float *__restrict__ x, int D, int8_t *__restrict__ q,
-                                                  float *__restrict__ d, float *__restrict__ xs)
+                                                  float *__restrict__ d)
 {
-    __shared__ double part[32];
+    extern __shared__ __align__(16) uint8_t qn[];  // D bytes
     const int row = blockIdx.x, tid = threadIdx.x, bs = tid >> 3, sub = tid & 7;
     const int nb = D / 32;
     const float *xr = x + (size_t)row * D;
-    double acc = 0.0;
     for (int b0 = 0; b0 < nb; b0 += 32) {
         const int b = b0 + bs;
         const bool live = b < nb;
-        const float4 v = live ? reinterpret_cast<const float4 *>(xr + 32 * b)[sub] : make_float4(0, 0, 0, 0);
+        const float4 v = reinterpret_cast<const float4 *>(xr + 32 * min(b, nb - 1))[sub];
         float db;
         const uint32_t packed = quant_block8(v, db);
-        int s = sdot4(packed, 0x01010101u, 0);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
         if (live) {
-            reinterpret_cast<uint32_t *>(q + (size_t)row * D + 32 * b)[sub] = packed;
-            if (sub == 0) {
-                d[(size_t)row * nb + b] = db;
-                acc += (double)db * (double)s;
-            }
+            reinterpret_cast<uint32_t *>(qn + 32 * b)[sub] = packed;
+            if (sub == 0) d[(size_t)row * nb + b] = db;
         }
     }
-    if (sub == 0) part[bs] = acc;
     __syncthreads();
-    if (tid == 0) {
-        double s = 0.0;
-        for (int i = 0; i < 32; i++) s += part[i];
-        xs[row] = (float)s;
-    }
+    uint32_t *qo = reinterpret_cast<uint32_t *>(q + (size_t)row * D);
+    for (int i = tid; i < D / 4; i += 256) qo[i] = gg_pack_dword<WB>(qn + 32 * (i >> 3), i & 7);
 }
 
-int launch_gg_quant(const float *x, int T, int D, int8_t *q, float *d, float *xs, hipStream_t st)
+int launch_gg_quant(const float *x, int T, int D, int wbits, int8_t *q, float *d, hipStream_t st)
 {
-    k_gg_quant<<<T, 256, 0, st>>>(x, D, q, d, xs);
+    const size_t lds = (size_t)D;
+    if (wbits == 4) k_gg_quant<4><<<T, 256, lds, st>>>(x, D, q, d);
+    else if (wbits == 8) k_gg_quant<8><<<T, 256, lds, st>>>(x, D, q, d);
+    else k_gg_quant<2><<<T, 256, lds, st>>>(x, D, q, d);
     return (int)hipGetLastError();
 }
 
-// ---------------------------------------------------------------- staging
-// One pipeline step moves K = 64 of kGgWRows weight rows and of kGgTN
-// activation rows into LDS as int8, both sides in the same code order within
-// each 16-byte group (the expansion of a packed dword interleaves codes).
-//
-// int4: a dword holds codes 8j..8j+7 (even code in the low nibble).  Its low
-//   nibbles become one dword (codes 0,2,4,6) and its high nibbles the next
-//   (1,3,5,7).
-// int2: a dword holds codes 16j..16j+15, code 4m+i at byte m, bits 2i.  Field
-//   i of the four bytes becomes dword i (codes i, 4+i, 8+i, 12+i).
-// int8: natural order.
-template <int WB> struct GgW;
+// ---------------------------------------------------------------- tiling
+// A workgroup of 512 threads (8 waves) owns 128 activation rows (one tile)
+// and 256 weight rows.  Per pipeline step it stages K = 128 codes of both in
+// LDS as int8 MFMA operands: the activation rows as stored (code order),
+// the weight rows expanded from their packed codes to the 16c / 64c form
+// (int4 / int2; int8 as stored), so that a wave reads every MFMA operand
+// with one ds_read_b128 and no further VALU work.
+constexpr int kGgKS = 128;               // K codes per step
+constexpr int kGgNBS = kGgKS / 32;       // activation blocks per step
+constexpr int kGgRowBytes = kGgKS;       // LDS bytes of a staged row per step (int8 operands)
+constexpr int kGgCPR = kGgRowBytes / 16; // 16-byte chunks per staged row
 
-template <> struct GgW<4> {
-    static constexpr int kOff = 8;
-    uint4 r;  // 32 codes: one block of one row
-    __device__ __forceinline__ void load(const uint8_t *row, int k0, int half)
-    {
-        r = *reinterpret_cast<const uint4 *>(row + k0 / 2 + 16 * half);
-    }
-    __device__ __forceinline__ void store(uint8_t *lds_row, int half) const
-    {
-        const uint32_t w0 = r.x ^ 0x88888888u, w1 = r.y ^ 0x88888888u;
-        const uint32_t w2 = r.z ^ 0x88888888u, w3 = r.w ^ 0x88888888u;
-        uint4 o0, o1;
-        o0.x = w0 & 0x0F0F0F0Fu; o0.y = (w0 >> 4) & 0x0F0F0F0Fu;
-        o0.z = w1 & 0x0F0F0F0Fu; o0.w = (w1 >> 4) & 0x0F0F0F0Fu;
-        o1.x = w2 & 0x0F0F0F0Fu; o1.y = (w2 >> 4) & 0x0F0F0F0Fu;
-        o1.z = w3 & 0x0F0F0F0Fu; o1.w = (w3 >> 4) & 0x0F0F0F0Fu;
-        uint4 *p = reinterpret_cast<uint4 *>(lds_row + 32 * half);
-        p[0] = o0;
-        p[1] = o1;
-    }
+template <int WB> struct GgCfg {
+    static constexpr int PRB = kGgKS * WB / 8;                 // packed weight bytes per row per step
+    static constexpr int PCR = PRB / 16;                       // packed 16-byte chunks per weight row per step
+    static constexpr int WCH = kGgWRows * PCR;                 // packed weight chunks per step
+    static constexpr int WLD = (WCH + kGgThreads - 1) / kGgThreads;  // per thread (the last one partial for int2)
+    static constexpr float kInv = WB == 4 ? 1.0f / 16 : WB == 2 ? 1.0f / 64 : 1.0f;  // code form scale
 };
+static_assert(kGgTN * kGgCPR == kGgThreads, "one activation chunk per thread per step");
+static_assert(kGgTN * kGgNBS <= kGgThreads, "one activation scale per thread per step");
 
-template <> struct GgW<8> {
-    static constexpr int kOff = 0;
-    v4i r0, r1;
-    __device__ __forceinline__ void load(const uint8_t *row, int k0, int half)
-    {
-        const v4i *p = reinterpret_cast<const v4i *>(row + k0 + 32 * half);
-        r0 = p[0];
-        r1 = p[1];
-    }
-    __device__ __forceinline__ void store(uint8_t *lds_row, int half) const
-    {
-        v4i *p = reinterpret_cast<v4i *>(lds_row + 32 * half);
-        p[0] = r0;
-        p[1] = r1;
-    }
-};
+// Chunk c of staged row r.  Rows are padded to 144 bytes (36 banks): the 16
+// lanes a ds_read_b128 serves at once read rows r .. r+15 at one chunk, and
+// these start on 16 distinct 4-bank groups; a fragment's address is one
+// base per row plus an immediate offset per block.
+constexpr int kGgRowStride = kGgRowBytes + 16;
+__device__ __forceinline__ int ldsoff(int r, int c) { return r * kGgRowStride + 16 * c; }
 
-template <> struct GgW<2> {
-    static constexpr int kOff = 2;
-    uint2 r;  // 32 codes: one block of one row
-    __device__ __forceinline__ void load(const uint8_t *row, int k0, int half)
-    {
-        r = *reinterpret_cast<const uint2 *>(row + k0 / 4 + 8 * half);
-    }
-    __device__ __forceinline__ void store(uint8_t *lds_row, int half) const
-    {
-        const uint32_t a = r.x ^ 0xAAAAAAAAu, b = r.y ^ 0xAAAAAAAAu;
-        uint4 o0, o1;
-        o0.x = a & 0x03030303u; o0.y = (a >> 2) & 0x03030303u;
-        o0.z = (a >> 4) & 0x03030303u; o0.w = (a >> 6) & 0x03030303u;
-        o1.x = b & 0x03030303u; o1.y = (b >> 2) & 0x03030303u;
-        o1.z = (b >> 4) & 0x03030303u; o1.w = (b >> 6) & 0x03030303u;
-        uint4 *p = reinterpret_cast<uint4 *>(lds_row + 32 * half);
-        p[0] = o0;
-        p[1] = o1;
-    }
-};
-
-// 16 activation codes in natural order -> the code order of the weights
-template <int WB> __device__ __forceinline__ uint4 gg_act_order(uint4 v)
-{
-    if constexpr (WB == 4) {
-        uint4 o;
-        o.x = perm(v.y, v.x, 0x06040200u); o.y = perm(v.y, v.x, 0x07050301u);
-        o.z = perm(v.w, v.z, 0x06040200u); o.w = perm(v.w, v.z, 0x07050301u);
-        return o;
-    } else if constexpr (WB == 2) {
-        const uint32_t p01 = perm(v.y, v.x, 0x06020400u), q01 = perm(v.y, v.x, 0x07030501u);
-        const uint32_t p23 = perm(v.w, v.z, 0x06020400u), q23 = perm(v.w, v.z, 0x07030501u);
-        uint4 o;
-        o.x = perm(p23, p01, 0x05040100u);
-        o.y = perm(q23, q01, 0x05040100u);
-        o.z = perm(p23, p01, 0x07060302u);
-        o.w = perm(q23, q01, 0x07060302u);
-        return o;
-    } else {
-        return v;
-    }
-}
-
+// The small arrays come first: LDS instructions encode offsets below 64 KB
+// as immediates, so the scales and activations are reached from one base
+// register each.
 struct GgLds {
-    uint8_t w[2][kGgWRows][kGgRow];  // weight rows (int8, offset form), two pipeline buffers
-    uint8_t a[2][kGgTN][kGgRow];     // activation rows
-    float d[2][2][kGgTN];            // activation block scales of the step's two blocks
-    int arow[kGgTN];                 // activation row of each tile row (-1: padding)
-    float corr[kGgTN];               // sum_b d_b S_b of each tile row
-    float cw[kGgTN];                 // combine weight of each tile row (down only)
+    float d[2][kGgNBS][kGgTN];                            // activation block scales, two pipeline buffers
+    int arow[kGgTN];                                      // source row of each tile row
+    float cw[kGgTN];                                      // combine weight of each tile row (down)
+    __align__(16) uint8_t a[2][kGgTN * kGgRowStride];     // activation operands
+    __align__(16) uint8_t w[2][kGgWRows * kGgRowStride];  // weight operands
 };
 
 __device__ __forceinline__ v4i lds16(const uint8_t *p) { return *reinterpret_cast<const v4i *>(p); }
 
-// Main loop shared by both GEMMs (n = live rows of the tile).  L.arow must
-// be set.  Thread tid loads
-// weight row tid/2 (wsrc), half tid%2 of each step; activation row tid/4,
-// 16-byte part tid%4; and (tid < 128) the scale of row tid/2, block tid%2.
-// Wave w computes activation rows 32*nt .. +32 of the tile against weight
-// tiles m0 and m1 (32 rows each); acc0 / acc1 come back in MFMA layout:
-// lane l, register v = weight row 8(v/4) + 4(l/32) + v%4 of the tile,
-// activation row l%32.
+// An empty instruction that takes the accumulator tuples as operands and
+// orders all memory accesses around it: everything that produces them is
+// issued before it, and no later load is issued ahead of it.
+__device__ __forceinline__ void pin_after(v16f &a, v16f &b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
+
+// Packed codes of one 16-byte chunk -> its MFMA operand chunks in LDS.
+//   int4: the chunk is one block of 32 codes; operand chunk 2b (lanes 0-31)
+//         holds the low nibbles masked into the top bits (16 c_even),
+//         chunk 2b+1 the high nibbles in place (16 c_odd);
+//   int2: the chunk is blocks 2p, 2p+1 (8 bytes each); for each block,
+//         operand chunk (lanes 0-31) holds fields 0, 1 of its two dwords
+//         shifted to the top bits, the next chunk fields 2, 3 (64c);
+//   int8: the chunk is half a block, stored as is.
 template <int WB>
-__device__ __forceinline__ void gg_mainloop(GgLds &L, const uint8_t *wsrc, const int8_t *__restrict__ aq,
-                                            const float *__restrict__ ad, int K, int nt, int m0, int m1, int n,
-                                            float (&acc0)[16], float (&acc1)[16])
+__device__ __forceinline__ void gg_stage_w(uint8_t *wbuf, int r, int pc, const v4u &v)
 {
-    // a wave whose 32 rows are all padding only loads and stages
-    const bool live = 32 * nt < n;
-    const int tid = threadIdx.x, l = lane_id();
+    if constexpr (WB == 4) {
+        v4u lo, hi;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            lo[j] = (v[j] << 4) & 0xF0F0F0F0u;
+            hi[j] = v[j] & 0xF0F0F0F0u;
+        }
+        *reinterpret_cast<v4u *>(wbuf + ldsoff(r, 2 * pc)) = lo;
+        *reinterpret_cast<v4u *>(wbuf + ldsoff(r, 2 * pc + 1)) = hi;
+    } else if constexpr (WB == 2) {
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const uint32_t d0 = v[2 * q], d1 = v[2 * q + 1];
+            v4u lo, hi;
+            lo[0] = (d0 << 6) & 0xC0C0C0C0u; lo[1] = (d0 << 4) & 0xC0C0C0C0u;
+            lo[2] = (d1 << 6) & 0xC0C0C0C0u; lo[3] = (d1 << 4) & 0xC0C0C0C0u;
+            hi[0] = (d0 << 2) & 0xC0C0C0C0u; hi[1] = d0 & 0xC0C0C0C0u;
+            hi[2] = (d1 << 2) & 0xC0C0C0C0u; hi[3] = d1 & 0xC0C0C0C0u;
+            *reinterpret_cast<v4u *>(wbuf + ldsoff(r, 4 * pc + 2 * q)) = lo;
+            *reinterpret_cast<v4u *>(wbuf + ldsoff(r, 4 * pc + 2 * q + 1)) = hi;
+        }
+    } else {
+        *reinterpret_cast<v4u *>(wbuf + ldsoff(r, pc)) = v;
+    }
+}
+
+// Staging registers of one pipeline step: the thread's packed weight
+// chunks, its activation chunk and (threads below 512) one activation scale.
+template <int WB> struct GgRegs {
+    v4u w[GgCfg<WB>::WLD], a;
+    float d;
+};
+
+// Main loop shared by both GEMMs.  The workgroup's 256 weight rows are
+// rows 0..255 after w0 (GU = false), or rows 0..127 after w0 and 0..127
+// after w1 (GU = true: gate then up), each of wrb bytes; its 128 activation
+// rows start at aq + L.arow[i] * K (codes in code order), their scales at
+// ad + L.arow[i] * (K/32).  Wave w computes the 32 tile rows 32 (w >> 2) ..
+// (LIVE: some of them are live; uniform in the wave) against the weight
+// rows wr[wt] + (lane % 32) of its two 32-row weight tiles.  acc[wt] comes
+// back in MFMA layout: lane l, register v = weight row
+// 8 (v / 4) + 4 (l / 32) + v % 4 of weight tile wt, tile row
+// 32 (w >> 2) + l % 32.
+//
+// Pipeline: two LDS buffers (one barrier per step).  At the start of step s
+// the loads of step s + 1 go out into the staging registers, the MFMAs of
+// step s run from LDS, then the registers are stored to the other buffer;
+// four waves per SIMD cover the load latency across waves.  Every staging
+// register is indexed by compile-time constants, so it stays in a VGPR.
+template <int WB, bool GU, bool LIVE>
+__device__ __forceinline__ void gg_mainloop(GgLds &L, const uint8_t *w0, const uint8_t *w1, size_t wrb,
+                                            const int (&wr)[2], const int8_t *__restrict__ aq,
+                                            const float *__restrict__ ad, int K, v16f (&acc)[2])
+{
+    using C = GgCfg<WB>;
+    const int tid = threadIdx.x, l = lane_id(), h = l >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int nbk = K / 32, nsteps = K / kGgKS;
-    const int wr = tid >> 1, wh = tid & 1;
-    const int ar = tid >> 2, ap = tid & 3;
-    const int dr = (tid >> 1) & (kGgTN - 1), db = tid & 1;
-    const int arow_a = L.arow[ar], arow_d = L.arow[dr];
-    const int8_t *asrc = arow_a >= 0 ? aq + (size_t)arow_a * K + 16 * ap : nullptr;
-    const float *dsrc = (tid < 2 * kGgTN && arow_d >= 0) ? ad + (size_t)arow_d * nbk + db : nullptr;
-    GgW<WB> wn;
-    uint4 an;
-    float dn;
-    auto fetch = [&](int s) {
-        const int k0 = s * kGgKS;
-        wn.load(wsrc, k0, wh);
-        an = asrc ? *reinterpret_cast<const uint4 *>(asrc + k0) : make_uint4(0, 0, 0, 0);
-        dn = dsrc ? dsrc[2 * s] : 0.f;
+    const int r0 = 32 * (w >> 2) + (l & 31);
+
+    // staging sources of this thread: packed weight chunks (id < WCH; for
+    // int2 the upper half of the workgroup has none, a whole-wave split),
+    // one activation chunk, one scale (threads < 512: row t/4, block t%4)
+    const uint8_t *wp[C::WLD];
+    int wrw[C::WLD], wpc[C::WLD];
+#pragma unroll
+    for (int i = 0; i < C::WLD; i++) {
+        const int id = min(tid + kGgThreads * i, C::WCH - 1), r = id / C::PCR, pc = id % C::PCR;
+        const bool up = GU && r >= 128;  // gate rows 0..127, up rows 128..255
+        wp[i] = (up ? w1 : w0) + (size_t)(up ? r - 128 : r) * wrb + 16 * pc;
+        wrw[i] = r;
+        wpc[i] = pc;
+    }
+    const bool wlast = tid + kGgThreads * (C::WLD - 1) < C::WCH;  // the last weight chunk is this thread's
+    const int ar = tid / kGgCPR, ac = tid % kGgCPR;
+    const int8_t *ap = aq + (size_t)L.arow[ar] * K + 16 * ac;
+    const int ao = ldsoff(ar, ac);
+    const bool dl = tid < kGgTN * kGgNBS;
+    const int dr = (tid >> 2) & (kGgTN - 1), db = tid & 3;
+    const float *dp = ad + (size_t)L.arow[dr] * nbk + db;
+
+    // loads of step s (a step past the end reads the last one again: an L2
+    // hit, and no load under a branch)
+    auto fetch = [&](GgRegs<WB> &R, int s) {
+        s = s < nsteps ? s : nsteps - 1;
+        const size_t kw = (size_t)s * C::PRB, ka = (size_t)s * kGgKS;
+#pragma unroll
+        for (int i = 0; i < C::WLD; i++) R.w[i] = *reinterpret_cast<const v4u *>(wp[i] + kw);
+        R.a = *reinterpret_cast<const v4u *>(ap + ka);
+        R.d = dp[s * kGgNBS];
     };
-    auto stage = [&](int buf) {
-        wn.store(L.w[buf][wr], wh);
-        *reinterpret_cast<uint4 *>(&L.a[buf][ar][16 * ap]) = gg_act_order<WB>(an);
-        if (tid < 2 * kGgTN) L.d[buf][db][dr] = dn;
+    auto stage = [&](const GgRegs<WB> &R, int buf) {
+#pragma unroll
+        for (int i = 0; i < C::WLD; i++)
+            if (i + 1 < C::WLD || wlast) gg_stage_w<WB>(L.w[buf], wrw[i], wpc[i], R.w[i]);
+        *reinterpret_cast<v4u *>(&L.a[buf][ao]) = R.a;
+        if (dl) L.d[buf][db][dr] = R.d;
     };
     v16i zero;
 #pragma unroll
     for (int v = 0; v < 16; v++) zero[v] = 0;
+    // MFMAs of the step in LDS buffer buf
+    auto compute = [&](int buf) {
+        if constexpr (LIVE) {
+            const uint8_t *wb = L.w[buf], *abuf = L.a[buf];
 #pragma unroll
-    for (int v = 0; v < 16; v++) { acc0[v] = 0.f; acc1[v] = 0.f; }
+            for (int b = 0; b < kGgNBS; b++) {
+                const int c = 2 * b + h;
+                const v4i a0 = lds16(wb + ldsoff(wr[0] + (l & 31), c));
+                const v4i a1 = lds16(wb + ldsoff(wr[1] + (l & 31), c));
+                const v4i b0 = lds16(abuf + ldsoff(r0, c));
+                const float d0 = L.d[buf][b][r0];
+                const v16i i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, zero, 0, 0, 0);
+                const v16i i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b0, zero, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    acc[0][v] = fmaf((float)i0[v], d0, acc[0][v]);
+                    acc[1][v] = fmaf((float)i1[v], d0, acc[1][v]);
+                }
+                // the block's rescale completes before the next block's LDS
+                // reads and MFMAs are issued: one block's operands and
+                // results live at a time (4 waves per SIMD: 128 VGPRs)
+                pin_after(acc[0], acc[1]);
+            }
+        }
+    };
+#pragma unroll
+    for (int wt = 0; wt < 2; wt++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[wt][v] = 0.f;
 
-    fetch(0);
-    stage(0);
+    GgRegs<WB> R;
+    fetch(R, 0);
+    stage(R, 0);
     __syncthreads();
     for (int s = 0; s < nsteps; s++) {
         const int buf = s & 1;
-        if (s + 1 < nsteps) fetch(s + 1);
-#pragma unroll
-        for (int b = 0; b < 2 && live; b++) {
-            const int koff = 32 * b + 16 * (l >> 5);
-            const v4i a0 = lds16(&L.w[buf][32 * m0 + (l & 31)][koff]);
-            const v4i a1 = lds16(&L.w[buf][32 * m1 + (l & 31)][koff]);
-            const v4i bx = lds16(&L.a[buf][32 * nt + (l & 31)][koff]);
-            const float dd = L.d[buf][b][32 * nt + (l & 31)];
-            const v16i i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, zero, 0, 0, 0);
-            const v16i i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, zero, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 16; v++) {
-                acc0[v] = fmaf((float)i0[v], dd, acc0[v]);
-                acc1[v] = fmaf((float)i1[v], dd, acc1[v]);
-            }
-        }
-        if (s + 1 < nsteps) stage(buf ^ 1);
+        fetch(R, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf);
+        __builtin_amdgcn_sched_barrier(0);
+        stage(R, buf ^ 1);
         __syncthreads();
     }
+}
+
+// the main loop for this wave's 32 tile rows: MFMAs only if one of them is live
+template <int WB, bool GU>
+__device__ __forceinline__ void gg_mainloop_rows(GgLds &L, const uint8_t *w0, const uint8_t *w1, size_t wrb,
+                                                 const int (&wr)[2], const int8_t *aq, const float *ad, int K, int n,
+                                                 v16f (&acc)[2])
+{
+    const int rbase = 32 * (__builtin_amdgcn_readfirstlane(wave_id()) >> 2);
+    if (rbase < n) gg_mainloop<WB, GU, true>(L, w0, w1, wrb, wr, aq, ad, K, acc);
+    else gg_mainloop<WB, GU, false>(L, w0, w1, wrb, wr, aq, ad, K, acc);
 }
 
 __device__ __forceinline__ const moe_weights_t &gg_expert(const GgArgs &a, int e, size_t &eo)
@@ -294,130 +367,140 @@ __device__ __forceinline__ const moe_weights_t &gg_expert(const GgArgs &a, int e
     return (e == a.E) ? a.shared : a.routed;
 }
 
+// The workgroup's (tile, channel group) under the XCD-aware order; false if
+// it has none.
+__device__ __forceinline__ bool gg_item(const GgArgs &a, int ncg, int &tile, int &cg)
+{
+    const int b = blockIdx.x, x = b & 7, j = b >> 3;
+    const int cpx = (ncg + 7) / 8;
+    tile = j / cpx;
+    const int c = j % cpx;
+    cg = x * cpx + c;
+    return cg < ncg && tile < a.tiles[0].x;
+}
+
 // ---------------------------------------------------------------- gate / up
+// Wave w: tile rows 32 (w >> 2) .. + 32 and intermediate channels
+// c0 + 32 (w & 3) .. + 32 (weight tile 0: their gate rows, 1: their up rows).
 template <int WB>
 __global__ __launch_bounds__(kGgThreads) void k_gg_gate_up(const GgArgs a)
 {
     __shared__ GgLds L;
-    if ((int)blockIdx.y >= a.tiles[0].x) return;
-    const int4 tile = a.tiles[1 + blockIdx.y];
+    int tix, cg;
+    if (!gg_item(a, a.I / 128, tix, cg)) return;
+    const int4 tile = a.tiles[1 + tix];
     const int e = tile.x, row0 = tile.y, n = tile.z;
     const int tid = threadIdx.x, H = a.H, I = a.I;
-    const int c0 = blockIdx.x * 64;
+    const int c0 = cg * 128;
     const size_t rb = (size_t)H * WB / 8;
     size_t eo;
     const moe_weights_t &W = gg_expert(a, e, eo);
     if (tid < kGgTN) {
-        int tok = -1;
-        if (tid < n) {
-            const int r = row0 + tid;
-            tok = (r < a.Tk) ? a.perm[r] / a.k : r - a.Tk;
-        }
-        L.arow[tid] = tok;
-        L.corr[tid] = tok >= 0 ? a.xs[tok] : 0.f;
+        // tile row -> token (rows past n repeat the first row's token: loaded, never stored)
+        const int r = row0 + (tid < n ? tid : 0);
+        L.arow[tid] = (r < a.Tk) ? a.perm[r] / a.k : r - a.Tk;
     }
     __syncthreads();
-    const int wr = tid >> 1;
-    const uint8_t *wsrc = (wr < 64) ? W.gate + (eo * I + c0 + wr) * rb : W.up + (eo * I + c0 + wr - 64) * rb;
-    const int wv = wave_id(), nt = wv >> 1, mh = wv & 1;
-    float ag[16], au[16];
-    gg_mainloop<WB>(L, wsrc, a.xq, a.xd, H, nt, mh, 2 + mh, n, ag, au);
+    const int w = __builtin_amdgcn_readfirstlane(wave_id()), cw = w & 3;
+    const int wr[2] = {32 * cw, 128 + 32 * cw};
+    v16f acc[2];
+    gg_mainloop_rows<WB, true>(L, W.gate + (eo * I + c0) * rb, W.up + (eo * I + c0) * rb, rb, wr, a.xq, a.xd, H,
+                               n, acc);
 
     // epilogue: lane = (tile row i, channel half hf); 16 channels of the
-    // wave's 32-channel block cb
-    const int l = lane_id(), i = 32 * nt + (l & 31), hf = l >> 5;
-    const float corr = (float)GgW<WB>::kOff * L.corr[i];
-    const int cb = c0 + 32 * mh;
-    const float *gs = W.gate_s + eo * I, *us = W.up_s + eo * I;
-    float h[16];
+    // wave's 32-channel block; h quantised per block, gathered in LDS in
+    // natural order, then written out in code order
+    const int l = lane_id(), hf = l >> 5;
+    const int i = 32 * (w >> 2) + (l & 31);
+    uint8_t *qs = &L.a[0][0];  // [128 rows][128 channels] over the activation buffers (36 KB), free now
+    const int cl = 32 * cw;    // the block's first channel within the workgroup's 128
+    const float *gs = W.gate_s + eo * I + c0 + cl, *us = W.up_s + eo * I + c0 + cl;
+    constexpr float inv = GgCfg<WB>::kInv;
+    float hv[16];
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-        const int ch = cb + 8 * (v >> 2) + 4 * hf + (v & 3);
-        const float g = gs[ch] * (ag[v] - corr);
-        const float u = us[ch] * (au[v] - corr);
-        h[v] = silu_mul(g, u);
+    for (int j = 0; j < 4; j++) {
+        const float4 g4 = *reinterpret_cast<const float4 *>(gs + 8 * j + 4 * hf);
+        const float4 u4 = *reinterpret_cast<const float4 *>(us + 8 * j + 4 * hf);
+        const float gsc[4] = {g4.x, g4.y, g4.z, g4.w}, usc[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+            hv[4 * j + m] = silu_mul((gsc[m] * inv) * acc[0][4 * j + m], (usc[m] * inv) * acc[1][4 * j + m]);
     }
     // Q8_0 quantisation of h over the block of 32 channels (this lane's 16
     // and lane l^32's 16)
     float amax = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; v++) amax = fmaxf(amax, fabsf(h[v]));
+    for (int v = 0; v < 16; v++) amax = fmaxf(amax, fabsf(hv[v]));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const float dq = amax / 127.0f;
-    uint32_t wq[4] = {0, 0, 0, 0};
-    int qsum = 0;
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-        float r = (dq == 0.0f) ? 0.0f : rintf(h[v] / dq);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        const int qi = (int)r;
-        qsum += qi;
-        wq[v >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (v & 3));
-    }
-    qsum += __shfl_xor(qsum, 32);
-    if (i < n) {
-        const size_t r = (size_t)row0 + i;
-        int8_t *qrow = a.qh + r * I;
+    for (int j = 0; j < 4; j++) {
+        uint32_t wq = 0;
 #pragma unroll
-        for (int j = 0; j < 4; j++) *reinterpret_cast<uint32_t *>(qrow + cb + 8 * j + 4 * hf) = wq[j];
-        if (hf == 0) {
-            a.dh[r * (I / 32) + cb / 32] = dq;
-            a.zh[r * (I / 32) + cb / 32] = dq * (float)qsum;
+        for (int m = 0; m < 4; m++) {
+            float r = (dq == 0.0f) ? 0.0f : rintf(hv[4 * j + m] / dq);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            wq |= ((uint32_t)(int)r & 0xFFu) << (8 * m);
         }
+        *reinterpret_cast<uint32_t *>(qs + i * 128 + cl + 8 * j + 4 * hf) = wq;
+    }
+    if (hf == 0 && i < n) a.dh[(size_t)(row0 + i) * (I / 32) + (c0 + cl) / 32] = dq;
+    __syncthreads();
+    // 128 rows x 4 blocks x 8 dwords, in code order
+    for (int id = tid; id < kGgTN * 32; id += kGgThreads) {
+        const int ri = id >> 5, o = id & 31, bb = o >> 3;
+        if (ri < n)
+            *reinterpret_cast<uint32_t *>(a.qh + (size_t)(row0 + ri) * I + c0 + 32 * bb + 4 * (o & 7)) =
+                gg_pack_dword<WB>(qs + ri * 128 + 32 * bb, o & 7);
     }
 }
 
 // ---------------------------------------------------------------- down
+// Wave w: tile rows 32 (w >> 2) .. + 32 and hidden channels
+// n0 + 64 (w & 3) .. + 64 (two weight tiles of 32).
 template <int WB>
 __global__ __launch_bounds__(kGgThreads) void k_gg_down(const GgArgs a)
 {
     __shared__ GgLds L;
-    if ((int)blockIdx.y >= a.tiles[0].x) return;
-    const int4 tile = a.tiles[1 + blockIdx.y];
+    int tix, cg;
+    if (!gg_item(a, a.H / 256, tix, cg)) return;
+    const int4 tile = a.tiles[1 + tix];
     const int e = tile.x, row0 = tile.y, n = tile.z;
-    const int tid = threadIdx.x, H = a.H, I = a.I, nbh = I / 32;
-    const int n0 = blockIdx.x * 128;
+    const int tid = threadIdx.x, H = a.H, I = a.I;
+    const int n0 = cg * 256;
     const size_t rb = (size_t)I * WB / 8;
     size_t eo;
     const moe_weights_t &W = gg_expert(a, e, eo);
-    {
-        // correction sum_b dh_b S_b of each row: 4 threads per row, fixed order
-        const int i = tid >> 2, p = tid & 3;
-        float z = 0.f;
-        if (i < n)
-            for (int b = p; b < nbh; b += 4) z += a.zh[(size_t)(row0 + i) * nbh + b];
-        z += __shfl_xor(z, 1);
-        z += __shfl_xor(z, 2);
-        if (p == 0) {
-            const int r = row0 + i;
-            L.arow[i] = (i < n) ? r : -1;
-            L.corr[i] = z;
-            L.cw[i] = (i < n && r < a.Tk) ? a.w[a.perm[r]] : 1.0f;
-        }
+    if (tid < kGgTN) {
+        const int r = row0 + (tid < n ? tid : 0);
+        L.arow[tid] = r;
+        L.cw[tid] = (r < a.Tk) ? a.w[a.perm[r]] : 1.0f;
     }
     __syncthreads();
-    const uint8_t *wsrc = W.down + (eo * H + n0 + (tid >> 1)) * rb;
-    const int wv = wave_id(), nt = wv >> 1, m0 = 2 * (wv & 1);
-    float y0[16], y1[16];
-    gg_mainloop<WB>(L, wsrc, a.qh, a.dh, I, nt, m0, m0 + 1, n, y0, y1);
+    const int w = __builtin_amdgcn_readfirstlane(wave_id()), cw = w & 3;
+    const int wr[2] = {64 * cw, 64 * cw + 32};
+    v16f acc[2];
+    gg_mainloop_rows<WB, false>(L, W.down + (eo * H + n0) * rb, nullptr, rb, wr, a.qh, a.dh, I, n, acc);
 
-    const int l = lane_id(), i = 32 * nt + (l & 31), hf = l >> 5;
+    const int l = lane_id(), hf = l >> 5;
+    const int i = 32 * (w >> 2) + (l & 31);
     if (i >= n) return;
-    const float corr = (float)GgW<WB>::kOff * L.corr[i], cw = L.cw[i];
     const float *ds = W.down_s + eo * H;
+    constexpr float inv = GgCfg<WB>::kInv;
+    const float cwt = L.cw[i];
     float *yrow = a.yrows + (size_t)(row0 + i) * H;
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-        const float *acc = t ? y1 : y0;
-        const int cbase = n0 + 32 * (m0 + t) + 4 * hf;
+    for (int wt = 0; wt < 2; wt++) {
+        const int cbase = n0 + 64 * cw + 32 * wt + 4 * hf;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int ch = cbase + 8 * j;
+            const float4 s4 = *reinterpret_cast<const float4 *>(ds + ch);
             float4 o;
-            o.x = ds[ch + 0] * (acc[4 * j + 0] - corr) * cw;
-            o.y = ds[ch + 1] * (acc[4 * j + 1] - corr) * cw;
-            o.z = ds[ch + 2] * (acc[4 * j + 2] - corr) * cw;
-            o.w = ds[ch + 3] * (acc[4 * j + 3] - corr) * cw;
+            o.x = (s4.x * inv) * acc[wt][4 * j + 0] * cwt;
+            o.y = (s4.y * inv) * acc[wt][4 * j + 1] * cwt;
+            o.z = (s4.z * inv) * acc[wt][4 * j + 2] * cwt;
+            o.w = (s4.w * inv) * acc[wt][4 * j + 3] * cwt;
             *reinterpret_cast<float4 *>(yrow + ch) = o;
         }
     }
@@ -468,9 +551,12 @@ __global__ __launch_bounds__(256) void k_gg_combine(const GgArgs a)
 }
 
 // ---------------------------------------------------------------- launchers
+// 1-D grids of 8 XCDs x (channel groups per XCD) x max_tiles workgroups
+static unsigned gg_grid(int ncg, int max_tiles) { return 8u * (unsigned)((ncg + 7) / 8) * (unsigned)max_tiles; }
+
 int launch_gg_gate_up(const GgArgs &a, int max_tiles, hipStream_t st)
 {
-    const dim3 grid(a.I / 64, max_tiles);
+    const unsigned grid = gg_grid(a.I / 128, max_tiles);
     if (a.wbits == 4) k_gg_gate_up<4><<<grid, kGgThreads, 0, st>>>(a);
     else if (a.wbits == 8) k_gg_gate_up<8><<<grid, kGgThreads, 0, st>>>(a);
     else k_gg_gate_up<2><<<grid, kGgThreads, 0, st>>>(a);
@@ -479,7 +565,7 @@ int launch_gg_gate_up(const GgArgs &a, int max_tiles, hipStream_t st)
 
 int launch_gg_down(const GgArgs &a, int max_tiles, hipStream_t st)
 {
-    const dim3 grid(a.H / 128, max_tiles);
+    const unsigned grid = gg_grid(a.H / 256, max_tiles);
     if (a.wbits == 4) k_gg_down<4><<<grid, kGgThreads, 0, st>>>(a);
     else if (a.wbits == 8) k_gg_down<8><<<grid, kGgThreads, 0, st>>>(a);
     else k_gg_down<2><<<grid, kGgThreads, 0, st>>>(a);

@@ -220,7 +220,7 @@ int launch_gate_up(const GemvArgs &a, hipStream_t st);
 int launch_down(const GemvArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------- grouped path
-constexpr int kGgTN = 64;  // rows (token, expert assignments) per grouped-GEMM tile
+constexpr int kGgTN = 128;  // rows (token, expert assignments) per grouped-GEMM tile
 
 // 256-assignment tiles of the permutation's counting sort
 inline int perm_tiles(int n) { return (n + 255) / 256; }
@@ -233,12 +233,12 @@ inline int gg_max_tiles(const moe_shape_t &s, int T)
     const long used = tk < s.n_experts ? tk : s.n_experts;
     return (int)(tk / kGgTN + used + 1 + (s.n_shared ? (T + kGgTN - 1) / kGgTN : 0));
 }
-// shapes the grouped kernels take: 64-channel gate/up tiles, 128-channel down
-// tiles, K in steps of 64
-inline bool gg_shape_ok(const moe_shape_t &s) { return s.hidden % 128 == 0 && s.inter % 64 == 0; }
+// shapes the grouped kernels take: gate/up workgroups of 128 intermediate
+// channels, down workgroups of 256 hidden channels, K in steps of 128
+inline bool gg_shape_ok(const moe_shape_t &s) { return s.hidden % 256 == 0 && s.inter % 128 == 0; }
 
 struct GgWs {
-    size_t logits, idx, w, xq, xd, xs, perm, off, inv, pscr, tiles, qh, dh, zh, y, total;
+    size_t logits, idx, w, xq, xd, perm, off, inv, pscr, tiles, qh, dh, y, total;
 };
 GgWs gg_ws(const moe_shape_t &s, int T);
 
@@ -249,15 +249,15 @@ struct GgArgs {
     const int32_t *inv;     // assignment -> row
     const float *w;         // combine weight of each assignment
     moe_weights_t routed, shared;
-    const int8_t *xq;       // [T][H] int8 x, block scales xd, offset sums xs
-    const float *xd, *xs;
-    int8_t *qh;             // [rows][I] int8 h, block scales dh, zh = dh * code sum
-    float *dh, *zh;
+    const int8_t *xq;       // [T][H] int8 x in the weights' code order (gg_act_pos), block scales xd
+    const float *xd;
+    int8_t *qh;             // [rows][I] int8 h in the same order, block scales dh
+    float *dh;
     float *yrows;           // [rows][H] weighted expert outputs
     float *y;               // [T][H] layer output
     int accumulate;
 };
-int launch_gg_quant(const float *x, int T, int D, int8_t *q, float *d, float *xs, hipStream_t st);
+int launch_gg_quant(const float *x, int T, int D, int wbits, int8_t *q, float *d, hipStream_t st);
 int launch_gg_gate_up(const GgArgs &a, int max_tiles, hipStream_t st);
 int launch_gg_down(const GgArgs &a, int max_tiles, hipStream_t st);
 int launch_gg_combine(const GgArgs &a, hipStream_t st);

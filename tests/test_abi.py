@@ -105,7 +105,7 @@ def test_grouped_workspace(m):
     assert ws > rows * 6144 * 4 + rows * 2048            # expert outputs + int8 h
     assert ws % 256 == 0
     assert m.moe_workspace_bytes(sh, 1, G) > 0
-    assert m.moe_workspace_bytes(big_shape(m, hidden=6080), 2048, G) == 0   # 6080 % 128 != 0
+    assert m.moe_workspace_bytes(big_shape(m, hidden=6080), 2048, G) == 0   # 6080 % 256 != 0
     # AUTO falls back to the GEMV path where the grouped kernels do not fit
     assert m.moe_workspace_bytes(big_shape(m, hidden=6080), 2048) > 0
 
