@@ -199,6 +199,8 @@ def main():
     ap.add_argument("--slots", type=int, default=32, help="tier_int4: HBM slots for routed experts (of 256)")
     ap.add_argument("--repin", type=int, default=16, help="tier_int4: tokens between live repins")
     ap.add_argument("--layers", type=int, default=4, help="tier_stack_int4: layers")
+    ap.add_argument("--lookahead", type=int, default=0,
+                    help="stack_int2: router lookahead, N workgroups per prefetched expert (0 = off)")
     ap.add_argument("--lookahead-ranks", type=int, default=None,
                     help="tier_stack_int4: prefetch only the first N ranks of each predicted selection")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -467,7 +469,8 @@ def bench_stack(args, wl):
         (wl.name, wl.layers, wl.hidden, wl.inter, wl.n_experts, wl.top_k, wl.wbits))
     hosts, layers = synth.device_stack(wl, dev)
     arr = moe.layers(layers)
-    ws = moe.workspace(moe.moe_stack_workspace_bytes(sh, 1), dev)
+    la = moe.MOE_LOOKAHEAD(args.lookahead)
+    ws = moe.workspace(moe.moe_stack_workspace_bytes(sh, 1, la), dev)
     xs = torch.stack([torch.from_numpy(synth.host_normals(wl.seed + i, synth.stream_id(0, synth.X), wl.hidden, 1.0)
                                        .reshape(1, wl.hidden)) for i in range(n_inputs)]).to(dev)
     x = torch.empty((1, wl.hidden), dtype=torch.float32, device=dev)
@@ -487,7 +490,7 @@ def bench_stack(args, wl):
         cap.wait_stream(stream)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=cap):
-            moe.moe_stack_forward(sh, x, arr, eps, ws)
+            moe.moe_stack_forward(sh, x, arr, eps, ws, flags=la)
         torch.cuda.synchronize()
 
     def step(i):
@@ -495,7 +498,7 @@ def bench_stack(args, wl):
         if graph is not None:
             graph.replay()
         else:
-            moe.moe_stack_forward(sh, x, arr, eps, ws)
+            moe.moe_stack_forward(sh, x, arr, eps, ws, flags=la)
 
     for i in range(warmup):
         flush()
@@ -617,7 +620,7 @@ def bench_stack(args, wl):
         "config": {"workload": wl.name, "T": 1, "layers": wl.layers, "hidden": wl.hidden, "inter": wl.inter,
                    "n_experts": wl.n_experts, "n_group": wl.n_group, "topk_group": wl.topk_group,
                    "top_k": wl.top_k, "n_shared": wl.n_shared, "wbits": wl.wbits, "rsf": wl.rsf,
-                   "path": "gemv", "graph": graph is not None},
+                   "path": "gemv", "graph": graph is not None, "lookahead_wgs": args.lookahead},
         "effective_weight_GBps": token_bytes / (ms * 1e-3) / 1e9,
         "effective_weight_frac": token_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -120,6 +120,10 @@ const char *moe_strerror(int code);
  * all of them, in order, with the same arguments and workspace. */
 #define MOE_STAGE(n)      (1u << (8 + (n)))
 #define MOE_STAGE_MASK    0xFF00u
+/* moe_stack_forward only: router lookahead with n (1 .. 63) workgroups per
+ * prefetched expert; 0 (the default) turns it off. */
+#define MOE_LOOKAHEAD(n)  ((uint32_t)(n) << 16)
+#define MOE_LOOKAHEAD_MASK 0x3F0000u
 
 /* ---------------------------------------------------------------- router */
 /* moe_route -- noaux_tc routing of T tokens (GeekNews #31297, implemented
@@ -242,9 +246,22 @@ int moe_rmsnorm(const float *x, const float *g, double eps, int32_t T, int32_t H
  *   flags    MOE_PATH_* (MOE_ACCUMULATE is implied); MOE_STAGE(n) selects
  *            stage n of every layer as moe_layer_stage_count counts them,
  *            with a separate RMSNorm launch (when there is one) run with
- *            stage 0
+ *            stage 0; MOE_LOOKAHEAD(n) turns on the router lookahead
+ *            (wpnews.pro Colibri page, paragraph "Router-lookahead prefetch
+ *            (PILOT=1)"): for one token on the GEMV path, where the router
+ *            launch normalises its input, layer l's router launch also runs
+ *            layer l+1's router (its norm weight, router weights and
+ *            correction bias) on layer l's input x, and layer l's gate/up
+ *            launch gets n extra workgroups per expert that prediction
+ *            selects (its top_k ranks by the noaux_tc selection, top-p not
+ *            applied) and per shared expert of layer l+1; they read that
+ *            expert's codes and scales with non-temporal loads so that they
+ *            sit in the memory-side cache when layer l+1 reads them.  The
+ *            results are identical with and without it; only the timing
+ *            changes.  Elsewhere (T > 1, grouped path) it is ignored.
  * ws: at least moe_stack_workspace_bytes(shape, T, flags) bytes, 256-byte
- *   aligned.  The launches only read the layers array during the call, so a
+ *   aligned (the lookahead adds the predicted logits and one word per
+ *   wave of its workgroups).  The launches only read the layers array during the call, so a
  *   stream capture of one call replays with the same device pointers. */
 typedef struct {
     const float *gate_w;        /* [E][H] router weights */

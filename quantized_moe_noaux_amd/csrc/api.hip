@@ -242,10 +242,22 @@ int moe_expert_ffn(const moe_shape_t *shape, const moe_weights_t *w, int32_t exp
     return MOE_OK;
 }
 
+// The next layer of a decode stack, for the router lookahead: its router
+// weights, norm weight, correction bias and experts, the workgroups per
+// prefetched expert, and workspace for its predicted logits and the sink.
+struct Lookahead {
+    const float *gate_w, *ng, *bias;
+    moe_weights_t routed, shared;
+    int wgs;
+    double *logits;
+    uint32_t *sink;
+};
+
 static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float *gate_w, const float *bias,
                       const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
                       float *w_out, uint32_t flags, void *ws, size_t ws_bytes, const float *ng, double eps,
-                      hipStream_t stream, const int64_t *toff = nullptr, uint32_t *counts = nullptr);
+                      hipStream_t stream, const int64_t *toff = nullptr, uint32_t *counts = nullptr,
+                      const Lookahead *la = nullptr);
 
 int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const float *gate_w, const float *bias,
                       const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
@@ -276,11 +288,14 @@ int moe_layer_forward(const moe_shape_t *shape, const float *x, int32_t T, const
 // moe_layer_forward on the GEMV path (arguments already checked).  With
 // ng != nullptr the layer input is RMSNorm(x) with weight ng, formed by the
 // router launch (router_norms_input must hold); y may then be x itself with
-// MOE_ACCUMULATE, since x is read by the router launch only.
+// MOE_ACCUMULATE, since x is read by the router launch only.  With la (one
+// token, routed inside the gate/up launch, ng given) the router launch also
+// computes the next layer's logits on the same input and the gate/up launch
+// prefetches the experts they select; the layer's results do not change.
 static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float *gate_w, const float *bias,
                       const moe_weights_t *routed, const moe_weights_t *shared, float *y, int32_t *idx_out,
                       float *w_out, uint32_t flags, void *ws, size_t ws_bytes, const float *ng, double eps,
-                      hipStream_t stream, const int64_t *toff, uint32_t *counts)
+                      hipStream_t stream, const int64_t *toff, uint32_t *counts, const Lookahead *la)
 {
     const moe_shape_t *shape = &sh;
     if (shape->hidden % kGemvDownRows) return MOE_EUNSUPPORTED;
@@ -320,9 +335,13 @@ static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float 
         a.counts = counts;
         return a;
     };
+    const bool here = gemv_inline_route(*shape, T);
+    if (la && (!here || !ng || toff || la->wgs <= 0)) la = nullptr;
     int stage = 0;
     if (T <= kGemvMaxT) {
-        if (run(stage) && launch_router_logits(x, T, H, gate_w, E, logits, xq, xd, ng, eps, stream))
+        if (run(stage) && launch_router_logits(x, T, H, gate_w, E, logits, xq, xd, ng, eps, stream,
+                                               la ? la->gate_w : nullptr, la ? la->ng : nullptr,
+                                               la ? la->logits : nullptr))
             return MOE_EHIP;
         stage++;
     } else {
@@ -332,10 +351,14 @@ static int layer_gemv(const moe_shape_t &sh, const float *x, int T, const float 
         if (run(stage) && launch_quant(x, T, H, xq, xd, stream)) return MOE_EHIP;
         stage++;
     }
-    const bool here = gemv_inline_route(*shape, T);
     for (int c0 = 0; c0 < T; c0 += Tc) {
         GemvArgs a = args(c0, (T - c0 < Tc) ? T - c0 : Tc);
         a.inline_route = here ? 1 : 0;
+        if (la) {
+            a.la_logits = la->logits; a.la_bias = la->bias;
+            a.la_routed = la->routed; a.la_shared = la->shared;
+            a.la_wgs = la->wgs; a.la_sink = la->sink;
+        }
         if (!here) {
             if (run(stage) && launch_plan(a, stream)) return MOE_EHIP;
             stage++;
@@ -688,11 +711,22 @@ int moe_rmsnorm(const float *x, const float *g, double eps, int32_t T, int32_t H
     return hip_rc(launch_rmsnorm(x, g, eps, T, H, out, stream));
 }
 
+// the lookahead's part of a stack's workspace: the next layer's logits of
+// the one token, then the sink words of its workgroups
+static size_t lookahead_bytes(const moe_shape_t &s, uint32_t flags)
+{
+    const int wgs = (int)((flags & MOE_LOOKAHEAD_MASK) >> 16);
+    if (!wgs) return 0;
+    return align256(sizeof(double) * s.n_experts) +
+           align256(sizeof(uint32_t) * kLookaheadSinkWords * wgs * (s.top_k + (s.n_shared ? 1 : 0)));
+}
+
 size_t moe_stack_workspace_bytes(const moe_shape_t *shape, int32_t T, uint32_t flags)
 {
-    const size_t layer = moe_workspace_bytes(shape, T, flags);
+    const size_t layer = moe_workspace_bytes(shape, T, flags & 3u);
     if (!layer) return 0;
-    return align256(sizeof(float) * (size_t)(T > 0 ? T : 1) * shape->hidden) + layer;
+    return align256(sizeof(float) * (size_t)(T > 0 ? T : 1) * shape->hidden) + lookahead_bytes(*shape, flags) +
+           layer;
 }
 
 int moe_stack_forward(const moe_shape_t *shape, float *x, int32_t T, const moe_layer_t *layers, int32_t n_layers,
@@ -702,7 +736,7 @@ int moe_stack_forward(const moe_shape_t *shape, float *x, int32_t T, const moe_l
     int rc = check_shape(shape);
     if (rc) return rc;
     if (T < 0 || n_layers < 0 || !(eps >= 0.0)) return MOE_EINVAL;
-    if (flags & ~(3u | MOE_STAGE_MASK)) return MOE_EINVAL;
+    if (flags & ~(3u | MOE_STAGE_MASK | MOE_LOOKAHEAD_MASK)) return MOE_EINVAL;
     if ((flags & 3u) == 3u) return MOE_EINVAL;
     if ((idx_out == nullptr) != (w_out == nullptr)) return MOE_EINVAL;
     if (T == 0 || n_layers == 0) return MOE_OK;
@@ -717,8 +751,12 @@ int moe_stack_forward(const moe_shape_t *shape, float *x, int32_t T, const moe_l
     if (!need) return MOE_EUNSUPPORTED;
     if (ws_bytes < need) return MOE_EWORKSPACE;
     const size_t nb = align256(sizeof(float) * (size_t)T * shape->hidden);
+    const size_t lab = lookahead_bytes(*shape, flags);
     float *n = static_cast<float *>(ws);
-    void *lws = static_cast<char *>(ws) + nb;
+    char *lap = static_cast<char *>(ws) + nb;
+    void *lws = lap + lab;
+    const size_t lws_bytes = ws_bytes - nb - lab;
+    const uint32_t lflags = flags & (3u | MOE_STAGE_MASK);
     const size_t tk = (size_t)T * shape->top_k;
     const uint32_t sel = (flags & MOE_STAGE_MASK) >> 8;
     for (int l = 0; l < n_layers; l++) {
@@ -726,16 +764,27 @@ int moe_stack_forward(const moe_shape_t *shape, float *x, int32_t T, const moe_l
         const moe_weights_t *sw = shape->n_shared ? &L.shared : nullptr;
         int32_t *il = idx_out ? idx_out + l * tk : nullptr;
         float *wl = w_out ? w_out + l * tk : nullptr;
-        if (!use_grouped(*shape, T, flags) && T <= kGemvMaxT && router_norms_input(x, L.norm_g, shape->hidden)) {
+        if (!use_grouped(*shape, T, lflags) && T <= kGemvMaxT && router_norms_input(x, L.norm_g, shape->hidden)) {
             // the router launch normalises the residual itself; the layer
             // adds its output to the residual in place
-            rc = layer_gemv(*shape, x, T, L.gate_w, L.bias, &L.routed, sw, x, il, wl, flags | MOE_ACCUMULATE, lws,
-                            ws_bytes - nb, L.norm_g, eps, stream);
+            Lookahead la{};
+            const bool look = lab && l + 1 < n_layers && router_norms_input(x, layers[l + 1].norm_g, shape->hidden);
+            if (look) {
+                const moe_layer_t &N = layers[l + 1];
+                la.gate_w = N.gate_w; la.ng = N.norm_g; la.bias = N.bias;
+                la.routed = N.routed;
+                if (shape->n_shared) la.shared = N.shared;
+                la.wgs = (int)((flags & MOE_LOOKAHEAD_MASK) >> 16);
+                la.logits = reinterpret_cast<double *>(lap);
+                la.sink = reinterpret_cast<uint32_t *>(lap + align256(sizeof(double) * shape->n_experts));
+            }
+            rc = layer_gemv(*shape, x, T, L.gate_w, L.bias, &L.routed, sw, x, il, wl, lflags | MOE_ACCUMULATE, lws,
+                            lws_bytes, L.norm_g, eps, stream, nullptr, nullptr, look ? &la : nullptr);
         } else {
             if ((sel == 0 || (sel & 1u)) && launch_rmsnorm(x, L.norm_g, eps, T, shape->hidden, n, stream))
                 return MOE_EHIP;
-            rc = moe_layer_forward(shape, n, T, L.gate_w, L.bias, &L.routed, sw, x, il, wl, flags | MOE_ACCUMULATE,
-                                   lws, ws_bytes - nb, stream);
+            rc = moe_layer_forward(shape, n, T, L.gate_w, L.bias, &L.routed, sw, x, il, wl, lflags | MOE_ACCUMULATE,
+                                   lws, lws_bytes, stream);
         }
         if (rc) return rc;
     }

@@ -836,6 +836,70 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
     }
 }
 
+// Router lookahead (wpnews.pro "Colibri -- GLM-5.2 (744B MoE) on 25GB RAM in
+// one pure C file", paragraph "Router-lookahead prefetch (PILOT=1)": layer
+// L+1's router, run on layer L's state, predicts the experts layer L+1 will
+// select, and those are fetched while layer L computes).
+// Lookahead workgroup j of unit j / la_wgs: units 0 .. k-1 are the experts of
+// ranks 0 .. k-1 of the next layer's selection (the full noaux_tc selection
+// on la_logits, the same wave-level routine as the routing itself; top-p is
+// ignored: every rank the prediction names is fetched), unit k is the next
+// layer's shared expert.  The workgroup streams slice j % la_wgs of the
+// expert's gate, up and down codes (and, slice 0, its row scales) with
+// non-temporal loads: they bypass the L2s and fill the memory-side cache,
+// from which that layer's kernels then read them.  The loaded data only
+// feeds an XOR stored to la_sink, which keeps the loads.
+template <int WB>
+__device__ void gate_up_lookahead(const GemvArgs &a, int j)
+{
+    __shared__ int s_e;
+    const int unit = j / a.la_wgs, slice = j % a.la_wgs, tid = threadIdx.x;
+    const moe_weights_t *W = &a.la_shared;
+    size_t e = 0;
+    if (unit < a.rc.k) {
+        RouteCfg rc = a.rc;
+        rc.top_p = 0.f;
+        if (__builtin_amdgcn_readfirstlane(wave_id()) == 0) {
+            const WaveSel ws = wave_topk(rc, a.la_logits, (size_t)a.E, 1, a.la_bias, unit + 1);
+            if (tid == 0) s_e = ws.last;
+        }
+        __syncthreads();
+        const int pe = s_e;
+        if (pe < 0 || pe >= a.E) return;
+        e = (size_t)pe;
+        W = &a.la_routed;
+    }
+    const size_t cb = (size_t)a.I * a.H * WB / 8;        // code bytes of each of gate, up, down
+    const size_t per = ((cb / 16) + a.la_wgs - 1) / a.la_wgs;  // 16-byte chunks per slice
+    const size_t c0 = (size_t)slice * per, c1 = min(c0 + per, cb / 16);
+    const uint8_t *src[3] = {W->gate + e * cb, W->up + e * cb, W->down + e * cb};
+    typedef unsigned v4u_nt __attribute__((ext_vector_type(4)));
+    uint32_t acc = 0;
+    constexpr int U = 8;  // loads in flight per thread
+#pragma unroll
+    for (int m = 0; m < 3; m++) {
+        const v4u_nt *p = reinterpret_cast<const v4u_nt *>(src[m]);
+        for (size_t c = c0 + tid; c < c1; c += (size_t)kSwThreads * U) {
+            v4u_nt v[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(p + min(c + (size_t)kSwThreads * u, c1 - 1));
+#pragma unroll
+            for (int u = 0; u < U; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        }
+    }
+    if (slice == 0) {
+        const float *sc[3] = {W->gate_s + e * a.I, W->up_s + e * a.I, W->down_s + e * a.H};
+        const int n[3] = {a.I, a.I, a.H};
+#pragma unroll
+        for (int m = 0; m < 3; m++)
+            for (int i = tid; i < n[m]; i += kSwThreads) acc ^= __float_as_uint(__builtin_nontemporal_load(sc[m] + i));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+    static_assert(kSwThreads / 64 <= kLookaheadSinkWords, "sink words per workgroup");
+    if (lane_id() == 0) a.la_sink[(size_t)j * kLookaheadSinkWords + wave_id()] = acc;
+}
+
 // TAB: routed experts through the expert table (a.toff)
 template <int WB, int CPT, int RPS, int TT, bool TAB = false>
 __global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, const ChunkCfg cc, const PlanDims pd)
@@ -845,6 +909,13 @@ __global__ __launch_bounds__(kSwThreads) void k_gate_up_sw(const GemvArgs a, con
     const int tiles = a.I / 32;
     if constexpr (TT == 1) {
         if (a.inline_route) {
+            if constexpr (!TAB) {
+                // the workgroups past the layer's own run the router lookahead
+                if ((int)blockIdx.x >= pd.S * tiles) {
+                    gate_up_lookahead<WB>(a, (int)blockIdx.x - pd.S * tiles);
+                    return;
+                }
+            }
             gate_up_sw_routed_here<WB, CPT, RPS, TAB>(a, pd, tiles, s_h, part);
             return;
         }
@@ -1146,10 +1217,18 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     }
 }
 
+// lookahead workgroups of a launch: la_wgs per predicted rank, and per
+// shared expert of the next layer (one-token launches that route inline)
+static int lookahead_wgs(const GemvArgs &a)
+{
+    if (!a.la_logits || a.la_wgs <= 0 || !a.inline_route || a.toff) return 0;
+    return a.la_wgs * (a.rc.k + (a.la_shared.gate ? 1 : 0));
+}
+
 template <int WB, int CPT, int RPS, int TT, bool TAB = false>
 static int run_gate_up_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
-    k_gate_up_sw<WB, CPT, RPS, TT, TAB><<<pd.S * (a.I / 32), kSwThreads, 0, st>>>(a, cc, pd);
+    k_gate_up_sw<WB, CPT, RPS, TT, TAB><<<pd.S * (a.I / 32) + lookahead_wgs(a), kSwThreads, 0, st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
 

@@ -151,7 +151,9 @@ GemvWs gemv_ws(const moe_shape_t &s, int T, int Tc, bool single);
 // Router logits (and the quantised x) of T <= kGemvMaxT tokens; with
 // ng != nullptr the input is RMSNorm(x) with weight ng, formed in the launch.
 int launch_router_logits(const float *x, int T, int H, const float *gate_w, int E, double *logits,
-                         int8_t *xq, float *xd, const float *ng, double eps, hipStream_t st);
+                         int8_t *xq, float *xd, const float *ng, double eps, hipStream_t st,
+                         const float *la_gate_w = nullptr, const float *la_ng = nullptr,
+                         double *la_logits = nullptr);
 // whether the router launch can normalise its own input for this row width
 inline bool router_norms_input(const float *x, const float *ng, int H)
 {
@@ -206,7 +208,19 @@ struct GemvArgs {
     const int64_t *toff;
     // per-expert selection counts, incremented by the routing (or nullptr)
     uint32_t *counts;
+    // router lookahead (one token routed inside the gate/up launch): the
+    // next layer's logits (computed by this layer's router launch), its
+    // correction bias and experts; la_wgs workgroups per prefetched expert
+    // (the k ranks the next layer's router predicts, then its shared
+    // expert) stream their share of its weights so that they are in the
+    // memory-side cache when that layer runs; 0 = no lookahead
+    const double *la_logits;
+    const float *la_bias;
+    moe_weights_t la_routed, la_shared;
+    int la_wgs;
+    uint32_t *la_sink;  // one word per lookahead workgroup (the loaded data's XOR; keeps the loads)
 };
+constexpr int kLookaheadSinkWords = 4;  // la_sink words per lookahead workgroup (>= its waves)
 // Whether a T-token call of this shape routes inside the gate/up launch
 // (one token, row-sweep gate/up kernel) instead of in a plan launch.
 // Whether the expert-table (tiered) GEMV kernels take this shape: int4

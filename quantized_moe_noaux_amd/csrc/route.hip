@@ -34,17 +34,26 @@ bool route_cfg(const moe_shape_t &s, RouteCfg &rc)
 // token, the same arithmetic as the RMSNorm kernel, so the values equal that
 // kernel's output) and the normalised row never goes through memory.  The
 // host only passes ng for H <= 8192, H % 4 == 0 and 16-byte aligned x, ng.
+// With la_logits != nullptr (router lookahead of a decode stack), blocks
+// E .. 2E-1 compute the next layer's logits the same way on the same x, with
+// that layer's router weights la_gate_w and norm weight la_ng.
 __global__ __launch_bounds__(256) void k_router_logits_small(
-    const float *__restrict__ x, int T, int H, const float *__restrict__ gate_w, int E,
-    double *__restrict__ logits, int8_t *__restrict__ xq, float *__restrict__ xd,
-    const float *__restrict__ ng, double eps)
+    const float *__restrict__ x, int T, int H, const float *__restrict__ gate_w_l, int E,
+    double *__restrict__ logits_l, int8_t *__restrict__ xq, float *__restrict__ xd,
+    const float *__restrict__ ng_l, double eps, const float *__restrict__ la_gate_w,
+    const float *__restrict__ la_ng, double *__restrict__ la_logits)
 {
     __shared__ double red[4][kGemvMaxT];
     __shared__ double nred[kGemvMaxT][4];
     const int tid = threadIdx.x;
     const int n4 = H / 4;
-    if ((int)blockIdx.x < E) {
-        const int e = blockIdx.x;
+    const int nlog = la_logits ? 2 * E : E;  // logit blocks
+    if ((int)blockIdx.x < nlog) {
+        const bool la = (int)blockIdx.x >= E;
+        const int e = la ? (int)blockIdx.x - E : (int)blockIdx.x;
+        const float *gate_w = la ? la_gate_w : gate_w_l;
+        const float *ng = la ? la_ng : ng_l;
+        double *logits = la ? la_logits : logits_l;
         double acc[kGemvMaxT];
 #pragma unroll
         for (int t = 0; t < kGemvMaxT; t++) acc[t] = 0.0;
@@ -109,14 +118,15 @@ __global__ __launch_bounds__(256) void k_router_logits_small(
         return;
     }
     // quantiser part: 8 lanes per block of 32
+    const float *ng = ng_l;
     const int nb = H / 32;
-    const int g = ((int)blockIdx.x - E) * 256 + tid;
+    const int g = ((int)blockIdx.x - nlog) * 256 + tid;
     const int b = g >> 3, sub = g & 7;
     const bool live = b < T * nb;
     float4 v = live ? reinterpret_cast<const float4 *>(x + (size_t)b * 32)[sub] : make_float4(0, 0, 0, 0);
     if (ng) {
         // the tokens this block's 32 blocks of 32 fall in (block-uniform bounds)
-        const int b0 = ((int)blockIdx.x - E) * 32;
+        const int b0 = ((int)blockIdx.x - nlog) * 32;
         const int b1 = min(b0 + 31, T * nb - 1);
         double r = 0.0;
         for (int t = b0 / nb; t <= b1 / nb; t++) {
@@ -136,11 +146,16 @@ __global__ __launch_bounds__(256) void k_router_logits_small(
 }
 
 int launch_router_logits(const float *x, int T, int H, const float *gate_w, int E, double *logits,
-                         int8_t *xq, float *xd, const float *ng, double eps, hipStream_t st)
+                         int8_t *xq, float *xd, const float *ng, double eps, hipStream_t st,
+                         const float *la_gate_w, const float *la_ng, double *la_logits)
 {
     if (ng && !router_norms_input(x, ng, H)) return (int)hipErrorInvalidValue;
+    if (la_logits && (!la_gate_w || !la_ng || !ng || !router_norms_input(x, la_ng, H)))
+        return (int)hipErrorInvalidValue;
     const int qblocks = xq ? (T * (H / 32) * 8 + 255) / 256 : 0;
-    k_router_logits_small<<<E + qblocks, 256, 0, st>>>(x, T, H, gate_w, E, logits, xq, xd, ng, eps);
+    const int nlog = la_logits ? 2 * E : E;
+    k_router_logits_small<<<nlog + qblocks, 256, 0, st>>>(x, T, H, gate_w, E, logits, xq, xd, ng, eps, la_gate_w,
+                                                          la_ng, la_logits);
     return (int)hipGetLastError();
 }
 

@@ -19,6 +19,13 @@ MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_GROUPED, MOE_ACCUMULATE = 0, 1, 2, 4
 
 
+def MOE_LOOKAHEAD(n):
+    """moe_stack_forward: router lookahead with n workgroups per prefetched expert."""
+    if not 0 <= n <= 63:
+        raise ValueError("lookahead workgroups must be in 0 .. 63")
+    return n << 16
+
+
 def MOE_STAGE(n):
     return 1 << (8 + n)
 

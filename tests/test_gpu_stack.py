@@ -178,3 +178,69 @@ def test_stack_stages_one_by_one(dev, m, stack):
         m.moe_stack_forward(sh, x, arr, EPS, ws, flags=m.MOE_STAGE(s))
     torch.cuda.synchronize()
     assert torch.equal(x, ref)
+
+
+@pytest.mark.parametrize("wgs", [1, 8, 32])
+def test_stack_lookahead_identical(dev, m, stack, wgs):
+    """The router lookahead only prefetches: with it on, every layer's
+    routing and the final residual are bit-identical to the stack without
+    it, through eager runs and a replayed graph capture."""
+    wl, hosts, layers = stack
+    sh = m.shape_of(wl)
+    x0 = to_dev(hosts[0].x, dev)
+    ref, idx_r, w_r = run_stack(m, wl, layers, x0, dev)
+    arr = m.layers(layers)
+    flags = m.MOE_LOOKAHEAD(wgs)
+    ws = m.workspace(m.moe_stack_workspace_bytes(sh, 1, flags), dev)
+    assert m.moe_stack_workspace_bytes(sh, 1, flags) > m.moe_stack_workspace_bytes(sh, 1)
+    x = x0.clone()
+    idx = torch.empty((wl.layers, 1, wl.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((wl.layers, 1, wl.top_k), dtype=torch.float32, device=dev)
+    m.moe_stack_forward(sh, x, arr, EPS, ws, idx, w, flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    assert np.array_equal(w.cpu().numpy(), w_r)
+    assert torch.equal(x, ref)
+    x_static = x0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        m.moe_stack_forward(sh, x_static, arr, EPS, ws, flags=flags)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        x_static.copy_(x0)
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (x0 * 2).sum().item()
+        assert torch.equal(x_static, ref), "lookahead graph replay %d" % rep
+
+
+def test_stack_lookahead_prediction(dev, m, stack, chain):
+    """The logits the lookahead predicts with: after a stack call the
+    workspace holds those of the last prediction, layer L-1's router on the
+    normalised residual before layer L-2.  Their sigmoid must match the
+    oracle's router scores on the oracle's RMSNorm of the GPU's own residual
+    there (the two norms agree to a few fp32 ulps, hence the tolerance).
+    The recall of the prediction (the predicted top-k among the experts the
+    next layer then selects) along the oracle chain is printed."""
+    wl, hosts, layers = stack
+    sh = m.shape_of(wl)
+    flags = m.MOE_LOOKAHEAD(8)
+    ws = m.workspace(m.moe_stack_workspace_bytes(sh, 1, flags), dev)
+    x = to_dev(hosts[0].x, dev)
+    m.moe_stack_forward(sh, x, m.layers(layers), EPS, ws, flags=flags)
+    torch.cuda.synchronize()
+    nb = (4 * wl.hidden + 255) // 256 * 256
+    logits = ws[nb:nb + 8 * wl.n_experts].view(torch.float64).cpu().numpy()
+    L = wl.layers
+    xp, _, _ = run_stack(m, wl, layers[:L - 2], to_dev(hosts[0].x, dev), dev)
+    n = oracle.rmsnorm(xp.cpu().numpy(), np.ones(wl.hidden, np.float32), EPS)
+    s, _ = oracle.router_scores(sh, n[0], hosts[L - 1].gate_w, hosts[L - 1].bias)
+    np.testing.assert_allclose(1.0 / (1.0 + np.exp(-logits)), s, rtol=0, atol=1e-6)
+    hits = 0
+    for l in range(L - 1):
+        pred, _ = oracle.route(sh, chain[l]["n"], hosts[l + 1].gate_w, hosts[l + 1].bias)
+        hits += len(set(pred[0].tolist()) & set(chain[l + 1]["idx"][0].tolist()))
+    print("lookahead recall along the chain: %.1f%% of %d selections" %
+          (100.0 * hits / ((L - 1) * wl.top_k), (L - 1) * wl.top_k))
