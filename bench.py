@@ -179,6 +179,36 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 10}), flush=True)
 
 
+def stream_ceiling():
+    """The read bandwidth a plain stream reaches on this GPU, with the
+    decode kernels' load pattern (moe_stream_read): 1 GiB, four times the
+    memory-side cache, read 20 times back to back; and a 128 MiB region,
+    which the memory-side cache can hold, read 20 times back to back."""
+    import torch
+    from quantized_moe_noaux_amd import moe
+    dev = "cuda:0"
+    sink = torch.empty(moe.MOE_STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+    big = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    region = big[: (128 << 20) // 4]
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, buf in (("hbm_1GiB", big), ("region_128MiB", region)):
+        for _ in range(3):
+            moe.moe_stream_read(buf, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            moe.moe_stream_read(buf, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbps = 20 * buf.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        out[name + "_GBps"] = gbps
+        log("bench: stream read %s: %.0f GB/s = %.1f%% of %d GB/s" % (name, gbps, 100 * gbps / HBM_PEAK_GBS,
+                                                                     HBM_PEAK_GBS))
+    out["hbm_frac_of_peak"] = out["hbm_1GiB_GBps"] / HBM_PEAK_GBS
+    print(json.dumps(out), flush=True)
+
+
 # ---------------------------------------------------------------- the layer benchmark
 def main():
     ap = argparse.ArgumentParser()
@@ -206,6 +236,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="measure the plain streaming-read bandwidth (the HBM kernels' practical ceiling)")
     ap.add_argument("--write-traffic", action="store_true")
     ap.add_argument("--kernel", default="gate_up_swiglu_quant")
     ap.add_argument("--pmc-fetch")
@@ -222,6 +254,8 @@ def main():
         return write_traffic(args)
     if args.copy_calibration:
         return copy_calibration()
+    if args.stream_ceiling:
+        return stream_ceiling()
 
     import numpy as np
     import torch

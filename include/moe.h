@@ -162,6 +162,18 @@ int moe_quant_act(const float *x, int32_t T, int32_t D, int8_t *q, float *d, hip
 int moe_block_dots(int32_t wbits, const uint8_t *codes, int32_t rows, int32_t D,
                    const int8_t *q, int32_t T, int32_t *out, hipStream_t stream);
 
+/* moe_stream_read -- a measurement aid: the practical read bandwidth
+ * that every HBM-bound kernel here is judged against.  Reads `bytes` bytes
+ * at src (16-byte aligned, bytes a multiple of 16) once, as the weight
+ * streams of the decode kernels do (16-byte non-temporal loads, 8 in flight
+ * per thread, every load instruction of a workgroup reading one contiguous
+ * window), in a grid of MOE_STREAM_SINK_WORDS threads; thread i writes the
+ * XOR of the 32-bit words it read to sink[i], so the XOR of all of sink is
+ * the XOR of all words of the buffer.  sink: MOE_STREAM_SINK_WORDS uint32
+ * (device).  bytes = 0 is a no-op; other misuse gives MOE_EINVAL. */
+#define MOE_STREAM_SINK_WORDS (2048u * 256u)
+int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* ---------------------------------------------------------------- experts */
 /* moe_expert_ffn -- one SwiGLU expert on quantised activations, unweighted:
  *   g = W_gate x, u = W_up x, h = silu(g) * u, (qh, dh) = quant(h),

@@ -177,6 +177,14 @@ int moe_quant_act(const float *x, int32_t T, int32_t D, int8_t *q, float *d, hip
     return hip_rc(launch_quant(x, T, D, q, d, stream));
 }
 
+int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream)
+{
+    if (bytes % 16) return MOE_EINVAL;
+    if (bytes == 0) return MOE_OK;
+    if (!src || !sink || !al(src, 16) || !al(sink, 4)) return MOE_EINVAL;
+    return hip_rc(launch_stream_read(src, bytes, sink, stream));
+}
+
 int moe_block_dots(int32_t wbits, const uint8_t *codes, int32_t rows, int32_t D, const int8_t *q, int32_t T,
                    int32_t *out, hipStream_t stream)
 {

@@ -101,6 +101,41 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t *__restrict__ 
     }
 }
 
+// ---------------------------------------------------------------- streaming read (measurement aid)
+// Thread i of the grid reads 16-byte chunks i, i + n, i + 2n, ... (n = the
+// grid's thread count) eight at a time, so that a workgroup's load
+// instruction covers one contiguous 4 KB window, with the non-temporal hint
+// of the decode kernels' weight loads; the data only feeds an XOR.
+constexpr int kStreamBlocks = 2048, kStreamThreads = 256, kStreamUnroll = 8;
+__global__ __launch_bounds__(kStreamThreads) void k_stream_read(const uint4 *__restrict__ p, size_t n16,
+                                                                uint32_t *__restrict__ sink)
+{
+    typedef unsigned v4u_s __attribute__((ext_vector_type(4)));
+    const v4u_s *q = reinterpret_cast<const v4u_s *>(p);
+    const size_t nthr = (size_t)kStreamBlocks * kStreamThreads;
+    size_t i = (size_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kStreamUnroll - 1) * nthr < n16; i += kStreamUnroll * nthr) {
+        v4u_s v[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; u++) v[u] = __builtin_nontemporal_load(q + i + u * nthr);
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += nthr) {
+        const v4u_s v = __builtin_nontemporal_load(q + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    sink[(size_t)blockIdx.x * kStreamThreads + threadIdx.x] = acc;
+}
+
+int launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st)
+{
+    static_assert((size_t)kStreamBlocks * kStreamThreads == MOE_STREAM_SINK_WORDS, "sink size");
+    k_stream_read<<<kStreamBlocks, kStreamThreads, 0, st>>>(static_cast<const uint4 *>(src), bytes / 16, sink);
+    return (int)hipGetLastError();
+}
+
 int launch_block_dots(int wbits, const uint8_t *codes, int rows, int D, const int8_t *q, int T,
                       int32_t *out, hipStream_t st)
 {

@@ -277,6 +277,7 @@ int launch_gg_down(const GgArgs &a, int max_tiles, hipStream_t st);
 int launch_gg_combine(const GgArgs &a, hipStream_t st);
 
 int launch_rmsnorm(const float *x, const float *g, double eps, int T, int H, float *out, hipStream_t st);
+int launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 int launch_block_dots(int wbits, const uint8_t *codes, int rows, int D, const int8_t *q, int T,
                       int32_t *out, hipStream_t st);
 // Stable counting sort of the T*k assignments by expert.  With tiles != null

@@ -73,6 +73,7 @@ def _load():
         "moe_route_workspace_bytes": (sz, [P(moe_shape_t), i32]),
         "moe_quant_act": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
         "moe_block_dots": (ctypes.c_int, [i32, vp, i32, i32, vp, i32, vp, vp]),
+        "moe_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
         "moe_expert_ffn": (ctypes.c_int, [P(moe_shape_t), P(moe_weights_t), i32, vp, vp, i32, vp, vp, sz, vp]),
         "moe_layer_forward": (ctypes.c_int, [P(moe_shape_t), vp, i32, vp, vp, P(moe_weights_t),
                                              P(moe_weights_t), vp, vp, vp, u32, vp, sz, vp]),
@@ -172,6 +173,18 @@ def moe_quant_act(x, q, d, stream=None):
     T, D = x.shape
     _chk("moe_quant_act", lib.moe_quant_act(_ptr(x, torch.float32), T, D, _ptr(q, torch.int8),
                                             _ptr(d, torch.float32), _stream(stream)))
+
+
+MOE_STREAM_SINK_WORDS = 2048 * 256
+
+
+def moe_stream_read(src, sink, stream=None):
+    """Reads every byte of the device tensor src once (measurement aid);
+    sink: MOE_STREAM_SINK_WORDS int32 words of XORs."""
+    if sink.numel() < MOE_STREAM_SINK_WORDS:
+        raise ValueError("sink needs %d words" % MOE_STREAM_SINK_WORDS)
+    _chk("moe_stream_read", lib.moe_stream_read(_ptr(src), src.numel() * src.element_size(),
+                                                _ptr(sink, torch.int32), _stream(stream)))
 
 
 def moe_block_dots(wbits, codes, D, q, out, stream=None):
