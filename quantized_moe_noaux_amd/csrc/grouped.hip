@@ -39,9 +39,11 @@
 // Work order.  The 1-D grid is dealt round-robin over the 8 XCDs (each with
 // its own L2).  XCD x takes the channel groups [x cpx, (x+1) cpx) of every
 // tile, and its workgroups walk tile by tile with a tile's channel groups
-// back to back: a tile's activation rows are fetched once per XCD, and the
-// tiles of one expert, running at the same time, share each weight slice in
-// that XCD's L2.
+// back to back, so a tile's activation rows are fetched once per XCD and the
+// tiles of one expert run at about the same time on the same XCD.  (The
+// L2-to-fabric counters show those tiles re-fetching most of their weight
+// slices rather than sharing them: the kernels are bound by the VALU, not
+// by this traffic, and an expert-contiguous order measured slower.)
 #include "moe_dev.h"
 #include "moe_internal.h"
 

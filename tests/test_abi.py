@@ -178,3 +178,27 @@ def test_mtp_accept_argument_checks(m):
     assert L.moe_mtp_accept(2, 4, 100, D_, P + 2, Q, 0.7, U, N, X, WS, need, None) == m.MOE_EINVAL  # misaligned
     assert L.moe_mtp_accept(2, 4, 320000, D_, P, Q, 0.7, U, N, X, WS, need - 1, None) == m.MOE_EWORKSPACE
     assert L.moe_mtp_accept(0, 4, 100, None, None, None, 0.7, None, None, None, None, 0, None) == m.MOE_OK
+
+
+def test_stack_lookahead_workspace_and_flag(m):
+    """MOE_LOOKAHEAD(n) adds the predicted logits (E fp64) and one sink word
+    per wave of the n (k + 1) lookahead workgroups (4 words each), each part
+    256-byte aligned; the helper refuses n outside 0 .. 63."""
+    sh = big_shape(m)
+    base = m.moe_stack_workspace_bytes(sh, 1)
+    for n in (1, 8, 32, 63):
+        got = m.moe_stack_workspace_bytes(sh, 1, m.MOE_LOOKAHEAD(n))
+        sink = 4 * 4 * n * (8 + 1)
+        assert got == base + 256 * 8 + (sink + 255) // 256 * 256
+    assert m.moe_stack_workspace_bytes(sh, 1, m.MOE_LOOKAHEAD(0)) == base
+    for bad in (-1, 64):
+        with pytest.raises(ValueError):
+            m.MOE_LOOKAHEAD(bad)
+
+
+def test_stream_read_rejects_misuse_before_any_launch(m):
+    f = m.lib.moe_stream_read
+    assert f(None, 16, None, None) == m.MOE_EINVAL
+    assert f(ctypes.c_void_p(16), 20, ctypes.c_void_p(16), None) == m.MOE_EINVAL   # not a multiple of 16
+    assert f(ctypes.c_void_p(20), 16, ctypes.c_void_p(16), None) == m.MOE_EINVAL   # misaligned source
+    assert f(None, 0, None, None) == m.MOE_OK                                       # nothing to read
