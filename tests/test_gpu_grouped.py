@@ -200,3 +200,23 @@ def test_grouped_top_p(dev, m, wbits, T, p):
     assert_close(y.cpu().numpy(), y_ref)
     yg, idxg, _ = forward(m, L, m.MOE_PATH_GEMV, T)
     assert np.array_equal(idxg, idx)
+
+
+# ---------------------------------------------------------------- full-size int8 and int2
+@pytest.mark.parametrize("name,T", [("verify_int8", 16), ("stack_int2", 64)])
+def test_full_size_int8_int2_both_paths(dev, m, name, T):
+    """The grouped GEMMs' int8 (weights copied into LDS as they are) and
+    int2 (four 2-bit fields expanded per byte) forms at the full H = 6144,
+    I = 2048, next to the int4 cases above: T independent tokens of the
+    verify_int8 layer and of layer 0 of the int2 stack, on the grouped and
+    the GEMV path, each against the oracle (routing bit-exact)."""
+    wl = synth.workload(name)
+    L = DevLayer(wl, dev, T=T)
+    print("full-size grouped parity: %s T=%d" % (name, T), flush=True)
+    yg, ig, wg = forward(m, L, m.MOE_PATH_GROUPED, T)
+    yv, iv, wv = forward(m, L, m.MOE_PATH_GEMV, T)
+    y_ref, idx_ref, w_ref = reference(L, np.arange(T))
+    assert np.array_equal(ig, idx_ref) and np.array_equal(iv, idx_ref)
+    np.testing.assert_allclose(wg, w_ref, rtol=1e-6)
+    assert_close(yg.cpu().numpy(), y_ref, what="grouped")
+    assert_close(yv.cpu().numpy(), y_ref, what="gemv")
