@@ -244,3 +244,48 @@ def test_stack_lookahead_prediction(dev, m, stack, chain):
         hits += len(set(pred[0].tolist()) & set(chain[l + 1]["idx"][0].tolist()))
     print("lookahead recall along the chain: %.1f%% of %d selections" %
           (100.0 * hits / ((L - 1) * wl.top_k), (L - 1) * wl.top_k))
+
+
+@pytest.mark.parametrize("H", [8192, 8448])
+def test_stack_norm_paths_at_the_width_limit(dev, m, H):
+    """The router launch forms RMSNorm(x) itself up to H = 8192; above, the
+    stack runs a separate RMSNorm launch.  A 3-layer stack of 2 tokens with
+    non-unit norm weights at H = 8192 (fused) and H = 8448 (separate): equal,
+    bit for bit, to moe_rmsnorm + moe_layer_forward launches adding into the
+    residual, with every layer's routing equal to the oracle chain's and the
+    final residual within tolerance of it."""
+    import types
+    wl = synth.workload("tiny", hidden=H, layers=3, T=2)
+    hosts, base = synth.device_stack(wl, dev)
+    rng = np.random.default_rng(H)
+    gs = [(1.0 + 0.1 * rng.standard_normal(H)).astype(np.float32) for _ in range(wl.layers)]
+    layers = [types.SimpleNamespace(gate_w=L.gate_w, bias=L.bias, norm_g=to_dev(g, dev), routed=L.routed,
+                                    shared=L.shared) for L, g in zip(base, gs)]
+    sh = m.shape_of(wl)
+    T = wl.T
+    x0 = to_dev(hosts[0].x, dev)
+    x = x0.clone()
+    idx = torch.empty((wl.layers, T, wl.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((wl.layers, T, wl.top_k), dtype=torch.float32, device=dev)
+    ws = m.workspace(m.moe_stack_workspace_bytes(sh, T), dev)
+    m.moe_stack_forward(sh, x, m.layers(layers), EPS, ws, idx, w)
+    xm = x0.clone()
+    n = torch.empty_like(xm)
+    lws = m.workspace(m.moe_workspace_bytes(sh, T), dev)
+    im = torch.empty_like(idx)
+    wm = torch.empty_like(w)
+    for l, L in enumerate(layers):
+        m.moe_rmsnorm(xm, L.norm_g, EPS, n)
+        m.moe_layer_forward(sh, n, L.gate_w, L.bias, L.routed, L.shared, xm, lws, im[l], wm[l],
+                            flags=m.MOE_ACCUMULATE)
+    torch.cuda.synchronize()
+    assert torch.equal(x, xm) and torch.equal(idx, im) and torch.equal(w, wm)
+    osh = oracle.shape_of(wl)
+    xr = hosts[0].x.copy()
+    for l, Hl in enumerate(hosts):
+        nr = oracle.rmsnorm(xr, gs[l], EPS)
+        ir, _ = oracle.route(osh, nr, Hl.gate_w, Hl.bias)
+        assert np.array_equal(idx[l].cpu().numpy(), ir), "layer %d routing" % l
+        yr, _, _ = oracle.layer_forward(osh, nr, Hl.gate_w, Hl.bias, oracle.layer_experts(Hl, ir), Hl.shared)
+        xr = (xr + yr).astype(np.float32)
+    assert_close(x.cpu().numpy(), xr, what="final residual at H=%d" % H)
