@@ -102,9 +102,9 @@ const char *moe_strerror(int code);
  * selected expert's rows streamed once per chunk and dotted against every
  * token of the chunk routed to it (HBM-bound decode and verify batches).
  * GROUPED: the T*k (token, expert) assignments are sorted by expert (as
- * moe_permute) and each expert's rows run as int8 MFMA GEMMs in tiles of 64
- * assignments, with a separate fixed-order combine (prefill); it takes
- * shapes with H a multiple of 128 and I a multiple of 64 and returns
+ * moe_permute) and each expert's rows run as int8 MFMA GEMMs in tiles of
+ * 128 assignments, with a separate fixed-order combine (prefill); it takes
+ * shapes with H a multiple of 256 and I a multiple of 128 and returns
  * MOE_EUNSUPPORTED otherwise.  AUTO: GEMV up to 8 tokens, GROUPED above
  * when the shape allows it, else GEMV.  Both paths give the same routing
  * bit for bit; their float outputs differ only by rounding order. */
