@@ -54,7 +54,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kGgThreads = 1024;
+constexpr int kGgThreads = 512;
 constexpr int kGgWRows = 256;  // weight rows staged per workgroup
 
 GgWs gg_ws(const moe_shape_t &s, int T)
@@ -150,12 +150,16 @@ int launch_gg_quant(const float *x, int T, int D, int wbits, int8_t *q, float *d
 
 // ---------------------------------------------------------------- tiling
 // A workgroup of 512 threads (8 waves) owns 128 activation rows (one tile)
-// and 256 weight rows.  Per pipeline step it stages K = 128 codes of both in
+// and 256 weight rows.  Per pipeline step it stages K = 64 codes of both in
 // LDS as int8 MFMA operands: the activation rows as stored (code order),
 // the weight rows expanded from their packed codes to the 16c / 64c form
 // (int4 / int2; int8 as stored), so that a wave reads every MFMA operand
-// with one ds_read_b128 and no further VALU work.
-constexpr int kGgKS = 128;               // K codes per step
+// with one ds_read_b128 and no further VALU work.  A workgroup takes 63 KB
+// of LDS and (int4, int2) at most 128 VGPRs per lane, so two fit on a CU:
+// one's prologue, epilogue and barrier waits overlap the other's MFMAs and
+// rescale.  (The int8 form stages twice the weight chunks per thread and
+// keeps one workgroup per CU rather than spill.)
+constexpr int kGgKS = 64;                // K codes per step
 constexpr int kGgNBS = kGgKS / 32;       // activation blocks per step
 constexpr int kGgRowBytes = kGgKS;       // LDS bytes of a staged row per step (int8 operands)
 constexpr int kGgCPR = kGgRowBytes / 16; // 16-byte chunks per staged row
@@ -170,7 +174,7 @@ template <int WB> struct GgCfg {
 static_assert(kGgTN * kGgCPR == kGgThreads, "one activation chunk per thread per step");
 static_assert(kGgTN * kGgNBS <= kGgThreads, "one activation scale per thread per step");
 
-// Chunk c of staged row r.  Rows are padded to 144 bytes (36 banks): the 16
+// Chunk c of staged row r.  Rows are padded to 80 bytes (20 banks): the 16
 // lanes a ds_read_b128 serves at once read rows r .. r+15 at one chunk, and
 // these start on 16 distinct 4-bank groups; a fragment's address is one
 // base per row plus an immediate offset per block.
@@ -194,6 +198,13 @@ __device__ __forceinline__ v4i lds16(const uint8_t *p) { return *reinterpret_cas
 // orders all memory accesses around it: everything that produces them is
 // issued before it, and no later load is issued ahead of it.
 __device__ __forceinline__ void pin_after(v16f &a, v16f &b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
+
+// Waves and weight tiles: wave w takes the 32 tile rows 32 (w / kGgCW) ..
+// and kGgWT weight tiles of 32 rows (wr[0 .. kGgWT-1] in the staged 256).
+constexpr int kGgWaves = kGgThreads / 64;
+constexpr int kGgCW = kGgWaves / (kGgTN / 32);  // waves per 32-row group
+constexpr int kGgWT = kGgWRows / 32 / kGgCW;    // weight tiles per wave
+static_assert(kGgCW * (kGgTN / 32) == kGgWaves && kGgWT % 2 == 0, "wave tiling");
 
 // Packed codes of one 16-byte chunk -> its MFMA operand chunks in LDS.
 //   int4: the chunk is one block of 32 codes; operand chunk 2b (lanes 0-31)
@@ -233,7 +244,7 @@ __device__ __forceinline__ void gg_stage_w(uint8_t *wbuf, int r, int pc, const v
 }
 
 // Staging registers of one pipeline step: the thread's packed weight
-// chunks, its activation chunk and (threads below 512) one activation scale.
+// chunks, its activation chunk and (threads below 256) one activation scale.
 template <int WB> struct GgRegs {
     v4u w[GgCfg<WB>::WLD], a;
     float d;
@@ -243,32 +254,32 @@ template <int WB> struct GgRegs {
 // rows 0..255 after w0 (GU = false), or rows 0..127 after w0 and 0..127
 // after w1 (GU = true: gate then up), each of wrb bytes; its 128 activation
 // rows start at aq + L.arow[i] * K (codes in code order), their scales at
-// ad + L.arow[i] * (K/32).  Wave w computes the 32 tile rows 32 (w >> 2) ..
-// (LIVE: some of them are live; uniform in the wave) against the weight
-// rows wr[wt] + (lane % 32) of its two 32-row weight tiles.  acc[wt] comes
+// ad + L.arow[i] * (K/32).  Wave w computes the 32 tile rows 32 (w / kGgCW)
+// .. (LIVE: some of them are live; uniform in the wave) against the weight
+// rows wr[wt] + (lane % 32) of its kGgWT 32-row weight tiles.  acc[wt] comes
 // back in MFMA layout: lane l, register v = weight row
 // 8 (v / 4) + 4 (l / 32) + v % 4 of weight tile wt, tile row
-// 32 (w >> 2) + l % 32.
+// 32 (w / kGgCW) + l % 32.
 //
 // Pipeline: two LDS buffers (one barrier per step).  At the start of step s
 // the loads of step s + 1 go out into the staging registers, the MFMAs of
 // step s run from LDS, then the registers are stored to the other buffer;
-// four waves per SIMD cover the load latency across waves.  Every staging
+// the waves of two workgroups per SIMD cover the load latency.  Every staging
 // register is indexed by compile-time constants, so it stays in a VGPR.
 template <int WB, bool GU, bool LIVE>
 __device__ __forceinline__ void gg_mainloop(GgLds &L, const uint8_t *w0, const uint8_t *w1, size_t wrb,
-                                            const int (&wr)[2], const int8_t *__restrict__ aq,
-                                            const float *__restrict__ ad, int K, v16f (&acc)[2])
+                                            const int (&wr)[kGgWT], const int8_t *__restrict__ aq,
+                                            const float *__restrict__ ad, int K, v16f (&acc)[kGgWT])
 {
     using C = GgCfg<WB>;
     const int tid = threadIdx.x, l = lane_id(), h = l >> 5;
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int nbk = K / 32, nsteps = K / kGgKS;
-    const int r0 = 32 * (w >> 2) + (l & 31);
+    const int r0 = 32 * (w / kGgCW) + (l & 31);
 
     // staging sources of this thread: packed weight chunks (id < WCH; for
     // int2 the upper half of the workgroup has none, a whole-wave split),
-    // one activation chunk, one scale (threads < 512: row t/4, block t%4)
+    // one activation chunk, one scale (threads < 256: row t/2, block t%2)
     const uint8_t *wp[C::WLD];
     int wrw[C::WLD], wpc[C::WLD];
 #pragma unroll
@@ -284,7 +295,7 @@ __device__ __forceinline__ void gg_mainloop(GgLds &L, const uint8_t *w0, const u
     const int8_t *ap = aq + (size_t)L.arow[ar] * K + 16 * ac;
     const int ao = ldsoff(ar, ac);
     const bool dl = tid < kGgTN * kGgNBS;
-    const int dr = (tid >> 2) & (kGgTN - 1), db = tid & 3;
+    const int dr = (tid / kGgNBS) & (kGgTN - 1), db = tid % kGgNBS;
     const float *dp = ad + (size_t)L.arow[dr] * nbk + db;
 
     // loads of step s (a step past the end reads the last one again: an L2
@@ -314,26 +325,29 @@ __device__ __forceinline__ void gg_mainloop(GgLds &L, const uint8_t *w0, const u
 #pragma unroll
             for (int b = 0; b < kGgNBS; b++) {
                 const int c = 2 * b + h;
-                const v4i a0 = lds16(wb + ldsoff(wr[0] + (l & 31), c));
-                const v4i a1 = lds16(wb + ldsoff(wr[1] + (l & 31), c));
                 const v4i b0 = lds16(abuf + ldsoff(r0, c));
                 const float d0 = L.d[buf][b][r0];
-                const v16i i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, zero, 0, 0, 0);
-                const v16i i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b0, zero, 0, 0, 0);
 #pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    acc[0][v] = fmaf((float)i0[v], d0, acc[0][v]);
-                    acc[1][v] = fmaf((float)i1[v], d0, acc[1][v]);
+                for (int t = 0; t < kGgWT; t += 2) {
+                    const v4i a0 = lds16(wb + ldsoff(wr[t] + (l & 31), c));
+                    const v4i a1 = lds16(wb + ldsoff(wr[t + 1] + (l & 31), c));
+                    const v16i i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, zero, 0, 0, 0);
+                    const v16i i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b0, zero, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        acc[t][v] = fmaf((float)i0[v], d0, acc[t][v]);
+                        acc[t + 1][v] = fmaf((float)i1[v], d0, acc[t + 1][v]);
+                    }
+                    // a pair of tiles' rescale completes before the next
+                    // pair's LDS reads and MFMAs are issued: two results
+                    // live at a time (4 waves per SIMD: 128 VGPRs)
+                    pin_after(acc[t], acc[t + 1]);
                 }
-                // the block's rescale completes before the next block's LDS
-                // reads and MFMAs are issued: one block's operands and
-                // results live at a time (4 waves per SIMD: 128 VGPRs)
-                pin_after(acc[0], acc[1]);
             }
         }
     };
 #pragma unroll
-    for (int wt = 0; wt < 2; wt++)
+    for (int wt = 0; wt < kGgWT; wt++)
 #pragma unroll
         for (int v = 0; v < 16; v++) acc[wt][v] = 0.f;
 
@@ -355,10 +369,10 @@ __device__ __forceinline__ void gg_mainloop(GgLds &L, const uint8_t *w0, const u
 // the main loop for this wave's 32 tile rows: MFMAs only if one of them is live
 template <int WB, bool GU>
 __device__ __forceinline__ void gg_mainloop_rows(GgLds &L, const uint8_t *w0, const uint8_t *w1, size_t wrb,
-                                                 const int (&wr)[2], const int8_t *aq, const float *ad, int K, int n,
-                                                 v16f (&acc)[2])
+                                                 const int (&wr)[kGgWT], const int8_t *aq, const float *ad, int K,
+                                                 int n, v16f (&acc)[kGgWT])
 {
-    const int rbase = 32 * (__builtin_amdgcn_readfirstlane(wave_id()) >> 2);
+    const int rbase = 32 * (__builtin_amdgcn_readfirstlane(wave_id()) / kGgCW);
     if (rbase < n) gg_mainloop<WB, GU, true>(L, w0, w1, wrb, wr, aq, ad, K, acc);
     else gg_mainloop<WB, GU, false>(L, w0, w1, wrb, wr, aq, ad, K, acc);
 }
@@ -382,10 +396,11 @@ __device__ __forceinline__ bool gg_item(const GgArgs &a, int ncg, int &tile, int
 }
 
 // ---------------------------------------------------------------- gate / up
-// Wave w: tile rows 32 (w >> 2) .. + 32 and intermediate channels
-// c0 + 32 (w & 3) .. + 32 (weight tile 0: their gate rows, 1: their up rows).
+// Wave w: tile rows 32 (w / kGgCW) .. + 32 and the intermediate channels
+// c0 + 64 (w % kGgCW) .. + 64: weight tiles 0, 1 are their gate rows, 2, 3
+// their up rows.
 template <int WB>
-__global__ __launch_bounds__(kGgThreads) void k_gg_gate_up(const GgArgs a)
+__global__ __launch_bounds__(kGgThreads, WB == 8 ? 3 : 4) void k_gg_gate_up(const GgArgs a)
 {
     __shared__ GgLds L;
     int tix, cg;
@@ -403,50 +418,55 @@ __global__ __launch_bounds__(kGgThreads) void k_gg_gate_up(const GgArgs a)
         L.arow[tid] = (r < a.Tk) ? a.perm[r] / a.k : r - a.Tk;
     }
     __syncthreads();
-    const int w = __builtin_amdgcn_readfirstlane(wave_id()), cw = w & 3;
-    const int wr[2] = {32 * cw, 128 + 32 * cw};
-    v16f acc[2];
+    static_assert(kGgWT == 4, "two gate and two up tiles per wave");
+    const int w = __builtin_amdgcn_readfirstlane(wave_id()), cw = w % kGgCW;
+    const int wr[kGgWT] = {64 * cw, 64 * cw + 32, 128 + 64 * cw, 128 + 64 * cw + 32};
+    v16f acc[kGgWT];
     gg_mainloop_rows<WB, true>(L, W.gate + (eo * I + c0) * rb, W.up + (eo * I + c0) * rb, rb, wr, a.xq, a.xd, H,
                                n, acc);
 
-    // epilogue: lane = (tile row i, channel half hf); 16 channels of the
-    // wave's 32-channel block; h quantised per block, gathered in LDS in
-    // natural order, then written out in code order
+    // epilogue: lane = (tile row i, channel half hf); per 32-channel block
+    // of the wave (gate tile t, up tile t + 2) 16 channels; h quantised per
+    // block, gathered in LDS in natural order, then written out in code order
     const int l = lane_id(), hf = l >> 5;
-    const int i = 32 * (w >> 2) + (l & 31);
-    uint8_t *qs = &L.a[0][0];  // [128 rows][128 channels] over the activation buffers (36 KB), free now
-    const int cl = 32 * cw;    // the block's first channel within the workgroup's 128
-    const float *gs = W.gate_s + eo * I + c0 + cl, *us = W.up_s + eo * I + c0 + cl;
+    const int i = 32 * (w / kGgCW) + (l & 31);
+    uint8_t *qs = &L.a[0][0];  // [128 rows][128 channels] over the activation buffers (20 KB), free now
     constexpr float inv = GgCfg<WB>::kInv;
-    float hv[16];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const float4 g4 = *reinterpret_cast<const float4 *>(gs + 8 * j + 4 * hf);
-        const float4 u4 = *reinterpret_cast<const float4 *>(us + 8 * j + 4 * hf);
-        const float gsc[4] = {g4.x, g4.y, g4.z, g4.w}, usc[4] = {u4.x, u4.y, u4.z, u4.w};
+    for (int t = 0; t < 2; t++) {
+        const int cl = 64 * cw + 32 * t;  // the block's first channel within the workgroup's 128
+        const float *gs = W.gate_s + eo * I + c0 + cl, *us = W.up_s + eo * I + c0 + cl;
+        float hv[16];
 #pragma unroll
-        for (int m = 0; m < 4; m++)
-            hv[4 * j + m] = silu_mul((gsc[m] * inv) * acc[0][4 * j + m], (usc[m] * inv) * acc[1][4 * j + m]);
-    }
-    // Q8_0 quantisation of h over the block of 32 channels (this lane's 16
-    // and lane l^32's 16)
-    float amax = 0.f;
+        for (int j = 0; j < 4; j++) {
+            const float4 g4 = *reinterpret_cast<const float4 *>(gs + 8 * j + 4 * hf);
+            const float4 u4 = *reinterpret_cast<const float4 *>(us + 8 * j + 4 * hf);
+            const float gsc[4] = {g4.x, g4.y, g4.z, g4.w}, usc[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
-    for (int v = 0; v < 16; v++) amax = fmaxf(amax, fabsf(hv[v]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float dq = amax / 127.0f;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        uint32_t wq = 0;
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-            float r = (dq == 0.0f) ? 0.0f : rintf(hv[4 * j + m] / dq);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            wq |= ((uint32_t)(int)r & 0xFFu) << (8 * m);
+            for (int m = 0; m < 4; m++)
+                hv[4 * j + m] =
+                    silu_mul((gsc[m] * inv) * acc[t][4 * j + m], (usc[m] * inv) * acc[t + 2][4 * j + m]);
         }
-        *reinterpret_cast<uint32_t *>(qs + i * 128 + cl + 8 * j + 4 * hf) = wq;
+        // Q8_0 quantisation of h over the block of 32 channels (this lane's
+        // 16 and lane l^32's 16)
+        float amax = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; v++) amax = fmaxf(amax, fabsf(hv[v]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const float dq = amax / 127.0f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            uint32_t wq = 0;
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                float r = (dq == 0.0f) ? 0.0f : rintf(hv[4 * j + m] / dq);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                wq |= ((uint32_t)(int)r & 0xFFu) << (8 * m);
+            }
+            *reinterpret_cast<uint32_t *>(qs + i * 128 + cl + 8 * j + 4 * hf) = wq;
+        }
+        if (hf == 0 && i < n) a.dh[(size_t)(row0 + i) * (I / 32) + (c0 + cl) / 32] = dq;
     }
-    if (hf == 0 && i < n) a.dh[(size_t)(row0 + i) * (I / 32) + (c0 + cl) / 32] = dq;
     __syncthreads();
     // 128 rows x 4 blocks x 8 dwords, in code order
     for (int id = tid; id < kGgTN * 32; id += kGgThreads) {
@@ -458,10 +478,10 @@ __global__ __launch_bounds__(kGgThreads) void k_gg_gate_up(const GgArgs a)
 }
 
 // ---------------------------------------------------------------- down
-// Wave w: tile rows 32 (w >> 2) .. + 32 and hidden channels
-// n0 + 64 (w & 3) .. + 64 (two weight tiles of 32).
+// Wave w: tile rows 32 (w / kGgCW) .. + 32 and hidden channels
+// n0 + 128 (w % kGgCW) .. + 128 (four weight tiles of 32).
 template <int WB>
-__global__ __launch_bounds__(kGgThreads) void k_gg_down(const GgArgs a)
+__global__ __launch_bounds__(kGgThreads, WB == 8 ? 3 : 4) void k_gg_down(const GgArgs a)
 {
     __shared__ GgLds L;
     int tix, cg;
@@ -479,21 +499,23 @@ __global__ __launch_bounds__(kGgThreads) void k_gg_down(const GgArgs a)
         L.cw[tid] = (r < a.Tk) ? a.w[a.perm[r]] : 1.0f;
     }
     __syncthreads();
-    const int w = __builtin_amdgcn_readfirstlane(wave_id()), cw = w & 3;
-    const int wr[2] = {64 * cw, 64 * cw + 32};
-    v16f acc[2];
+    const int w = __builtin_amdgcn_readfirstlane(wave_id()), cw = w % kGgCW;
+    int wr[kGgWT];
+#pragma unroll
+    for (int t = 0; t < kGgWT; t++) wr[t] = 32 * (kGgWT * cw + t);
+    v16f acc[kGgWT];
     gg_mainloop_rows<WB, false>(L, W.down + (eo * H + n0) * rb, nullptr, rb, wr, a.qh, a.dh, I, n, acc);
 
     const int l = lane_id(), hf = l >> 5;
-    const int i = 32 * (w >> 2) + (l & 31);
+    const int i = 32 * (w / kGgCW) + (l & 31);
     if (i >= n) return;
     const float *ds = W.down_s + eo * H;
     constexpr float inv = GgCfg<WB>::kInv;
     const float cwt = L.cw[i];
     float *yrow = a.yrows + (size_t)(row0 + i) * H;
 #pragma unroll
-    for (int wt = 0; wt < 2; wt++) {
-        const int cbase = n0 + 64 * cw + 32 * wt + 4 * hf;
+    for (int wt = 0; wt < kGgWT; wt++) {
+        const int cbase = n0 + 32 * (kGgWT * cw + wt) + 4 * hf;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int ch = cbase + 8 * j;
