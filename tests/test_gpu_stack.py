@@ -289,3 +289,30 @@ def test_stack_norm_paths_at_the_width_limit(dev, m, H):
         yr, _, _ = oracle.layer_forward(osh, nr, Hl.gate_w, Hl.bias, oracle.layer_experts(Hl, ir), Hl.shared)
         xr = (xr + yr).astype(np.float32)
     assert_close(x.cpu().numpy(), xr, what="final residual at H=%d" % H)
+
+
+@pytest.mark.parametrize("top_p", [0.0, 0.7])
+def test_stack_lookahead_identical_with_top_p_and_batches(dev, m, stack, top_p):
+    """The lookahead fetches every predicted rank whatever the adaptive
+    top-p keeps, and is ignored for batches of more than one token: with
+    top-p 0.7 on one token, and for a batch of 3 tokens, the first 8 layers
+    give bit-identical routing and residuals with and without it."""
+    wl, hosts, layers = stack
+    sh = m.shape_of(synth.workload("stack_int2", top_p=top_p))
+    arr = m.layers(layers[:8])
+    for T in (1, 3):
+        x0 = torch.from_numpy(np.stack([synth.host_normals(50 + t, synth.stream_id(0, synth.X), wl.hidden, 1.0)
+                                        for t in range(T)])).to(dev)
+        outs = []
+        for flags in (0, m.MOE_LOOKAHEAD(8)):
+            ws = m.workspace(m.moe_stack_workspace_bytes(sh, T, flags), dev)
+            x = x0.clone()
+            idx = torch.empty((8, T, wl.top_k), dtype=torch.int32, device=dev)
+            w = torch.empty((8, T, wl.top_k), dtype=torch.float32, device=dev)
+            m.moe_stack_forward(sh, x, arr, EPS, ws, idx, w, flags=flags)
+            torch.cuda.synchronize()
+            outs.append((x, idx, w))
+        (xa, ia, wa), (xb, ib, wb) = outs
+        assert torch.equal(xa, xb) and torch.equal(ia, ib) and torch.equal(wa, wb), "T=%d top_p=%.1f" % (T, top_p)
+        if top_p:
+            assert (ia < 0).any(), "top-p dropped no slot"
