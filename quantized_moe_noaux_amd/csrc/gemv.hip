@@ -278,9 +278,12 @@ int launch_plan(const GemvArgs &a, hipStream_t st)
 }
 
 // ---------------------------------------------------------------- activations in LDS
-// Per token, the activation operand of every chunk position of a row, laid
-// out for act_from_lds: A [cpr][NA] dwords (already permuted for the weight
-// packing), D [blocks] scales, Q [blocks] block sums (int4 / int2 only).
+// Per token, the activation operand of every chunk position of a row (nch
+// positions), laid out for act_from_lds: A [NA / 4][nch] 16-byte pieces
+// (already permuted for the weight packing; piece i of consecutive
+// positions is contiguous, so the lanes of a read take consecutive 16-byte
+// words, free of bank conflicts), then per block its scale (int8: D
+// [blocks]) or its scale and code sum (int4 / int2: {d, qs} [blocks]).
 template <int WB> struct ActShape;
 template <> struct ActShape<8> { static constexpr int NA = 4; };
 template <> struct ActShape<4> { static constexpr int NA = 8; };
@@ -291,48 +294,49 @@ template <> struct ActShape<2> { static constexpr int NA = 16; };
 constexpr int stage_batch(int wb) { return wb == 8 ? 5 : wb == 4 ? 3 : 2; }
 
 template <int WB>
-__device__ __forceinline__ void store_act(const Act<WB> &A, int pos, uint32_t *la, float *ld, int *lq)
+__device__ __forceinline__ void store_act(const Act<WB> &A, int pos, int nch, uint32_t *la, float *ld)
 {
-    uint4 *dst = reinterpret_cast<uint4 *>(la + pos * ActShape<WB>::NA);
+    uint4 *dst = reinterpret_cast<uint4 *>(la);
 #pragma unroll
     for (int i = 0; i < ActShape<WB>::NA / 4; i++)
-        dst[i] = make_uint4(A.a[4 * i], A.a[4 * i + 1], A.a[4 * i + 2], A.a[4 * i + 3]);
+        dst[i * nch + pos] = make_uint4(A.a[4 * i], A.a[4 * i + 1], A.a[4 * i + 2], A.a[4 * i + 3]);
     if constexpr (WB == 8) {
         ld[pos >> 1] = A.d;  // both chunks of a block store the block's scale
     } else if constexpr (WB == 4) {
-        ld[pos] = A.d;
-        lq[pos] = A.qs;
+        reinterpret_cast<float2 *>(ld)[pos] = make_float2(A.d, __int_as_float(A.qs));
     } else {
-        ld[2 * pos] = A.d0; ld[2 * pos + 1] = A.d1;
-        lq[2 * pos] = A.qs0; lq[2 * pos + 1] = A.qs1;
+        reinterpret_cast<float4 *>(ld)[pos] =
+            make_float4(A.d0, __int_as_float(A.qs0), A.d1, __int_as_float(A.qs1));
     }
 }
 
 template <int WB>
-__device__ __forceinline__ void stage_act(const int8_t *q, const float *d, int pos, uint32_t *la, float *ld, int *lq)
+__device__ __forceinline__ void stage_act(const int8_t *q, const float *d, int pos, int nch, uint32_t *la, float *ld)
 {
     Act<WB> A;
     A.load(q, d, pos);
-    store_act<WB>(A, pos, la, ld, lq);
+    store_act<WB>(A, pos, nch, la, ld);
 }
 
 template <int WB>
-__device__ __forceinline__ void act_from_lds(Act<WB> &A, const uint32_t *la, const float *ld, const int *lq, int pos)
+__device__ __forceinline__ void act_from_lds(Act<WB> &A, const uint32_t *la, const float *ld, int pos, int nch)
 {
-    const uint4 *src = reinterpret_cast<const uint4 *>(la + pos * ActShape<WB>::NA);
+    const uint4 *src = reinterpret_cast<const uint4 *>(la);
 #pragma unroll
     for (int i = 0; i < ActShape<WB>::NA / 4; i++) {
-        const uint4 v = src[i];
+        const uint4 v = src[i * nch + pos];
         A.a[4 * i] = v.x; A.a[4 * i + 1] = v.y; A.a[4 * i + 2] = v.z; A.a[4 * i + 3] = v.w;
     }
     if constexpr (WB == 8) {
         A.d = ld[pos >> 1];
     } else if constexpr (WB == 4) {
-        A.set_scale(ld[pos]);
-        A.qs = lq[pos];
+        const float2 v = reinterpret_cast<const float2 *>(ld)[pos];
+        A.set_scale(v.x);
+        A.qs = __float_as_int(v.y);
     } else {
-        A.set_scale(ld[2 * pos], ld[2 * pos + 1]);
-        A.qs0 = lq[2 * pos]; A.qs1 = lq[2 * pos + 1];
+        const float4 v = reinterpret_cast<const float4 *>(ld)[pos];
+        A.set_scale(v.x, v.z);
+        A.qs0 = __float_as_int(v.y); A.qs1 = __float_as_int(v.w);
     }
 }
 
@@ -377,11 +381,10 @@ __global__ __launch_bounds__(256) void k_gate_up_rg(const GemvArgs a, const Chun
     const size_t tok_bytes = act_lds_bytes(WB, H);
     auto la_of = [&](int tt) { return reinterpret_cast<uint32_t *>(lds_act + tt * tok_bytes); };
     auto ld_of = [&](int tt) { return reinterpret_cast<float *>(lds_act + tt * tok_bytes + H); };
-    auto lq_of = [&](int tt) { return reinterpret_cast<int *>(lds_act + tt * tok_bytes + H + 4 * nb); };
     for (int c = tid; c < n_u * cpr; c += 256) {
         const int tt = c / cpr, pos = c - tt * cpr;
         const int t = plan[pd.o_t + p0 + tt];
-        stage_act<WB>(a.xq + (size_t)t * H, a.xd + (size_t)t * nb, pos, la_of(tt), ld_of(tt), lq_of(tt));
+        stage_act<WB>(a.xq + (size_t)t * H, a.xd + (size_t)t * nb, pos, cpr, la_of(tt), ld_of(tt));
     }
     __syncthreads();
 
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(256) void k_gate_up_rg(const GemvArgs a, const Chun
                 for (int tt = 0; tt < TT; tt++) {
                     if (tt < n_u) {
                         Act<WB> A;
-                        act_from_lds<WB>(A, la_of(tt), ld_of(tt), lq_of(tt), pos);
+                        act_from_lds<WB>(A, la_of(tt), ld_of(tt), pos, cpr);
                         accg[tt] += A.dot(g[j]);
                         accu[tt] += A.dot(v[j]);
                     }
@@ -484,7 +487,6 @@ __global__ __launch_bounds__(256) void k_down_rg(const GemvArgs a, const ChunkCf
     const size_t pair_bytes = act_lds_bytes(WB, I);
     auto la_of = [&](int p) { return reinterpret_cast<uint32_t *>(act + p * pair_bytes); };
     auto ld_of = [&](int p) { return reinterpret_cast<float *>(act + p * pair_bytes + I); };
-    auto lq_of = [&](int p) { return reinterpret_cast<int *>(act + p * pair_bytes + I + 4 * nbh); };
 
     for (int i = tid; i < pd.words; i += 256) plan[i] = a.plan[i];
     __syncthreads();
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(256) void k_down_rg(const GemvArgs a, const ChunkCf
     const PlanPairs pp = plan_pairs(plan, pd);
     for (int c = tid; c < pp.count() * cpr; c += 256) {
         const int i = c / cpr, pos = c - i * cpr, p = pp(i);
-        stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pos, la_of(p), ld_of(p), lq_of(p));
+        stage_act<WB>(a.qh + (size_t)p * I, a.dh + (size_t)p * nbh, pos, cpr, la_of(p), ld_of(p));
     }
     __syncthreads();
 
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(256) void k_down_rg(const GemvArgs a, const ChunkCf
                 const int pos = sub + kDnLanes * (b * kDnBatch + j);
                 if (pos < cpr) {
                     Act<WB> A;
-                    act_from_lds<WB>(A, la_of(p), ld_of(p), lq_of(p), pos);
+                    act_from_lds<WB>(A, la_of(p), ld_of(p), pos, cpr);
                     part += A.dot(w[j]);
                 }
             }
@@ -778,15 +780,20 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
 // Every slot of a chunk, with the plan the plan kernel published.  The plan
 // is range-checked, so a corrupt plan can only skip work, never steer a load
 // out of the weight tensors.
-// One token, no plan launch: the first n_shared * tiles workgroups take the
-// shared expert, which needs no routing, and start streaming at once; the
-// workgroups of routed slot u take the expert of rank u, found by the first
+// One token, no plan launch: the shared expert's workgroups need no routing
+// and start streaming at once; the workgroups of routed slot u take the
+// expert of rank u, found by the first
 // u + 1 rounds of the selection in their first wave (the same inputs in the
 // same order, so every workgroup reaches the same ranking), so a slot's
 // stream starts as soon as its own rank is known.  Workgroup (u = 0, tile 0)
 // runs the whole selection and publishes the plan for the down kernel, and
 // the routing when asked; with adaptive top-p every workgroup does, since
 // whether rank u is kept depends on all the weights.
+// Dispatch order: the routed slots in rank order, then the shared expert.
+// The launch has more workgroups than two per CU, and the last dispatched
+// land on CUs that already stream two; there a selection runs slowest (it
+// shares the SIMDs with the streaming waves), so those places go to the
+// workgroups that select nothing.
 template <int WB, int CPT, int RPS, bool TAB>
 __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, int tiles, float (*s_h)[32],
                                        float (*part)[1][kSwGroups][32])
@@ -794,7 +801,10 @@ __device__ void gate_up_sw_routed_here(const GemvArgs &a, const PlanDims &pd, in
     __shared__ int plan[1 + 5 * (kMaxTopK + 1)];
     __shared__ int s_idx[kMaxTopK];
     __shared__ float s_w[kMaxTopK];
-    const int v = blockIdx.x / tiles, tile = blockIdx.x % tiles, row0 = tile * 32;
+    const int b = blockIdx.x / tiles, tile = blockIdx.x % tiles, row0 = tile * 32;
+    const int nr = pd.S - a.n_shared;  // routed slots
+    // slot v: 0 .. n_shared - 1 the shared experts, then rank v - n_shared
+    const int v = b < nr ? b + a.n_shared : b - nr;
     if (v < a.n_shared) {
         if (threadIdx.x == 0) plan[0] = 0;  // the token list of the shared slot: token 0
         __syncthreads();
@@ -964,6 +974,10 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     static_assert(!(EARLY && (MB || TT != 1)), "the early prologue is for one token, one batch");
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ float part[TT][kDsGroups][kDsRows];
+    // EARLY: one record per slot {offset of the rows (low, high; bit 31 of
+    // the high word: the shared expert's weights), staged pair (-1: none),
+    // pair weight}, formed once after the plan barrier
+    __shared__ int4 sdesc[EARLY ? kMaxTopK + 1 : 1];
     constexpr int NSTEP = kDsRows / RPS;
     const int tid = threadIdx.x, lane = lane_id();
     const int I = a.I, nbh = I / 32, cpr = cc.cpr;
@@ -973,7 +987,6 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     const size_t pair_bytes = act_lds_bytes(WB, I);
     auto la_of = [&](int p) { return reinterpret_cast<uint32_t *>(act + p * pair_bytes); };
     auto ld_of = [&](int p) { return reinterpret_cast<float *>(act + p * pair_bytes + I); };
-    auto lq_of = [&](int p) { return reinterpret_cast<int *>(act + p * pair_bytes + I + 4 * nbh); };
     // every slot's kDsRows row scales, [slot][row], after a.down_pmax pairs
     float *lsc = reinterpret_cast<float *>(act + (size_t)a.down_pmax * pair_bytes);
 
@@ -1010,18 +1023,19 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     const size_t step_bytes = (size_t)kDsThreads * 16;
     auto slot_w = [&](int u) -> const moe_weights_t & { return plan[pd.o_e + u] >= 0 ? a.routed : a.shared; };
     auto slot_ee = [&](int u) { return max(plan[pd.o_e + u], 0); };
-    // the slot's base address is workgroup-uniform (scalar registers): the
-    // loads then take a fixed per-lane offset
-    auto slot_src = [&](int u) {
-        const int uu = __builtin_amdgcn_readfirstlane(u);
+    // the first of the workgroup's rows of slot u
+    auto slot_rows = [&](int u) {
         if constexpr (TAB) {
-            const int e = plan[pd.o_e + uu];
+            const int e = plan[pd.o_e + u];
             const int64_t off = a.toff[(size_t)max(e, 0) * 6 + 2];
             const uint8_t *b = (e >= 0) ? a.routed.down + off : a.shared.down;
-            return b + (size_t)row_base * rowbytes + (size_t)tid * 16;
+            return b + (size_t)row_base * rowbytes;
         }
-        return slot_w(uu).down + ((size_t)slot_ee(uu) * a.H + row_base) * rowbytes + (size_t)tid * 16;
+        return slot_w(u).down + ((size_t)slot_ee(u) * a.H + row_base) * rowbytes;
     };
+    // the slot's base address is workgroup-uniform (scalar registers): the
+    // loads then take a fixed per-lane offset
+    auto slot_src = [&](int u) { return slot_rows(__builtin_amdgcn_readfirstlane(u)) + (size_t)tid * 16; };
     float acc[TT][NSTEP];
 #pragma unroll
     for (int tt = 0; tt < TT; tt++)
@@ -1073,11 +1087,23 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
                 const int p = p0 + q, li = lidx(p);
                 const float pw = __int_as_float(plan[pd.o_w + p]);
                 Act<WB> A;
-                act_from_lds<WB>(A, la_of(li), ld_of(li), lq_of(li), pos);
+                act_from_lds<WB>(A, la_of(li), ld_of(li), pos, cpr);
 #pragma unroll
                 for (int j = 0; j < NSTEP; j++) acc[tt][j] += A.dot(wb[j]) * (pw * sb[j]);
                 q++;
             }
+        }
+    };
+    // the same for one token from the slot's record (li: staged pair, -1 for none)
+    auto use_slot1 = [&](int u, const uint4 (&wb)[NSTEP], int li, float pw) {
+        float sb[NSTEP];
+#pragma unroll
+        for (int j = 0; j < NSTEP; j++) sb[j] = lsc[u * kDsRows + j * RPS + rowoff];
+        if (li >= 0) {
+            Act<WB> A;
+            act_from_lds<WB>(A, la_of(li), ld_of(li), pos, cpr);
+#pragma unroll
+            for (int j = 0; j < NSTEP; j++) acc[0][j] += A.dot(wb[j]) * (pw * sb[j]);
         }
     };
     // Staging.  Every slot's row scales go to LDS once.  The pairs' int8 h
@@ -1107,7 +1133,7 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
         for (int b = 0; b < SB; b++) {
             const int i = scs[b] / cpr, pp = scs[b] - i * cpr;
             sa[b].finish();
-            store_act<WB>(sa[b], pp, la_of(i), ld_of(i), lq_of(i));
+            store_act<WB>(sa[b], pp, cpr, la_of(i), ld_of(i));
         }
     };
     auto scale_issue = [&](int i0) {
@@ -1150,6 +1176,14 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
         if (plan[pd.o_e + S - 1] != -1) return;  // the shared slot is last
         nsc = S * kDsRows;
         bend = S;
+        if (tid < S) {  // the slot records (a pair is used when its token is 0)
+            const int n = plan[pd.o_n + tid], p0 = plan[pd.o_p0 + tid];
+            const bool sh = plan[pd.o_e + tid] < 0;
+            const uint64_t off = (uint64_t)(slot_rows(tid) - (sh ? a.shared.down : a.routed.down));
+            const bool use = n > 0 && plan[pd.o_t + p0] == 0;
+            sdesc[tid] = make_int4((int)(uint32_t)off, (int)((uint32_t)(off >> 32) | (sh ? 0x80000000u : 0u)),
+                                   use ? lidx(p0) : -1, use ? plan[pd.o_w + p0] : 0);
+        }
         scale_issue(0);
 #pragma unroll
         for (int b = 1; b < NB - 1; b++) load_slot(slot_at(min(b, S - 1)), wr[b]);
@@ -1175,6 +1209,22 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     }
     stage_rest(SB * kDsThreads);
     __syncthreads();
+    // EARLY: the record fields of the ring's slots (scalar registers)
+    int dli[NB];
+    float dpw[NB];
+    auto take_record = [&](int u, int r) {
+        const int4 d = sdesc[u];
+        dli[r] = __builtin_amdgcn_readfirstlane(d.z);
+        dpw[r] = __int_as_float(__builtin_amdgcn_readfirstlane(d.w));
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(d.x), hi = __builtin_amdgcn_readfirstlane(d.y);
+        // from the weights' own base pointers, so the loads stay global ones
+        const uint8_t *base = (hi >> 31) ? a.shared.down : a.routed.down;
+        return base + ((uint64_t)(hi & 0x7fffffffu) << 32 | lo);
+    };
+    if constexpr (EARLY) {
+#pragma unroll
+        for (int b = 0; b < NB - 1; b++) take_record(slot_at(min(b, S - 1)), b);
+    }
     for (int u0 = 0; u0 < S; u0 += NB) {
 #pragma unroll
         for (int b = 0; b < NB; b++) {
@@ -1182,7 +1232,12 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
             // unconditional (past the end: the last slot again, an L2 hit),
             // so the ring's registers carry no merge of loaded and unloaded
             // values and every wait counts the ring's loads exactly
-            load_slot(slot_at(min(u + NB - 1, S - 1)), wr[(b + NB - 1) % NB]);
+            if constexpr (EARLY) {
+                const int r = (b + NB - 1) % NB;
+                load_rows(take_record(slot_at(min(u + NB - 1, S - 1)), r) + (size_t)tid * 16, wr[r]);
+            } else {
+                load_slot(slot_at(min(u + NB - 1, S - 1)), wr[(b + NB - 1) % NB]);
+            }
             if (MB && u < S && u == bend) {  // next batch of pairs (uniform)
                 __syncthreads();
                 batch_from(u);
@@ -1194,7 +1249,10 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
             if (u == S / 4) __builtin_amdgcn_s_setprio(2);
             if (u == S / 2) __builtin_amdgcn_s_setprio(1);
             if (u == (3 * S) / 4) __builtin_amdgcn_s_setprio(0);
-            if (u < S) use_slot(slot_at(u), wr[b]);
+            if (u < S) {
+                if constexpr (EARLY) use_slot1(slot_at(u), wr[b], dli[b], dpw[b]);
+                else use_slot(slot_at(u), wr[b]);
+            }
         }
     }
     const int l32 = lane & 31;
