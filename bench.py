@@ -5,7 +5,11 @@ Default workload: single-token decode through one GLM-5.2-scale MoE layer
 top-4 groups, top-8 experts, 1 shared expert, int4 weights with per-row
 scales): ~171 MB of expert weights per token, HBM-bound.  Other workloads
 (--workload): verify_int8 (3 tokens, int8 weights), prefill_int4 (2048
-tokens through the expert-grouped int8-MFMA path).
+tokens through the expert-grouped int8-MFMA path), stack_int2 (75 layers),
+mtp_int4 (draft verification and acceptance), tier_int4 and tier_stack_int4
+(experts over HBM and host memory).  The default run also records the
+workloads in SECONDARY, each run by a child process with its defaults, under
+"secondary" in its JSON line (--no-secondary skips them).
 
 A step is one moe_layer_forward over one input batch; the inputs rotate
 (64 distinct tokens for decode and verify, 4 batches for prefill) so the
@@ -168,6 +172,43 @@ def write_traffic(args):
     log("bench: wrote %s: %.1f MB per launch of %s" % (p, total / 1e6, kernel))
 
 
+# The default run (the int4 decode layer) also records the other workloads,
+# each in a child process of its own with its default steps, so that one run
+# carries every configuration's figure; the headline line is unaffected.
+SECONDARY = ["prefill_int4", "stack_int2", "verify_int8", "mtp_int4", "tier_int4"]
+SECONDARY_TIMEOUT_S = 300
+
+
+def run_secondary():
+    import subprocess
+    res = {}
+    for w in SECONDARY:
+        log("bench: secondary workload %s" % w)
+        t0 = time.time()
+        try:
+            p = subprocess.run([sys.executable, os.path.abspath(__file__), "--workload", w, "--no-cpu-baseline",
+                                "--no-secondary"], stdout=subprocess.PIPE, text=True, timeout=SECONDARY_TIMEOUT_S)
+        except subprocess.TimeoutExpired:
+            res[w] = {"error": "timed out after %d s" % SECONDARY_TIMEOUT_S}
+            continue
+        lines = [ln for ln in p.stdout.splitlines() if ln.startswith("{")]
+        if p.returncode != 0 or not lines:
+            res[w] = {"error": "exit status %d" % p.returncode}
+            continue
+        j = json.loads(lines[-1])
+        rf = j.get("roofline") or {}
+        det = j.get("detail") or {}
+        rec = {k: j.get(k) for k in ("value", "unit", "ms_per_step", "steps", "warmup", "higher_is_better", "dtype")}
+        rec["config"] = j.get("config")
+        rec["roofline"] = {k: rf.get(k) for k in ("bound", "kernel", "achieved", "peak", "unit", "frac", "traffic")}
+        for k in ("stage_us", "per_layer_us", "tokens_per_step", "hit_rate"):
+            if k in det:
+                rec[k] = det[k]
+        rec["wall_s"] = time.time() - t0
+        res[w] = rec
+    return res
+
+
 def copy_calibration():
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
@@ -234,6 +275,8 @@ def main():
     ap.add_argument("--lookahead-ranks", type=int, default=None,
                     help="tier_stack_int4: prefetch only the first N ranks of each predicted selection")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="default run: skip the other workloads' records (see SECONDARY)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--stream-ceiling", action="store_true",
@@ -482,6 +525,13 @@ def main():
                    "router_weight_bytes": router_bytes, "wall_s_timed_loop_incl_flush": wall},
         "cpu_baseline": cpu,
     }
+    default_run = (wl.name == "decode_int4" and args.tokens is None and not args.top_p and not args.graph
+                   and not args.no_flush)
+    if default_run and not args.no_secondary:
+        del routed, shared, xs, flush_buf, ws, rws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["secondary"] = run_secondary()
     print(json.dumps(out), flush=True)
 
 
