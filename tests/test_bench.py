@@ -1,7 +1,8 @@
 """The measurement harness on the CPU: the one-GPU rule, the rocprofv3
 counter arithmetic that turns FETCH_SIZE / WRITE_SIZE into HBM-side bytes
 per launch (calibrated against a plain copy of known size), and the
-refusal of a counter file that holds no dispatch of the kernel asked for."""
+refusal of a counter file that holds no dispatch of the kernel asked for,
+and the default run's records of the other workloads."""
 import csv
 import importlib.util
 import json
@@ -80,3 +81,35 @@ def test_missing_kernel_is_refused(bench, tmp_path, monkeypatch):
                                     copy_fetch=str(tmp_path / "c"), copy_write=str(tmp_path / "c"), commands=[])
     with pytest.raises(SystemExit):
         bench.write_traffic(args)
+
+
+def test_secondary_records(bench, monkeypatch):
+    """The default run's child runs: a child's last JSON line becomes its
+    record; a failed or timed-out child leaves an error entry, and every
+    workload of SECONDARY is run once with the defaults."""
+    calls = []
+
+    def fake_run(cmd, stdout=None, text=None, timeout=None):
+        w = cmd[cmd.index("--workload") + 1]
+        calls.append(cmd)
+        assert "--no-secondary" in cmd and "--no-cpu-baseline" in cmd and timeout == bench.SECONDARY_TIMEOUT_S
+        if w == "stack_int2":
+            raise subprocess.TimeoutExpired(cmd, timeout)
+        if w == "verify_int8":
+            return subprocess.CompletedProcess(cmd, 1, stdout="", stderr=None)
+        line = {"value": 2.0, "unit": "tokens/s", "ms_per_step": 0.5, "steps": 3, "warmup": 1,
+                "higher_is_better": True, "dtype": "i8", "config": {"workload": w},
+                "roofline": {"bound": "hbm", "kernel": "k", "achieved": 1.0, "peak": 8.0, "unit": "GB/s",
+                             "frac": 0.125, "traffic": None, "extra": 7},
+                "detail": {"stage_us": {"a": 1.0}, "other": 3}}
+        return subprocess.CompletedProcess(cmd, 0, stdout="progress\n" + json.dumps(line) + "\n", stderr=None)
+
+    monkeypatch.setattr(subprocess, "run", fake_run)
+    res = bench.run_secondary()
+    assert [c[c.index("--workload") + 1] for c in calls] == bench.SECONDARY
+    assert set(res) == set(bench.SECONDARY)
+    assert "timed out" in res["stack_int2"]["error"]
+    assert res["verify_int8"]["error"] == "exit status 1"
+    r = res["prefill_int4"]
+    assert r["value"] == 2.0 and r["config"] == {"workload": "prefill_int4"} and r["stage_us"] == {"a": 1.0}
+    assert r["roofline"]["frac"] == 0.125 and "extra" not in r["roofline"] and "other" not in r
