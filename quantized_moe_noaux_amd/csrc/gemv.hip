@@ -1286,6 +1286,8 @@ static int lookahead_wgs(const GemvArgs &a)
 template <int WB, int CPT, int RPS, int TT, bool TAB = false>
 static int run_gate_up_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
+    // the sweep's row width (kSwThreads * CPT / RPS chunks) must be the row's
+    if (cc.cpr * RPS != kSwThreads * CPT) return (int)hipErrorInvalidValue;
     k_gate_up_sw<WB, CPT, RPS, TT, TAB><<<pd.S * (a.I / 32) + lookahead_wgs(a), kSwThreads, 0, st>>>(a, cc, pd);
     return (int)hipGetLastError();
 }
@@ -1294,6 +1296,8 @@ template <int WB, int RPS, int TT, bool TAB = false>
 static int run_down_sw(const GemvArgs &a, const ChunkCfg &cc, const PlanDims &pd, hipStream_t st)
 {
     constexpr int NB = kDownRing;
+    // a step covers RPS whole rows: a row of cc.cpr chunks must tile the block
+    if (cc.cpr * RPS != kDsThreads) return (int)hipErrorInvalidValue;
     const size_t lds = down_sw_lds_bytes(WB, a.I, pd, a.down_pmax);
     // one staging batch holds every pair (one token at the production
     // shapes): the kernel without the batch switch in its slot loop
@@ -1424,16 +1428,17 @@ int launch_down(const GemvArgs &args, hipStream_t st)
     const int kind = down_sw_kind(cc.cpr);
     if (a.toff) {
         if (kind != 1 || a.wbits != 4 || a.H % kDsRows) return (int)hipErrorInvalidValue;
-        return a.T == 1 ? run_down_sw<4, 4, 1, true>(a, cc, pd, st) : run_down_sw<4, 4, 8, true>(a, cc, pd, st);
+        return a.T == 1 ? run_down_sw<4, kDsThreads / 64, 1, true>(a, cc, pd, st)
+                        : run_down_sw<4, kDsThreads / 64, 8, true>(a, cc, pd, st);
     }
     if (a.H % kDsRows == 0) {
-        if (kind == 1 && a.wbits == 4) { MOE_SW_TTX(run_down_sw, 4, 4) }
-        if (kind == 1 && a.wbits == 8) { MOE_SW_TT(run_down_sw, 8, 4) }
-        if (kind == 1 && a.wbits == 2) { MOE_SW_TT(run_down_sw, 2, 4) }
-        if (kind == 2 && a.wbits == 8) { MOE_SW_TTX(run_down_sw, 8, 2) }
-        if (kind == 2 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, 2) }
-        if (kind == 3 && a.wbits == 2) { MOE_SW_TTX(run_down_sw, 2, 8) }
-        if (kind == 3 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, 8) }
+        if (kind == 1 && a.wbits == 4) { MOE_SW_TTX(run_down_sw, 4, kDsThreads / 64) }
+        if (kind == 1 && a.wbits == 8) { MOE_SW_TT(run_down_sw, 8, kDsThreads / 64) }
+        if (kind == 1 && a.wbits == 2) { MOE_SW_TT(run_down_sw, 2, kDsThreads / 64) }
+        if (kind == 2 && a.wbits == 8) { MOE_SW_TTX(run_down_sw, 8, kDsThreads / 128) }
+        if (kind == 2 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, kDsThreads / 128) }
+        if (kind == 3 && a.wbits == 2) { MOE_SW_TTX(run_down_sw, 2, kDsThreads / 32) }
+        if (kind == 3 && a.wbits == 4) { MOE_SW_TT(run_down_sw, 4, kDsThreads / 32) }
     }
     MOE_DISPATCH(run_down)
 }
