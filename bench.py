@@ -72,7 +72,7 @@ def log(*a):
 
 
 # sources (and build script) that make the kernels of each path
-PATH_SOURCES = {"gemv": ["gemv.hip", "route.hip", "moe_dev.h", "topk_dev.h", "moe_internal.h"],
+PATH_SOURCES = {"gemv": ["gemv.hip", "route.hip", "moe_dev.h", "topk_dev.h", "moe_internal.h", "slot_record.h"],
                 "grouped": ["grouped.hip", "route.hip", "misc.hip", "moe_dev.h", "topk_dev.h", "moe_internal.h"]}
 
 

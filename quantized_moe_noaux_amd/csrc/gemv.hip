@@ -28,6 +28,7 @@
 // expert's workgroups, which need no routing, already stream their rows.
 #include "moe_dev.h"
 #include "moe_internal.h"
+#include "slot_record.h"
 #include "topk_dev.h"
 
 namespace moe {
@@ -640,10 +641,18 @@ constexpr int kSwThreads = 192;  // gate/up row-sweep block
 static_assert(kSwThreads % 32 == 0, "row r of a tile is handled by threads r mod 32");
 constexpr int kSwGroups = kSwThreads / 32;
 constexpr int kSwDepth = 11;     // steps of prefetch in flight (<= 168 VGPRs: 3 waves per SIMD)
+// Batches of 2-8 tokens: per-token accumulators and activations are live
+// registers, so a batch kernel takes passes of 4 rows (one token: 8) and,
+// with one chunk per thread, 4 steps of prefetch: at most ~200 VGPRs, two or
+// three waves per SIMD.  With the one-token settings the batch kernels held
+// 256 VGPRs plus AGPR spills, one wave per SIMD (measured on MI355X: verify
+// batches of 2, 3, 5 and 8 tokens 6%, 9%, 14% and 22% faster this way).
+constexpr int kSwDepthBatch = 4;
+constexpr int kSwPassRowsBatch = 4;
 
 // gate/up of one 32-row tile of one expert for the n_u tokens of a slot: a
 // step reads RPS rows of gate and of up (kSwThreads * CPT chunks each,
-// contiguous), in passes of 8 rows.  toks lists the slot's tokens; pair
+// contiguous), in passes of 8 rows (4 for batches).  toks lists the slot's tokens; pair
 // p_first + tt receives token tt's quantised h.  All threads of the block
 // must call it.
 template <int WB, int CPT, int RPS, int TT>
@@ -652,8 +661,12 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
                                                 float (*part)[TT][kSwGroups][32])
 {
     static_assert(CPT == 1 || RPS == 1, "chunks of one thread stay in one row");
-    constexpr int NSTEP = 32 / RPS, PS = 8 / RPS;
-    constexpr int PF = (CPT == 1) ? kSwDepth : kSwDepth / 2;
+    // batches of tokens: shorter passes (fewer live accumulators) and, with
+    // one chunk per thread, a shallower prefetch (each step's dots are TT
+    // times the work)
+    constexpr int PASS_ROWS = TT > 1 ? kSwPassRowsBatch : 8;
+    constexpr int NSTEP = 32 / RPS, PS = PASS_ROWS / RPS;
+    constexpr int PF = (CPT == 1) ? (TT > 1 ? kSwDepthBatch : kSwDepth) : kSwDepth / 2;
     const int tid = threadIdx.x, lane = lane_id();
     const int cpr = (kSwThreads * CPT) / RPS, H = a.H, nb = H / 32;
     const size_t rowbytes = (size_t)cpr * 16;
@@ -745,8 +758,8 @@ __device__ __forceinline__ void gate_up_tile_sw(const GemvArgs &a, const moe_wei
                     const float g = group32_reduce_scatter<PS, (TT > 1)>(accg[tt]);
                     const float v = group32_reduce_scatter<PS, (TT > 1)>(accu[tt]);
                     if (writer) {
-                        part[0][tt][grp][pass * 8 + jj * RPS + rowoff] = g;
-                        part[1][tt][grp][pass * 8 + jj * RPS + rowoff] = v;
+                        part[0][tt][grp][pass * PASS_ROWS + jj * RPS + rowoff] = g;
+                        part[1][tt][grp][pass * PASS_ROWS + jj * RPS + rowoff] = v;
                     }
                 }
             }
@@ -974,9 +987,9 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     static_assert(!(EARLY && (MB || TT != 1)), "the early prologue is for one token, one batch");
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ float part[TT][kDsGroups][kDsRows];
-    // EARLY: one record per slot {offset of the rows (low, high; bit 31 of
-    // the high word: the shared expert's weights), staged pair (-1: none),
-    // pair weight}, formed once after the plan barrier
+    // EARLY: one record per slot (slot_record.h), formed once after the
+    // plan barrier
+    static_assert(kMaxTopK + 1 <= kRecordMaxPair, "a record's staged pair index");
     __shared__ int4 sdesc[EARLY ? kMaxTopK + 1 : 1];
     constexpr int NSTEP = kDsRows / RPS;
     const int tid = threadIdx.x, lane = lane_id();
@@ -1179,10 +1192,15 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
         if (tid < S) {  // the slot records (a pair is used when its token is 0)
             const int n = plan[pd.o_n + tid], p0 = plan[pd.o_p0 + tid];
             const bool sh = plan[pd.o_e + tid] < 0;
-            const uint64_t off = (uint64_t)(slot_rows(tid) - (sh ? a.shared.down : a.routed.down));
             const bool use = n > 0 && plan[pd.o_t + p0] == 0;
-            sdesc[tid] = make_int4((int)(uint32_t)off, (int)((uint32_t)(off >> 32) | (sh ? 0x80000000u : 0u)),
-                                   use ? lidx(p0) : -1, use ? plan[pd.o_w + p0] : 0);
+            SlotRecord rec;
+            rec.off = slot_rows(tid) - (sh ? a.shared.down : a.routed.down);
+            rec.pair = use ? lidx(p0) : -1;
+            rec.shared = sh;
+            rec.w_bits = use ? plan[pd.o_w + p0] : 0;
+            int w[4];
+            record_pack(rec, w);
+            sdesc[tid] = make_int4(w[0], w[1], w[2], w[3]);
         }
         scale_issue(0);
 #pragma unroll
@@ -1214,12 +1232,12 @@ __global__ __launch_bounds__(kDsThreads) void k_down_sw(const GemvArgs a, const 
     float dpw[NB];
     auto take_record = [&](int u, int r) {
         const int4 d = sdesc[u];
-        dli[r] = __builtin_amdgcn_readfirstlane(d.z);
-        dpw[r] = __int_as_float(__builtin_amdgcn_readfirstlane(d.w));
-        const uint32_t lo = __builtin_amdgcn_readfirstlane(d.x), hi = __builtin_amdgcn_readfirstlane(d.y);
+        const SlotRecord rec = record_unpack(__builtin_amdgcn_readfirstlane(d.x), __builtin_amdgcn_readfirstlane(d.y),
+                                             __builtin_amdgcn_readfirstlane(d.z), __builtin_amdgcn_readfirstlane(d.w));
+        dli[r] = rec.pair;
+        dpw[r] = __int_as_float(rec.w_bits);
         // from the weights' own base pointers, so the loads stay global ones
-        const uint8_t *base = (hi >> 31) ? a.shared.down : a.routed.down;
-        return base + ((uint64_t)(hi & 0x7fffffffu) << 32 | lo);
+        return (rec.shared ? a.shared.down : a.routed.down) + rec.off;
     };
     if constexpr (EARLY) {
 #pragma unroll
